@@ -1,0 +1,73 @@
+"""Algorithmic work of the sparse MoE feed-forward layer: flops and bytes.
+
+These are the counts the roofline fractions are computed from.  They follow
+the shapes of "Mixtral > Architecture Overview" (mbrenndoerfer.com),
+hyperparameter list and parameter-count paragraph: per layer, E experts, each
+with gate [f, d], up [f, d] and down [d, f] matrices; each token runs k of
+them.  The router is one [E, d] matrix ("Mixtral of Experts", azimuth.plus,
+router paragraph).
+
+Nothing here executes the layer; it only counts.
+"""
+
+from __future__ import annotations
+
+MIXTRAL = dict(layers=32, d=4096, f=14336, E=8, k=2)
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA, published
+PEAK_FP32_FLOPS = 157.3e12    # MI355X fp32 vector, published
+PEAK_HBM_BYTES = 8.0e12       # MI355X HBM3E, published
+
+
+def projection_params(d: int, f: int) -> int:
+    """Parameters of one projection matrix (gate, up or down)."""
+    return d * f
+
+
+def expert_params(d: int, f: int, layers: int = 1) -> int:
+    """Parameters of one expert's three projections, over ``layers`` layers."""
+    return 3 * d * f * layers
+
+
+def ffn_params(d: int, f: int, E: int, layers: int = 1) -> int:
+    """All expert parameters (E experts per layer)."""
+    return E * expert_params(d, f, layers)
+
+
+def active_ffn_params(d: int, f: int, k: int, layers: int = 1) -> int:
+    """Expert parameters one token touches (k experts per layer)."""
+    return k * expert_params(d, f, layers)
+
+
+def router_flops_per_token(d: int, E: int) -> int:
+    return 2 * d * E
+
+
+def expert_flops_per_token(d: int, f: int, k: int) -> int:
+    """Multiply-adds of k SwiGLU experts, counted as 2 flops each."""
+    return 2 * k * 3 * d * f
+
+
+def up_flops_per_slot(d: int, f: int) -> int:
+    """Gate and up projections of one (token, expert) slot."""
+    return 2 * 2 * d * f
+
+
+def down_flops_per_slot(d: int, f: int) -> int:
+    return 2 * d * f
+
+
+def layer_flops(T: int, d: int, f: int, E: int, k: int) -> int:
+    """Whole layer: router + k experts per token."""
+    return T * (router_flops_per_token(d, E) + expert_flops_per_token(d, f, k))
+
+
+def expert_weight_bytes(d: int, f: int, n_experts: int, elem_bytes: int = 2) -> int:
+    """Bytes of the three matrices of ``n_experts`` experts."""
+    return n_experts * 3 * d * f * elem_bytes
+
+
+def decode_layer_bytes(T: int, d: int, f: int, E: int, k: int, n_touched: int, elem_bytes: int = 2) -> int:
+    """Minimum HBM traffic of one layer when the weights dominate: every
+    touched expert's weights once, the router matrix, x in and y out."""
+    return (expert_weight_bytes(d, f, n_touched, elem_bytes) + E * d * elem_bytes
+            + 2 * T * d * elem_bytes)
