@@ -1,0 +1,191 @@
+/*
+ * moe.h -- C ABI of libmoe.so, the MI355X (gfx950) sparse mixture-of-experts
+ * feed-forward layer (Mixtral: E = 8 experts, top-2 routing, SwiGLU experts).
+ *
+ * The layer, per token x (a row of length d):
+ *   l = x W_g^T (+ b)               8 router scores, one per expert
+ *   (a, b) = the two largest scores, larger first, ties to the lower index;
+ *            every other score becomes -inf
+ *   g = softmax over the surviving pair  (g_a = 1/(1+exp(l_b-l_a)), g_b = 1-g_a)
+ *   o_e = (SiLU(x w1_e^T) * (x w3_e^T)) w2_e^T   for e in {a, b}
+ *   y = g_a o_a + g_b o_b           (dropless: every token gets both experts)
+ * Sources: "Mixtral of Experts" (azimuth.plus), router paragraph (linear map
+ * x W_g to 8 scores, top-2 kept, others -inf, softmax over the survivors)
+ * and architecture paragraph (SwiGLU experts with their own weights);
+ * "Mixtral > Architecture Overview" (mbrenndoerfer.com), hyperparameter list
+ * (d = 4096, f = 14336, 8 experts, 2 active) and parameter-count paragraph
+ * (gate, up and down projections); "Mixtral & Sparse MoE (2024) > The
+ * Solution" (mbrenndoerfer.com), routing paragraph (outputs combined by the
+ * routing scores, each token routed on its own).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Tensor pointers are DEVICE pointers to row-major, contiguous arrays,
+ *   16-byte aligned.  Scalars and the dims struct are host memory.
+ * - Layouts: x [T, d]; w_gate [E, d] (one row per expert: the transpose of
+ *   the d x E map the router multiplies by); w1 (gate) and w3 (up) [E, f, d];
+ *   w2 (down) [E, d, f]; logit_bias [E] fp32 or NULL.
+ * - dtype MOE_BF16: x, weights, h and y are bf16; accumulation, router
+ *   scores, gates and y_rows are fp32; h and y are rounded to nearest even.
+ *   dtype MOE_F32: everything fp32.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *   work is enqueued on it; calls return right after enqueueing and never
+ *   synchronise, allocate, free, or keep a pointer after returning.
+ * - Errors: every argument is checked on the host before anything is
+ *   enqueued; on error nothing is enqueued and outputs are untouched.
+ *   NULL required pointer, T < 0, misaligned pointer -> MOE_ERR_INVALID_ARGUMENT;
+ *   E != 8, k != 2, d or f not a multiple of 128, unknown dtype/variant,
+ *   or a size above a stated limit -> MOE_ERR_UNSUPPORTED;
+ *   T == 0 -> MOE_OK with nothing enqueued.  A failed launch -> MOE_ERR_HIP
+ *   (outputs unspecified).  Device faults surface at the caller's next sync.
+ * - Calls on one stream are ordered; the library holds no mutable state
+ *   besides a lazily filled, lock-protected per-device property cache.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Kernel family for the expert GEMMs.  AUTO picks DECODE (weight streaming,
+ * token groups of 16 on MFMA) when T <= 64 and PREFILL (LDS-tiled grouped
+ * GEMM) otherwise.  Both compute the same function; the choice only affects
+ * speed.  MOE_F32 always uses its own fp32 kernels. */
+typedef enum { MOE_VARIANT_AUTO = 0, MOE_VARIANT_DECODE = 1, MOE_VARIANT_PREFILL = 2 } moe_variant;
+
+typedef struct {
+  int64_t T;        /* tokens, >= 0; T * k must fit in int32 */
+  int32_t d;        /* hidden size, multiple of 128 */
+  int32_t f;        /* expert FFN width, multiple of 128 */
+  int32_t E;        /* experts, must be 8 */
+  int32_t k;        /* experts per token, must be 2 */
+  int32_t dtype;    /* moe_dtype */
+  int32_t variant;  /* moe_variant */
+} moe_dims;
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_string(moe_status s);
+
+/* Library version, e.g. "1.0.0" (static string). */
+const char* moe_version(void);
+
+/*
+ * Router: scores, top-2 selection and the softmax over the kept pair.
+ * "Mixtral of Experts" (azimuth.plus), router paragraph.
+ *   x [T, d] (dtype), w_gate [E, d] (dtype), logit_bias [E] fp32 or NULL
+ *   (added to every token's scores; a workload device, not part of Mixtral).
+ *   Outputs: topk_idx [T, 2] int32 (slot 0 = larger score, ties to the lower
+ *   index), topk_w [T, 2] fp32 (>= 0, sum 1), logits [T, E] fp32 or NULL.
+ *   Scores are accumulated in fp32.  Limit: E * d * elem_size <= 128 KiB
+ *   (the router matrix is staged in LDS), i.e. d <= 8192 for bf16.
+ */
+moe_status moe_router_topk(const moe_dims* dims, const void* x, const void* w_gate,
+                           const float* logit_bias, int32_t* topk_idx, float* topk_w,
+                           float* logits, void* stream);
+
+/*
+ * Expert-major permutation of the token slots (slot s = t * k + j is token
+ * t's j-th expert).  It groups each expert's tokens so the expert GEMMs read
+ * them contiguously; it changes no value ("Mixtral & Sparse MoE (2024) > The
+ * Solution", routing paragraph: each token is routed on its own).
+ *   topk_idx [T, k] int32 (values must lie in [0, E); other values are
+ *   undefined behaviour).
+ *   Outputs: expert_offsets [E + 1] int32 (exclusive prefix sum of the per-
+ *   expert counts; offsets[E] = T * k), sorted_slots [T * k] int32 (slots of
+ *   expert 0 in increasing slot id, then expert 1, ...: a stable order),
+ *   slot_rows [T * k] int32 (inverse: position of slot s in sorted_slots).
+ *   Deterministic.  Runs as one workgroup.
+ */
+moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* expert_offsets,
+                       int32_t* sorted_slots, int32_t* slot_rows, void* stream);
+
+/*
+ * Both expert projections for every slot, in expert-major order:
+ *   h[r, :]      = SiLU(x[tok] w1_e^T) * (x[tok] w3_e^T)   (dtype)
+ *   y_rows[r, :] = h[r, :] w2_e^T                          (fp32)
+ * for r in [offsets[e], offsets[e+1]), tok = sorted_slots[r] / k.
+ * "Mixtral of Experts" (azimuth.plus), architecture paragraph (SwiGLU
+ * experts); "Mixtral > Architecture Overview" (mbrenndoerfer.com),
+ * parameter-count paragraph (gate, up and down projections).
+ *   expert_offsets [E + 1], sorted_slots [T * k] as produced by moe_permute
+ *   (device memory; the host never reads them).  h [T * k, f] and
+ *   y_rows [T * k, d] are caller-owned outputs.
+ */
+moe_status moe_grouped_swiglu(const moe_dims* dims, const void* x, const int32_t* expert_offsets,
+                              const int32_t* sorted_slots, const void* w1, const void* w3,
+                              const void* w2, void* h, float* y_rows, void* stream);
+
+/*
+ * The two halves of moe_grouped_swiglu as separate calls (same kernels), so
+ * that each projection can be timed or checked on its own:
+ *   moe_expert_up:   h[r, :] = SiLU(x[tok] w1_e^T) * (x[tok] w3_e^T)   (dtype)
+ *   moe_expert_down: y_rows[r, :] = h[r, :] w2_e^T                     (fp32)
+ * Arguments, layouts and sources as for moe_grouped_swiglu.
+ */
+moe_status moe_expert_up(const moe_dims* dims, const void* x, const int32_t* expert_offsets,
+                         const int32_t* sorted_slots, const void* w1, const void* w3, void* h, void* stream);
+moe_status moe_expert_down(const moe_dims* dims, const void* h, const int32_t* expert_offsets, const void* w2,
+                           float* y_rows, void* stream);
+
+/*
+ * Gate-weighted combine: y[t, :] = topk_w[t, 0] * y_rows[slot_rows[2t], :]
+ *                                 + topk_w[t, 1] * y_rows[slot_rows[2t+1], :]
+ * added in that order in fp32, then rounded once to dtype.
+ * "Mixtral & Sparse MoE (2024) > The Solution" (mbrenndoerfer.com), routing
+ * paragraph; "Mixtral of Experts" (azimuth.plus), router paragraph (the
+ * gates set how much each expert's output contributes).
+ *   y_rows [T * k, d] fp32, slot_rows [T * k] int32, topk_w [T, k] fp32,
+ *   y [T, d] (dtype, output).
+ */
+moe_status moe_combine(const moe_dims* dims, const float* y_rows, const int32_t* slot_rows,
+                       const float* topk_w, void* y, void* stream);
+
+/*
+ * The whole layer: router -> permute -> grouped SwiGLU experts -> combine.
+ *   x, w_gate, logit_bias, w1, w3, w2 as above; y [T, d] (dtype) output.
+ *   Optional outputs (NULL to skip): topk_idx_out [T, 2] int32,
+ *   topk_w_out [T, 2] fp32, expert_counts_out [E] int32.
+ *   workspace: caller-owned device memory, 256-byte aligned.  With
+ *   workspace == NULL the call only writes the required size to
+ *   *workspace_bytes and returns MOE_OK (nothing enqueued).  Otherwise
+ *   *workspace_bytes is its size; too small -> MOE_ERR_WORKSPACE_TOO_SMALL.
+ *   The workspace holds the routing, permutation, h [T*k, f] and
+ *   y_rows [T*k, d]; its contents after the call are unspecified.
+ */
+moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_gate,
+                           const float* logit_bias, const void* w1, const void* w3, const void* w2,
+                           void* y, int32_t* topk_idx_out, float* topk_w_out,
+                           int32_t* expert_counts_out, void* workspace, size_t* workspace_bytes,
+                           void* stream);
+
+/*
+ * Glue between stacked layers (not part of the MoE layer itself; the
+ * pages' decoder blocks are stacked with a residual stream, "Mixtral >
+ * Architecture Overview", layer-components list):
+ *   resid[t, :] += y_add[t, :]            (if y_add != NULL; fp32 residual)
+ *   u[t, :] = resid[t, :] / sqrt(mean(resid[t, :]^2) + eps)   (unit gain)
+ *   resid [T, d] fp32 in/out, y_add [T, d] (dtype) or NULL, u_out [T, d]
+ *   (dtype) output.  d must be a multiple of 128 and at most 16384.
+ */
+moe_status moe_rmsnorm_residual(int64_t T, int32_t d, float* resid, const void* y_add, void* u_out,
+                                float eps, int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

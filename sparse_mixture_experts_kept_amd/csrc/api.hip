@@ -1,0 +1,281 @@
+// extern "C" entry points of libmoe: host-side validation, workspace
+// carve-up, kernel-family choice and launch sequencing on the caller's
+// stream.  The declarations, with the passages of the pages each entry point
+// realises, are in include/moe.h.
+#include <mutex>
+
+#include "../../include/moe.h"
+#include "launch.hpp"
+
+namespace {
+
+using moe::bf16_t;
+
+constexpr int64_t kDecodeMaxTokens = 64;
+constexpr size_t kRouterLdsLimit = 128 * 1024;
+constexpr int kMaxDevices = 64;
+
+int g_cu_count[kMaxDevices];
+std::mutex g_cu_mutex;
+
+// Compute units of the current device (cached per device).
+moe_status cu_count(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_cu_mutex);
+  if (g_cu_count[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return MOE_ERR_HIP;
+    g_cu_count[dev] = n;
+  }
+  *out = g_cu_count[dev];
+  return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_size(int dtype) { return dtype == moe::kDtypeBF16 ? 2 : 4; }
+
+// Shape checks shared by every entry point that takes dims.
+moe_status check_dims(const moe_dims* dims) {
+  if (!dims) return MOE_ERR_INVALID_ARGUMENT;
+  if (dims->T < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (dims->E != 8 || dims->k != 2) return MOE_ERR_UNSUPPORTED;
+  if (dims->d <= 0 || dims->f <= 0 || dims->d % 128 != 0 || dims->f % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (dims->dtype != MOE_F32 && dims->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (dims->variant < MOE_VARIANT_AUTO || dims->variant > MOE_VARIANT_PREFILL) return MOE_ERR_UNSUPPORTED;
+  if (dims->T > (int64_t{1} << 30) / dims->k) return MOE_ERR_UNSUPPORTED;  // slot ids are int32
+  // Largest row offset of h / y_rows must fit comfortably in int64 (always true) and
+  // element offsets r*f, r*d are formed in int64 on the device.
+  return MOE_OK;
+}
+
+bool use_decode(const moe_dims* dims) {
+  if (dims->variant == MOE_VARIANT_DECODE) return true;
+  if (dims->variant == MOE_VARIANT_PREFILL) return false;
+  return dims->T <= kDecodeMaxTokens;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t{255}; }
+
+struct Workspace {
+  size_t idx, w, offsets, sorted, rows, h, y_rows, total;
+};
+
+Workspace plan_workspace(const moe_dims* dims) {
+  const size_t slots = static_cast<size_t>(dims->T) * dims->k;
+  Workspace ws;
+  size_t o = 0;
+  ws.idx = o; o += align256(slots * 4);
+  ws.w = o; o += align256(slots * 4);
+  ws.offsets = o; o += align256((dims->E + 1) * 4);
+  ws.sorted = o; o += align256(slots * 4);
+  ws.rows = o; o += align256(slots * 4);
+  ws.h = o; o += align256(slots * dims->f * elem_size(dims->dtype));
+  ws.y_rows = o; o += align256(slots * dims->d * 4);
+  ws.total = o;
+  return ws;
+}
+
+moe_status run_router(const moe_dims* dims, const void* x, const void* w_gate, const float* bias, int32_t* idx,
+                      float* w, float* logits, hipStream_t s) {
+  int n_cu = 0;
+  moe_status st = cu_count(&n_cu);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_router(dims->dtype, x, w_gate, bias, idx, w, logits, dims->T, dims->d, n_cu, s));
+}
+
+moe_status run_up(const moe_dims* dims, const void* x, const int32_t* offs, const int32_t* sorted, const void* w1,
+                  const void* w3, void* h, hipStream_t s) {
+  if (dims->dtype == MOE_F32)
+    return hip_status(moe::launch_up_f32(static_cast<const float*>(x), offs, sorted, static_cast<const float*>(w1),
+                                         static_cast<const float*>(w3), static_cast<float*>(h), dims->T * dims->k,
+                                         dims->d, dims->f, s));
+  const bf16_t* xb = static_cast<const bf16_t*>(x);
+  const bf16_t* w1b = static_cast<const bf16_t*>(w1);
+  const bf16_t* w3b = static_cast<const bf16_t*>(w3);
+  bf16_t* hb = static_cast<bf16_t*>(h);
+  if (use_decode(dims)) return hip_status(moe::launch_up_decode(xb, offs, sorted, w1b, w3b, hb, dims->d, dims->f, s));
+  int n_cu = 0;
+  const moe_status st = cu_count(&n_cu);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_up_prefill(xb, offs, sorted, w1b, w3b, hb, dims->d, dims->f, n_cu, s));
+}
+
+moe_status run_down(const moe_dims* dims, const void* h, const int32_t* offs, const void* w2, float* y_rows,
+                    hipStream_t s) {
+  if (dims->dtype == MOE_F32)
+    return hip_status(moe::launch_down_f32(static_cast<const float*>(h), offs, static_cast<const float*>(w2), y_rows,
+                                           dims->T * dims->k, dims->d, dims->f, s));
+  const bf16_t* hb = static_cast<const bf16_t*>(h);
+  const bf16_t* w2b = static_cast<const bf16_t*>(w2);
+  if (use_decode(dims)) return hip_status(moe::launch_down_decode(hb, offs, w2b, y_rows, dims->d, dims->f, s));
+  int n_cu = 0;
+  const moe_status st = cu_count(&n_cu);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_down_prefill(hb, offs, w2b, y_rows, dims->d, dims->f, n_cu, s));
+}
+
+moe_status run_experts(const moe_dims* dims, const void* x, const int32_t* offs, const int32_t* sorted,
+                       const void* w1, const void* w3, const void* w2, void* h, float* y_rows, hipStream_t s) {
+  const moe_status st = run_up(dims, x, offs, sorted, w1, w3, h, s);
+  if (st != MOE_OK) return st;
+  return run_down(dims, h, offs, w2, y_rows, s);
+}
+
+moe_status run_combine(const moe_dims* dims, const float* y_rows, const int32_t* slot_rows, const float* w, void* y,
+                       hipStream_t s) {
+  int n_cu = 0;
+  moe_status st = cu_count(&n_cu);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_combine(dims->dtype, y_rows, slot_rows, w, y, dims->T, dims->d, n_cu, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_UNKNOWN_STATUS";
+}
+
+const char* moe_version(void) { return "1.0.0"; }
+
+moe_status moe_router_topk(const moe_dims* dims, const void* x, const void* w_gate, const float* logit_bias,
+                           int32_t* topk_idx, float* topk_w, float* logits, void* stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (static_cast<size_t>(dims->E) * dims->d * elem_size(dims->dtype) > kRouterLdsLimit) return MOE_ERR_UNSUPPORTED;
+  if (dims->T == 0) return MOE_OK;
+  if (!x || !w_gate || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(topk_idx, 8) || !aligned(topk_w, 8) ||
+      (logits && !aligned(logits, 16)) || (logit_bias && !aligned(logit_bias, 16)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return run_router(dims, x, w_gate, logit_bias, topk_idx, topk_w, logits, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* expert_offsets, int32_t* sorted_slots,
+                       int32_t* slot_rows, void* stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (dims->T == 0) return MOE_OK;
+  if (!expert_offsets || !topk_idx || !sorted_slots || !slot_rows) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(topk_idx, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_slots, 4) || !aligned(slot_rows, 4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(moe::launch_permute(topk_idx, static_cast<int32_t>(dims->T * dims->k), expert_offsets,
+                                        sorted_slots, slot_rows, nullptr, static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_grouped_swiglu(const moe_dims* dims, const void* x, const int32_t* expert_offsets,
+                              const int32_t* sorted_slots, const void* w1, const void* w3, const void* w2, void* h,
+                              float* y_rows, void* stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (dims->T == 0) return MOE_OK;
+  if (!x || !expert_offsets || !sorted_slots || !w1 || !w3 || !w2 || !h || !y_rows) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w3, 16) || !aligned(w2, 16) || !aligned(h, 16) ||
+      !aligned(y_rows, 16) || !aligned(expert_offsets, 4) || !aligned(sorted_slots, 4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return run_experts(dims, x, expert_offsets, sorted_slots, w1, w3, w2, h, y_rows, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_expert_up(const moe_dims* dims, const void* x, const int32_t* expert_offsets,
+                         const int32_t* sorted_slots, const void* w1, const void* w3, void* h, void* stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (dims->T == 0) return MOE_OK;
+  if (!x || !expert_offsets || !sorted_slots || !w1 || !w3 || !h) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w3, 16) || !aligned(h, 16) || !aligned(expert_offsets, 4) ||
+      !aligned(sorted_slots, 4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return run_up(dims, x, expert_offsets, sorted_slots, w1, w3, h, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_expert_down(const moe_dims* dims, const void* h, const int32_t* expert_offsets, const void* w2,
+                           float* y_rows, void* stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (dims->T == 0) return MOE_OK;
+  if (!h || !expert_offsets || !w2 || !y_rows) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(h, 16) || !aligned(w2, 16) || !aligned(y_rows, 16) || !aligned(expert_offsets, 4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return run_down(dims, h, expert_offsets, w2, y_rows, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_combine(const moe_dims* dims, const float* y_rows, const int32_t* slot_rows, const float* topk_w,
+                       void* y, void* stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (dims->T == 0) return MOE_OK;
+  if (!y_rows || !slot_rows || !topk_w || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(y_rows, 16) || !aligned(y, 16) || !aligned(slot_rows, 8) || !aligned(topk_w, 8))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return run_combine(dims, y_rows, slot_rows, topk_w, y, static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_gate, const float* logit_bias,
+                           const void* w1, const void* w3, const void* w2, void* y, int32_t* topk_idx_out,
+                           float* topk_w_out, int32_t* expert_counts_out, void* workspace, size_t* workspace_bytes,
+                           void* stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (!workspace_bytes) return MOE_ERR_INVALID_ARGUMENT;
+  if (static_cast<size_t>(dims->E) * dims->d * elem_size(dims->dtype) > kRouterLdsLimit) return MOE_ERR_UNSUPPORTED;
+  const Workspace plan = plan_workspace(dims);
+  if (!workspace) {
+    *workspace_bytes = plan.total;
+    return MOE_OK;
+  }
+  if (dims->T == 0) return MOE_OK;
+  if (*workspace_bytes < plan.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!x || !w_gate || !w1 || !w3 || !w2 || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(workspace, 256) || !aligned(x, 16) || !aligned(w_gate, 16) || !aligned(w1, 16) || !aligned(w3, 16) ||
+      !aligned(w2, 16) || !aligned(y, 16) || (logit_bias && !aligned(logit_bias, 16)) ||
+      (topk_idx_out && !aligned(topk_idx_out, 8)) || (topk_w_out && !aligned(topk_w_out, 8)) ||
+      (expert_counts_out && !aligned(expert_counts_out, 4)))
+    return MOE_ERR_INVALID_ARGUMENT;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* idx = topk_idx_out ? topk_idx_out : reinterpret_cast<int32_t*>(ws + plan.idx);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + plan.w);
+  int32_t* offs = reinterpret_cast<int32_t*>(ws + plan.offsets);
+  int32_t* sorted = reinterpret_cast<int32_t*>(ws + plan.sorted);
+  int32_t* rows = reinterpret_cast<int32_t*>(ws + plan.rows);
+  void* h = ws + plan.h;
+  float* y_rows = reinterpret_cast<float*>(ws + plan.y_rows);
+
+  st = run_router(dims, x, w_gate, logit_bias, idx, w, nullptr, s);
+  if (st != MOE_OK) return st;
+  st = hip_status(moe::launch_permute(idx, static_cast<int32_t>(dims->T * dims->k), offs, sorted, rows,
+                                      expert_counts_out, s));
+  if (st != MOE_OK) return st;
+  st = run_experts(dims, x, offs, sorted, w1, w3, w2, h, y_rows, s);
+  if (st != MOE_OK) return st;
+  return run_combine(dims, y_rows, rows, w, y, s);
+}
+
+moe_status moe_rmsnorm_residual(int64_t T, int32_t d, float* resid, const void* y_add, void* u_out, float eps,
+                                int32_t dtype, void* stream) {
+  if (T < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (d <= 0 || d % 128 != 0 || d > 16384) return MOE_ERR_UNSUPPORTED;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (T > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (!resid || !u_out) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(resid, 16) || !aligned(u_out, 16) || (y_add && !aligned(y_add, 16))) return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(
+      moe::launch_rmsnorm_residual(dtype, resid, y_add, u_out, T, d, eps, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Internal launchers of libmoe (host side).  Each enqueues its kernels on
+// `s` and returns the launch status; argument validation happens in api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeBF16 = 1;
+
+hipError_t launch_router(int dtype, const void* x, const void* wg, const float* bias, int32_t* idx, float* w,
+                         float* logits, int64_t T, int d, int n_cu, hipStream_t s);
+
+hipError_t launch_permute(const int32_t* idx, int32_t n_slots, int32_t* offsets, int32_t* sorted_slots,
+                          int32_t* slot_rows, int32_t* counts_out, hipStream_t s);
+
+// Expert projections.  up: h = SiLU(x w1^T) * (x w3^T) over the gathered
+// rows; down: y_rows = h w2^T.  n_slots = T * k.
+hipError_t launch_up_f32(const float* x, const int32_t* offs, const int32_t* sorted_slots, const float* w1,
+                         const float* w3, float* h, int64_t n_slots, int d, int f, hipStream_t s);
+hipError_t launch_down_f32(const float* h, const int32_t* offs, const float* w2, float* y_rows, int64_t n_slots,
+                           int d, int f, hipStream_t s);
+
+hipError_t launch_up_prefill(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
+                             const bf16_t* w3, bf16_t* h, int d, int f, int n_cu, hipStream_t s);
+hipError_t launch_down_prefill(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,
+                               int n_cu, hipStream_t s);
+
+hipError_t launch_up_decode(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
+                            const bf16_t* w3, bf16_t* h, int d, int f, hipStream_t s);
+hipError_t launch_down_decode(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,
+                              hipStream_t s);
+
+hipError_t launch_combine(int dtype, const float* y_rows, const int32_t* slot_rows, const float* topk_w, void* y,
+                          int64_t T, int d, int n_cu, hipStream_t s);
+
+hipError_t launch_rmsnorm_residual(int dtype, float* resid, const void* y_add, void* u, int64_t T, int d, float eps,
+                                   hipStream_t s);
+
+}  // namespace moe

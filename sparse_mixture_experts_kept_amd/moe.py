@@ -1,0 +1,258 @@
+"""Thin ctypes binding of libmoe.so (declared in include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch provides device memory and the current HIP stream.  The
+library must have been built (``python -m sparse_mixture_experts_kept_amd.build``);
+if it is missing, every call raises -- there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+VARIANT_AUTO, VARIANT_DECODE, VARIANT_PREFILL = 0, 1, 2
+E_EXPERTS, TOP_K = 8, 2
+
+EXPORTED = ("moe_status_string", "moe_version", "moe_router_topk", "moe_permute", "moe_grouped_swiglu",
+            "moe_expert_up", "moe_expert_down", "moe_combine", "moe_ffn_forward", "moe_rmsnorm_residual")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status, text):
+        super().__init__(f"{fn} failed: {text} ({status})")
+        self.status = status
+
+
+class MoeDims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("f", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("dtype", ctypes.c_int32), ("variant", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmoe.so and declare its signatures (cached)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run python -m sparse_mixture_experts_kept_amd.build")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.POINTER(
+        ctypes.c_size_t)
+    D = ctypes.POINTER(MoeDims)
+    sig = {
+        "moe_status_string": (ctypes.c_char_p, [I32]),
+        "moe_version": (ctypes.c_char_p, []),
+        "moe_router_topk": (I32, [D, P, P, P, P, P, P, P]),
+        "moe_permute": (I32, [D, P, P, P, P, P]),
+        "moe_grouped_swiglu": (I32, [D, P, P, P, P, P, P, P, P, P]),
+        "moe_expert_up": (I32, [D, P, P, P, P, P, P, P]),
+        "moe_expert_down": (I32, [D, P, P, P, P, P]),
+        "moe_combine": (I32, [D, P, P, P, P, P]),
+        "moe_ffn_forward": (I32, [D, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "moe_rmsnorm_residual": (I32, [I64, I32, P, P, P, F32, I32, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().moe_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        raise MoeError(fn, status, status_string(status))
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return MOE_BF16
+    if t == torch.float32:
+        return MOE_F32
+    raise ValueError(f"unsupported dtype {t}")
+
+
+def torch_dtype(code: int) -> torch.dtype:
+    return torch.bfloat16 if code == MOE_BF16 else torch.float32
+
+
+def make_dims(T, d, f, dtype, variant=VARIANT_AUTO, E=E_EXPERTS, k=TOP_K) -> MoeDims:
+    if isinstance(dtype, torch.dtype):
+        dtype = dtype_code(dtype)
+    return MoeDims(int(T), int(d), int(f), int(E), int(k), int(dtype), int(variant))
+
+
+def ptr(t):
+    """Device address of a CUDA tensor (None -> NULL).  Checks contiguity."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors passed to libmoe must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libmoe must be contiguous")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def stream_handle():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _layer_dims(x, w1, variant):
+    T, d = x.shape
+    f = w1.shape[1]
+    return make_dims(T, d, f, x.dtype, variant)
+
+
+# --------------------------------------------------------------------------- staged calls
+
+
+def router_topk(x, w_gate, logit_bias=None, return_logits=False):
+    """topk_idx [T,2] int32, topk_w [T,2] fp32 (and logits [T,8] fp32)."""
+    lib = load_library()
+    T, d = x.shape
+    dims = make_dims(T, d, 128, x.dtype)
+    idx = torch.empty((T, TOP_K), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, TOP_K), dtype=torch.float32, device=x.device)
+    logits = torch.empty((T, E_EXPERTS), dtype=torch.float32, device=x.device) if return_logits else None
+    _check("moe_router_topk", lib.moe_router_topk(ctypes.byref(dims), ptr(x), ptr(w_gate), ptr(logit_bias),
+                                                  ptr(idx), ptr(w), ptr(logits), stream_handle()))
+    return (idx, w, logits) if return_logits else (idx, w)
+
+
+def permute(topk_idx, d=128, f=128):
+    """expert_offsets [9], sorted_slots [T*2], slot_rows [T*2] (int32)."""
+    lib = load_library()
+    T = topk_idx.shape[0]
+    dims = make_dims(T, d, f, MOE_BF16)
+    offs = torch.zeros((E_EXPERTS + 1,), dtype=torch.int32, device=topk_idx.device)
+    sorted_slots = torch.empty((T * TOP_K,), dtype=torch.int32, device=topk_idx.device)
+    slot_rows = torch.empty((T * TOP_K,), dtype=torch.int32, device=topk_idx.device)
+    _check("moe_permute", lib.moe_permute(ctypes.byref(dims), ptr(topk_idx), ptr(offs), ptr(sorted_slots),
+                                          ptr(slot_rows), stream_handle()))
+    return offs, sorted_slots, slot_rows
+
+
+def grouped_swiglu(x, expert_offsets, sorted_slots, w1, w3, w2, variant=VARIANT_AUTO):
+    """h [T*2, f] (x's dtype) and y_rows [T*2, d] fp32, in expert-major order."""
+    lib = load_library()
+    dims = _layer_dims(x, w1, variant)
+    T, d = x.shape
+    f = w1.shape[1]
+    h = torch.empty((T * TOP_K, f), dtype=x.dtype, device=x.device)
+    y_rows = torch.empty((T * TOP_K, d), dtype=torch.float32, device=x.device)
+    _check("moe_grouped_swiglu", lib.moe_grouped_swiglu(ctypes.byref(dims), ptr(x), ptr(expert_offsets),
+                                                        ptr(sorted_slots), ptr(w1), ptr(w3), ptr(w2), ptr(h),
+                                                        ptr(y_rows), stream_handle()))
+    return h, y_rows
+
+
+def expert_up(x, expert_offsets, sorted_slots, w1, w3, variant=VARIANT_AUTO, h=None):
+    """h [T*2, f] = SiLU(x w1^T) * (x w3^T) over the expert-major rows."""
+    lib = load_library()
+    dims = _layer_dims(x, w1, variant)
+    T = x.shape[0]
+    if h is None:
+        h = torch.empty((T * TOP_K, w1.shape[1]), dtype=x.dtype, device=x.device)
+    _check("moe_expert_up", lib.moe_expert_up(ctypes.byref(dims), ptr(x), ptr(expert_offsets), ptr(sorted_slots),
+                                              ptr(w1), ptr(w3), ptr(h), stream_handle()))
+    return h
+
+
+def expert_down(h, expert_offsets, w2, T, variant=VARIANT_AUTO, y_rows=None):
+    """y_rows [T*2, d] fp32 = h w2^T over the expert-major rows."""
+    lib = load_library()
+    d, f = w2.shape[1], w2.shape[2]
+    dims = make_dims(T, d, f, h.dtype, variant)
+    if y_rows is None:
+        y_rows = torch.empty((T * TOP_K, d), dtype=torch.float32, device=h.device)
+    _check("moe_expert_down", lib.moe_expert_down(ctypes.byref(dims), ptr(h), ptr(expert_offsets), ptr(w2),
+                                                  ptr(y_rows), stream_handle()))
+    return y_rows
+
+
+def combine(y_rows, slot_rows, topk_w, out_dtype):
+    """y [T, d] = w[:,0] * y_rows[slot_rows[2t]] + w[:,1] * y_rows[slot_rows[2t+1]]."""
+    lib = load_library()
+    T = topk_w.shape[0]
+    d = y_rows.shape[1]
+    dims = make_dims(T, d, 128, out_dtype)
+    y = torch.empty((T, d), dtype=out_dtype, device=y_rows.device)
+    _check("moe_combine", lib.moe_combine(ctypes.byref(dims), ptr(y_rows), ptr(slot_rows), ptr(topk_w), ptr(y),
+                                          stream_handle()))
+    return y
+
+
+# --------------------------------------------------------------------------- whole layer
+
+
+def workspace_size(T, d, f, dtype, variant=VARIANT_AUTO) -> int:
+    lib = load_library()
+    dims = make_dims(T, d, f, dtype, variant)
+    n = ctypes.c_size_t(0)
+    _check("moe_ffn_forward", lib.moe_ffn_forward(ctypes.byref(dims), None, None, None, None, None, None, None,
+                                                  None, None, None, None, ctypes.byref(n), None))
+    return n.value
+
+
+def alloc_workspace(T, d, f, dtype, variant=VARIANT_AUTO, device="cuda"):
+    n = workspace_size(T, d, f, dtype, variant)
+    return torch.empty((max(n, 256),), dtype=torch.uint8, device=device)
+
+
+class FFN:
+    """The whole layer with preallocated outputs and workspace, for repeated
+    calls on the same shapes (what the benchmark times)."""
+
+    def __init__(self, x, w_gate, w1, w3, w2, logit_bias=None, variant=VARIANT_AUTO, routing=True):
+        self.lib = load_library()
+        self.dims = _layer_dims(x, w1, variant)
+        T, d = x.shape
+        self.args = (x, w_gate, logit_bias, w1, w3, w2)
+        self.y = torch.empty((T, d), dtype=x.dtype, device=x.device)
+        self.idx = torch.empty((T, TOP_K), dtype=torch.int32, device=x.device) if routing else None
+        self.w = torch.empty((T, TOP_K), dtype=torch.float32, device=x.device) if routing else None
+        self.counts = torch.empty((E_EXPERTS,), dtype=torch.int32, device=x.device) if routing else None
+        self.ws = alloc_workspace(T, d, w1.shape[1], x.dtype, variant, x.device)
+        self.ws_bytes = ctypes.c_size_t(self.ws.numel())
+
+    def __call__(self, stream=None):
+        x, w_gate, bias, w1, w3, w2 = self.args
+        s = ctypes.c_void_p(stream) if stream is not None else stream_handle()
+        _check("moe_ffn_forward", self.lib.moe_ffn_forward(
+            ctypes.byref(self.dims), ptr(x), ptr(w_gate), ptr(bias), ptr(w1), ptr(w3), ptr(w2), ptr(self.y),
+            ptr(self.idx), ptr(self.w), ptr(self.counts), ptr(self.ws), ctypes.byref(self.ws_bytes), s))
+        return self.y
+
+
+def ffn_forward(x, w_gate, w1, w3, w2, logit_bias=None, variant=VARIANT_AUTO, return_routing=False):
+    """y [T, d] (x's dtype); with return_routing also (topk_idx, topk_w, counts)."""
+    layer = FFN(x, w_gate, w1, w3, w2, logit_bias, variant, routing=True)
+    y = layer()
+    if return_routing:
+        return y, layer.idx, layer.w, layer.counts
+    return y
+
+
+def rmsnorm_residual(resid, y_add, out_dtype, eps=1e-5):
+    """resid += y_add (in place, if given); returns u = resid / rms(resid)."""
+    lib = load_library()
+    T, d = resid.shape
+    u = torch.empty((T, d), dtype=out_dtype, device=resid.device)
+    _check("moe_rmsnorm_residual", lib.moe_rmsnorm_residual(T, d, ptr(resid), ptr(y_add), ptr(u), eps,
+                                                            dtype_code(out_dtype), stream_handle()))
+    return u

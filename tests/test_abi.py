@@ -1,0 +1,166 @@
+"""C-ABI library: it loads, exports every function include/moe.h declares,
+and rejects bad arguments on the host before touching the GPU (CPU only)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from sparse_mixture_experts_kept_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _lib():
+    if not os.path.exists(moe.LIB_PATH):
+        from sparse_mixture_experts_kept_amd import build
+
+        build.build()
+    return moe.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for required in ("moe_router_topk", "moe_permute", "moe_grouped_swiglu", "moe_combine", "moe_ffn_forward"):
+        assert required in names
+    assert set(names) == set(moe.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (moe_[a-z_]+)\b", out))
+    assert set(_declared_functions()) <= exported
+    assert moe.status_string(moe.MOE_ERR_UNSUPPORTED) == "MOE_ERR_UNSUPPORTED"
+    assert lib.moe_version().decode().count(".") == 2
+
+
+needs_no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                                  reason="host-validation checks with fake pointers run only where no GPU exists")
+
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: every call below must fail validation
+MISALIGNED = ctypes.c_void_p(0x100002)
+
+
+def _dims(**kw):
+    base = dict(T=16, d=256, f=512, dtype=moe.MOE_BF16, variant=0)
+    base.update(kw)
+    return moe.make_dims(**base)
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), moe.MOE_ERR_INVALID_ARGUMENT),
+    (dict(d=200), moe.MOE_ERR_UNSUPPORTED),
+    (dict(f=100), moe.MOE_ERR_UNSUPPORTED),
+    (dict(d=0), moe.MOE_ERR_UNSUPPORTED),
+    (dict(dtype=7), moe.MOE_ERR_UNSUPPORTED),
+    (dict(variant=3), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=1 << 31), moe.MOE_ERR_UNSUPPORTED),
+])
+def test_bad_dims_are_rejected(kw, status):
+    lib = _lib()
+    dims = _dims(**kw)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_router_topk(ctypes.byref(dims), FAKE, FAKE, None, FAKE, FAKE, None, None) == status
+    assert lib.moe_permute(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, None) == status
+    assert lib.moe_grouped_swiglu(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
+    assert lib.moe_combine(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, None) == status
+    assert lib.moe_ffn_forward(ctypes.byref(dims), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, None,
+                               None, ctypes.byref(n), None) == status
+
+
+@needs_no_gpu
+def test_wrong_expert_count_or_k():
+    lib = _lib()
+    for E, k in ((4, 2), (8, 1), (16, 2), (8, 3)):
+        dims = moe.make_dims(16, 256, 512, moe.MOE_BF16, E=E, k=k)
+        assert lib.moe_router_topk(ctypes.byref(dims), FAKE, FAKE, None, FAKE, FAKE, None, None) == \
+            moe.MOE_ERR_UNSUPPORTED
+
+
+@needs_no_gpu
+def test_null_and_misaligned_pointers():
+    lib = _lib()
+    dims = _dims()
+    INV = moe.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_router_topk(None, FAKE, FAKE, None, FAKE, FAKE, None, None) == INV
+    assert lib.moe_router_topk(ctypes.byref(dims), None, FAKE, None, FAKE, FAKE, None, None) == INV
+    assert lib.moe_router_topk(ctypes.byref(dims), MISALIGNED, FAKE, None, FAKE, FAKE, None, None) == INV
+    assert lib.moe_permute(ctypes.byref(dims), FAKE, None, FAKE, FAKE, None) == INV
+    assert lib.moe_permute(ctypes.byref(dims), FAKE, FAKE, MISALIGNED, FAKE, None) == INV
+    assert lib.moe_grouped_swiglu(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == INV
+    assert lib.moe_grouped_swiglu(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, MISALIGNED, FAKE,
+                                  None) == INV
+    assert lib.moe_combine(ctypes.byref(dims), FAKE, FAKE, FAKE, None, None) == INV
+    assert lib.moe_combine(ctypes.byref(dims), MISALIGNED, FAKE, FAKE, FAKE, None) == INV
+    assert lib.moe_rmsnorm_residual(4, 256, None, None, FAKE, 1e-5, 1, None) == INV
+    assert lib.moe_rmsnorm_residual(-1, 256, FAKE, None, FAKE, 1e-5, 1, None) == INV
+    assert lib.moe_rmsnorm_residual(4, 250, FAKE, None, FAKE, 1e-5, 1, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_rmsnorm_residual(4, 256, FAKE, None, FAKE, 1e-5, 5, None) == moe.MOE_ERR_UNSUPPORTED
+
+
+@needs_no_gpu
+def test_router_lds_limit():
+    lib = _lib()
+    dims = moe.make_dims(16, 8192 + 128, 512, moe.MOE_BF16)
+    assert lib.moe_router_topk(ctypes.byref(dims), FAKE, FAKE, None, FAKE, FAKE, None, None) == \
+        moe.MOE_ERR_UNSUPPORTED
+    dims = moe.make_dims(16, 4096 + 128, 512, moe.MOE_F32)
+    assert lib.moe_router_topk(ctypes.byref(dims), FAKE, FAKE, None, FAKE, FAKE, None, None) == \
+        moe.MOE_ERR_UNSUPPORTED
+
+
+@needs_no_gpu
+def test_workspace_query_and_too_small():
+    lib = _lib()
+    T, d, f = 4096, 4096, 14336
+    dims = moe.make_dims(T, d, f, moe.MOE_BF16)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_ffn_forward(ctypes.byref(dims), None, None, None, None, None, None, None, None, None, None,
+                               None, ctypes.byref(n), None) == moe.MOE_OK
+    slots = T * 2
+    # h (bf16) and y_rows (fp32) dominate; routing arrays are small
+    assert n.value >= slots * f * 2 + slots * d * 4
+    assert n.value < slots * f * 2 + slots * d * 4 + (1 << 20)
+    small = ctypes.c_size_t(n.value - 1)
+    ws = ctypes.c_void_p(0x200000)
+    assert lib.moe_ffn_forward(ctypes.byref(dims), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, None, ws,
+                               ctypes.byref(small), None) == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert lib.moe_ffn_forward(ctypes.byref(dims), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, None, ws,
+                               None, None) == moe.MOE_ERR_INVALID_ARGUMENT
+    big = ctypes.c_size_t(n.value)
+    assert lib.moe_ffn_forward(ctypes.byref(dims), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, None,
+                               ctypes.c_void_p(0x200010), ctypes.byref(big), None) == moe.MOE_ERR_INVALID_ARGUMENT
+
+
+@needs_no_gpu
+def test_zero_tokens_is_a_no_op():
+    lib = _lib()
+    dims = _dims(T=0)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_router_topk(ctypes.byref(dims), None, None, None, None, None, None, None) == moe.MOE_OK
+    assert lib.moe_permute(ctypes.byref(dims), None, None, None, None, None) == moe.MOE_OK
+    assert lib.moe_grouped_swiglu(ctypes.byref(dims), None, None, None, None, None, None, None, None, None) == \
+        moe.MOE_OK
+    assert lib.moe_combine(ctypes.byref(dims), None, None, None, None, None) == moe.MOE_OK
+    assert lib.moe_ffn_forward(ctypes.byref(dims), None, None, None, None, None, None, None, None, None, None,
+                               None, ctypes.byref(n), None) == moe.MOE_OK
+    assert lib.moe_rmsnorm_residual(0, 256, None, None, None, 1e-5, 1, None) == moe.MOE_OK
+
+
+def test_binding_refuses_cpu_tensors():
+    with pytest.raises(ValueError):
+        moe.ptr(torch.zeros(4))

@@ -1,0 +1,308 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Acceptance rules:
+* routing (expert ids, per-expert counts) bit-exact for every token whose
+  oracle 2nd-3rd score gap exceeds 1e-4; near-tie tokens must hold a valid
+  top-2 pair within 1e-4 and are checked under the pair the GPU chose;
+* gates within 1e-5 of the oracle's (fp32 scores vs fp64);
+* outputs: max|gpu - ref| <= 2e-2 * max|ref| + 2e-3 for bf16 (bf16 inputs,
+  fp32 accumulation, bf16 hidden and output roundings), and
+  <= 1e-5 * max|ref| for fp32.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from sparse_mixture_experts_kept_amd import inputs, moe
+
+pytestmark = pytest.mark.gpu
+
+GAP = 1e-4
+
+
+def _cpu(t):
+    return None if t is None else t.detach().cpu()
+
+
+def _tol(dtype, ref):
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    return 1e-5 * scale if dtype == "f32" else 2e-2 * scale + 2e-3
+
+
+def _widen_experts(layer):
+    w1, w3, w2 = _cpu(layer["w1"]), _cpu(layer["w3"]), _cpu(layer["w2"])
+    return lambda e: (O._f64(w1[e]), O._f64(w3[e]), O._f64(w2[e]))
+
+
+def _check_routing(idx_gpu, w_gpu, ref, tokens=None):
+    logits = ref["logits"]
+    gap = O.second_third_gap(logits)
+    clear = gap > GAP
+    gi = idx_gpu if tokens is None else idx_gpu[tokens]
+    gw = w_gpu if tokens is None else w_gpu[tokens]
+    np.testing.assert_array_equal(gi[clear], ref["idx"][clear])
+    assert O.is_valid_top2(logits, gi, GAP).all()
+    np.testing.assert_allclose(gw[clear], ref["gates"][clear], atol=1e-5, rtol=0)
+    np.testing.assert_allclose(gw.sum(axis=1), 1.0, atol=1e-6)
+    assert (gw >= 0).all()
+    return clear
+
+
+def run_and_check(layer, variant=moe.VARIANT_AUTO, sample=None):
+    """Whole layer on the GPU vs the oracle on all tokens (or a sample)."""
+    dims = layer["dims"]
+    x = layer["x"]
+    y, idx, w, counts = moe.ffn_forward(x, layer["w_gate"], layer["w1"], layer["w3"], layer["w2"],
+                                        logit_bias=layer.get("logit_bias"), variant=variant, return_routing=True)
+    torch.cuda.synchronize()
+    idx_g = idx.cpu().numpy().astype(np.int64)
+    w_g = w.cpu().numpy().astype(np.float64)
+    counts_g = counts.cpu().numpy()
+    np.testing.assert_array_equal(counts_g, np.bincount(idx_g.reshape(-1), minlength=8))
+    tok = np.arange(dims["T"]) if sample is None else np.asarray(sample)
+    xs = _cpu(x)[tok]
+    bias = _cpu(layer.get("logit_bias"))
+    widen = _widen_experts(layer)
+    ref = O.moe_ffn(xs, _cpu(layer["w_gate"]), None, None, None, logit_bias=bias, widen_expert=widen)
+    clear = _check_routing(idx_g[tok], w_g[tok], ref)
+    if sample is None:
+        # per-expert counts over the tokens whose routing is decided beyond the tie margin
+        np.testing.assert_array_equal(np.bincount(idx_g[clear].reshape(-1), minlength=8),
+                                      np.bincount(ref["idx"][clear].reshape(-1), minlength=8))
+    # outputs, under the assignment the GPU made (identical to the oracle's on clear tokens)
+    if not np.array_equal(idx_g[tok], ref["idx"]):
+        ref = O.moe_ffn(xs, _cpu(layer["w_gate"]), None, None, None, logit_bias=bias, idx=idx_g[tok],
+                        widen_expert=widen)
+    yg = y.float().cpu().numpy().astype(np.float64)[tok]
+    err = np.abs(yg - ref["y"]).max() if yg.size else 0.0
+    tol = _tol(dims["dtype"], ref["y"])
+    assert err <= tol, f"max |gpu - oracle| = {err:.4e} > {tol:.4e}"
+    return dict(y=y, idx=idx, w=w, counts=counts, err=err, tol=tol)
+
+
+def _layer(T, d, f, dtype="bf16", seed=0, skew=False, dev="cuda"):
+    return inputs.make_custom(T, d, f, dtype=dtype, seed=seed, device=dev, skew=skew)
+
+
+# --------------------------------------------------------------------------- small / medium layers, every variant
+
+
+def test_tiny_fp32_workload():
+    layer = inputs.make_workload("tiny_fp32", device="cuda")
+    run_and_check(layer)
+
+
+@pytest.mark.parametrize("T,d,f", [(1, 128, 256), (64, 128, 384), (700, 256, 512)])
+def test_fp32_shapes(T, d, f):
+    run_and_check(_layer(T, d, f, dtype="f32", seed=T))
+
+
+@pytest.mark.parametrize("T,d,f", [(1200, 512, 1024), (1500, 256, 512), (777, 384, 640), (300, 256, 384)])
+def test_bf16_prefill_kernels(T, d, f):
+    # several m-tiles per expert with ragged tails; d=384 leaves a half-empty
+    # n-tile in the down projection; f=640 an odd number of k-steps
+    run_and_check(_layer(T, d, f, seed=T), variant=moe.VARIANT_PREFILL)
+
+
+@pytest.mark.parametrize("T", [1, 2, 5, 17])
+def test_bf16_prefill_kernels_tiny_batches(T):
+    run_and_check(_layer(T, 256, 512, seed=100 + T), variant=moe.VARIANT_PREFILL)
+
+
+@pytest.mark.parametrize("T,d,f", [(32, 512, 1024), (64, 256, 512), (1, 256, 512), (7, 128, 256)])
+def test_bf16_decode_kernels(T, d, f):
+    run_and_check(_layer(T, d, f, seed=200 + T), variant=moe.VARIANT_DECODE)
+
+
+@pytest.mark.parametrize("T", [200, 600])
+def test_bf16_decode_kernels_many_rows_per_expert(T):
+    # more than 16 and more than 64 rows per expert: several token groups and passes
+    run_and_check(_layer(T, 256, 384, seed=300 + T), variant=moe.VARIANT_DECODE)
+
+
+@pytest.mark.parametrize("variant", [moe.VARIANT_DECODE, moe.VARIANT_PREFILL])
+def test_all_tokens_on_two_experts(variant):
+    # degenerate routing: a large bias sends every token to experts 3 then 6;
+    # the other six experts are empty
+    layer = _layer(300, 256, 512, seed=7)
+    b = torch.zeros(8, dtype=torch.float32)
+    b[3], b[6] = 60.0, 40.0
+    layer["logit_bias"] = b.cuda()
+    out = run_and_check(layer, variant=variant)
+    np.testing.assert_array_equal(out["counts"].cpu().numpy(), [0, 0, 0, 300, 0, 0, 300, 0])
+    assert (out["idx"][:, 0] == 3).all() and (out["idx"][:, 1] == 6).all()
+
+
+@pytest.mark.parametrize("variant", [moe.VARIANT_DECODE, moe.VARIANT_PREFILL])
+def test_skewed_routing_small(variant):
+    layer = _layer(900, 256, 512, seed=11, skew=True)
+    out = run_and_check(layer, variant=variant)
+    c = out["counts"].cpu().numpy()
+    assert c.max() > 3 * c.min()
+
+
+def test_variants_agree():
+    layer = _layer(48, 256, 512, seed=12)
+    ys = []
+    for v in (moe.VARIANT_DECODE, moe.VARIANT_PREFILL):
+        ys.append(moe.ffn_forward(layer["x"], layer["w_gate"], layer["w1"], layer["w3"], layer["w2"], variant=v))
+    torch.cuda.synchronize()
+    a, b = ys[0].float(), ys[1].float()
+    assert (a - b).abs().max().item() <= 2e-2 * a.abs().max().item() + 2e-3
+
+
+def test_deterministic():
+    layer = _layer(1000, 256, 512, seed=13)
+    f = moe.FFN(layer["x"], layer["w_gate"], layer["w1"], layer["w3"], layer["w2"])
+    y1 = f().clone()
+    y2 = f().clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_batch_split_matches_whole_batch():
+    layer = _layer(600, 256, 512, seed=14)
+    args = (layer["w_gate"], layer["w1"], layer["w3"], layer["w2"])
+    y, idx, _, _ = moe.ffn_forward(layer["x"], *args, return_routing=True)
+    ya, ia, _, _ = moe.ffn_forward(layer["x"][:250].contiguous(), *args, return_routing=True)
+    yb, ib, _, _ = moe.ffn_forward(layer["x"][250:].contiguous(), *args, return_routing=True)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([ia, ib]), idx)  # routing is per token
+    d = (torch.cat([ya, yb]).float() - y.float()).abs().max().item()
+    assert d <= 2e-2 * y.float().abs().max().item() + 2e-3
+
+
+# --------------------------------------------------------------------------- staged calls
+
+
+def test_router_parity():
+    for dtype, T, d in (("bf16", 513, 4096), ("f32", 100, 128), ("bf16", 64, 8192)):
+        layer = _layer(T, d, 128, dtype=dtype, seed=15)
+        idx, w, logits = moe.router_topk(layer["x"], layer["w_gate"], return_logits=True)
+        torch.cuda.synchronize()
+        ref = O.moe_ffn(_cpu(layer["x"]), _cpu(layer["w_gate"]), None, None, None,
+                        widen_expert=lambda e: (np.zeros((1, d)), np.zeros((1, d)), np.zeros((d, 1))))
+        xs = O._f64(_cpu(layer["x"]))
+        wg = O._f64(_cpu(layer["w_gate"]))
+        bound = 1e-5 * np.linalg.norm(xs, axis=1)[:, None] * np.linalg.norm(wg, axis=1)[None, :]
+        assert (np.abs(logits.cpu().numpy() - ref["logits"]) <= bound).all()
+        _check_routing(idx.cpu().numpy().astype(np.int64), w.cpu().numpy().astype(np.float64), ref)
+
+
+def test_router_exact_ties_go_to_lower_index():
+    # x = 1 in one coordinate, rows of W_g chosen so scores tie exactly
+    d = 128
+    x = torch.zeros((3, d), dtype=torch.float32)
+    x[:, 0] = 1.0
+    wg = torch.zeros((8, d), dtype=torch.float32)
+    wg[:, 0] = torch.tensor([1.0, 2.0, 2.0, 2.0, 0.0, 0.0, 0.0, 0.0])
+    idx, w = moe.router_topk(x.cuda(), wg.cuda())
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), [[1, 2]] * 3)
+    np.testing.assert_allclose(w.cpu().numpy(), 0.5, atol=0)
+
+
+def test_permute_matches_oracle_bit_exact():
+    for T, bias in ((4096, None), (8192, [3.0, 0, 0, 0, 0, 0, 0, -3.0]), (1, None), (1000, [50.0, 40, 0, 0, 0, 0, 0, 0])):
+        g = torch.Generator().manual_seed(T)
+        logits = torch.randn((T, 8), generator=g)
+        if bias is not None:
+            logits += torch.tensor(bias)
+        idx = torch.topk(logits, 2, dim=1).indices.to(torch.int32)
+        offs, sorted_slots, slot_rows = moe.permute(idx.cuda())
+        torch.cuda.synchronize()
+        eo, es, er = O.expert_permutation(idx.numpy(), 8)
+        np.testing.assert_array_equal(offs.cpu().numpy(), eo)
+        np.testing.assert_array_equal(sorted_slots.cpu().numpy(), es)
+        np.testing.assert_array_equal(slot_rows.cpu().numpy(), er)
+
+
+@pytest.mark.parametrize("variant", [moe.VARIANT_DECODE, moe.VARIANT_PREFILL])
+def test_staged_path_under_the_oracle_assignment(variant):
+    """Feed the oracle's own routing (ids and gates) through permute ->
+    grouped_swiglu -> combine; checks h, y_rows and y element by element."""
+    T, d, f = 640, 256, 512
+    layer = _layer(T, d, f, seed=16)
+    xc, wgc, w1c, w3c, w2c = (_cpu(layer[k]) for k in ("x", "w_gate", "w1", "w3", "w2"))
+    ref = O.moe_ffn(xc, wgc, w1c, w3c, w2c)
+    idx = torch.from_numpy(ref["idx"].astype(np.int32)).cuda()
+    gates = torch.from_numpy(ref["gates"].astype(np.float32)).cuda()
+    offs, sorted_slots, slot_rows = moe.permute(idx, d, f)
+    h, y_rows = moe.grouped_swiglu(layer["x"], offs, sorted_slots, layer["w1"], layer["w3"], layer["w2"],
+                                   variant=variant)
+    y = moe.combine(y_rows, slot_rows, gates, torch.bfloat16)
+    torch.cuda.synchronize()
+    _, es, _ = O.expert_permutation(ref["idx"], 8)
+    tok = es // 2
+    exp_of_row = ref["idx"].reshape(-1)[es]
+    hg = O._f64(h.cpu())
+    h_ref = np.zeros((T * 2, f))
+    yr_ref = np.zeros((T * 2, d))
+    for e in range(8):
+        rows = np.nonzero(exp_of_row == e)[0]
+        h_ref[rows] = O.swiglu_hidden(xc[tok[rows]], w1c[e], w3c[e])
+        # down projection of the GPU's own bf16 h: only fp32 accumulation separates them
+        yr_ref[rows] = hg[rows] @ O._f64(w2c[e]).T
+    assert np.abs(hg - h_ref).max() <= 2e-2 * np.abs(h_ref).max() + 2e-3
+    assert np.abs(y_rows.cpu().numpy() - yr_ref).max() <= 1e-4 * np.abs(yr_ref).max()
+    yg = O._f64(y.cpu())
+    assert np.abs(yg - ref["y"]).max() <= _tol("bf16", ref["y"])
+
+
+def test_rmsnorm_residual():
+    T, d = 37, 4096
+    g = torch.Generator().manual_seed(17)
+    resid = torch.randn((T, d), generator=g) * 3
+    add = torch.randn((T, d), generator=g).to(torch.bfloat16)
+    r_gpu = resid.cuda()
+    u = moe.rmsnorm_residual(r_gpu, add.cuda(), torch.bfloat16, eps=1e-5)
+    torch.cuda.synchronize()
+    r_ref = O._f64(resid) + O._f64(add)
+    np.testing.assert_allclose(r_gpu.cpu().numpy(), r_ref, rtol=1e-6, atol=1e-6)
+    u_ref = O.rmsnorm(r_ref, 1e-5)
+    assert np.abs(O._f64(u.cpu()) - u_ref).max() <= 1e-2 * np.abs(u_ref).max()
+    u32 = moe.rmsnorm_residual(r_gpu, None, torch.float32, eps=1e-5)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(u32.cpu().numpy(), O.rmsnorm(r_gpu.cpu(), 1e-5), rtol=1e-5, atol=1e-6)
+
+
+def test_errors_with_real_tensors():
+    layer = _layer(16, 256, 512, seed=18)
+    lib = moe.load_library()
+    import ctypes
+    dims = moe.make_dims(16, 256, 512, moe.MOE_BF16)
+    ws = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    n = ctypes.c_size_t(1024)
+    y = torch.empty((16, 256), dtype=torch.bfloat16, device="cuda")
+    st = lib.moe_ffn_forward(ctypes.byref(dims), moe.ptr(layer["x"]), moe.ptr(layer["w_gate"]), None,
+                             moe.ptr(layer["w1"]), moe.ptr(layer["w3"]), moe.ptr(layer["w2"]), moe.ptr(y), None,
+                             None, None, moe.ptr(ws), ctypes.byref(n), moe.stream_handle())
+    assert st == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+    with pytest.raises(moe.MoeError):
+        moe.ffn_forward(layer["x"][:, :200].contiguous(), layer["w_gate"][:, :200].contiguous(), layer["w1"],
+                        layer["w3"], layer["w2"])
+    y0 = moe.ffn_forward(layer["x"][:0], layer["w_gate"], layer["w1"], layer["w3"], layer["w2"])
+    assert y0.shape == (0, 256)
+
+
+# --------------------------------------------------------------------------- full Mixtral-sized layers (sampled)
+
+
+def test_decode_workload_full():
+    # T = 32: the oracle checks every token
+    layer = inputs.make_workload("decode", device="cuda")
+    run_and_check(layer)
+
+
+@pytest.mark.parametrize("name", ["prefill", "prefill_skewed"])
+def test_prefill_workloads_sampled(name):
+    layer = inputs.make_workload(name, device="cuda")
+    rng = np.random.default_rng(5)
+    sample = np.sort(rng.choice(layer["dims"]["T"], size=48, replace=False))
+    sample[-1] = layer["dims"]["T"] - 1
+    out = run_and_check(layer, sample=sample)
+    if name == "prefill_skewed":
+        c = out["counts"].cpu().numpy() / (2 * layer["dims"]["T"])
+        assert c.max() > 0.35 and c.min() < 0.06
