@@ -40,8 +40,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample", type=int, default=512, help="tokens of the prefill workload the oracle runs")
+    p.add_argument("--cpu-sample", type=int, default=4096, help="tokens of the prefill workload the oracle runs")
+    p.add_argument("--cpu-repeats", type=int, default=3)
     p.add_argument("--only", choices=["prefill", "decode", "all"], default="all")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -87,7 +90,7 @@ def staged_timing(L, steps, torch, moe, variant):
     return out
 
 
-def cpu_baseline(L, sample_tokens):
+def cpu_baseline(L, sample_tokens, repeats):
     """The fp64 oracle on `sample_tokens` tokens of the workload (weights
     widened to fp64 beforehand, not timed)."""
     import numpy as np
@@ -107,13 +110,14 @@ def cpu_baseline(L, sample_tokens):
     xs = x[tok]
     wg = L["w_gate"].cpu()
     t0 = time.perf_counter()
-    moe_oracle.moe_ffn(xs, wg, None, None, None, widen_expert=lambda e: (w1[e], w3[e], w2[e]))
-    dt = time.perf_counter() - t0
+    for _ in range(repeats):
+        moe_oracle.moe_ffn(xs, wg, None, None, None, widen_expert=lambda e: (w1[e], w3[e], w2[e]))
+    dt = (time.perf_counter() - t0) / repeats
     blas = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
     threads = blas[0]["num_threads"] if blas else 1
     return {"value": len(tok) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(tok)} of {T} tokens of the prefill layer (per-token independent), fp64 NumPy; "
-                      f"{dt:.1f} s compute, weight widening to fp64 ({widen_s:.1f} s) excluded; "
+            "sample": f"{len(tok)} of {T} tokens of the prefill layer, fp64 NumPy, mean of {repeats} runs; "
+                      f"{dt:.2f} s compute per run, weight widening to fp64 ({widen_s:.1f} s) excluded; "
                       f"{len(os.sched_getaffinity(0))} cores visible, BLAS "
                       f"{blas[0].get('internal_api', '?') if blas else '?'} {threads} threads"}
 
@@ -131,6 +135,15 @@ def main():
     from sparse_mixture_experts_kept_amd import inputs, moe
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": src.numel() * 2, "copy_probe_bytes_written": dst.numel() * 2,
+                          "launches": 3}))
+        return
     moe.load_library()
     dev = "cuda"
     m = A.MIXTRAL
@@ -164,7 +177,7 @@ def main():
         })
         if not args.no_cpu_baseline:
             _log("cpu baseline: running the fp64 oracle on a token sample")
-            result["cpu_baseline"] = cpu_baseline(L, args.cpu_sample)
+            result["cpu_baseline"] = cpu_baseline(L, args.cpu_sample, args.cpu_repeats)
         del layer, L
         torch.cuda.empty_cache()
 

@@ -10,12 +10,15 @@
 // sorted_slots[r] / k, the gather fused into the A-tile load).
 //
 // Design (gfx950): persistent workgroups of 256 threads (4 waves, one per
-// SIMD), 256 x 256 x 64 block tiles, each wave a 128 x 128 sub-tile built
-// from v_mfma_f32_16x16x32_bf16 with fp32 accumulators.  A and B tiles are
-// double-buffered in LDS (2 x 64 KiB) and filled one k-step ahead with
-// direct global->LDS loads (global_load_lds_dwordx4), so no registers are
-// spent on staging.  LDS rows are 128 B with the 16-byte chunk index
-// XOR-swizzled by the row so the fragment reads spread over all banks.  For
+// SIMD), 256 x 256 block tiles stepped 32 deep in k, each wave a 128 x 128
+// sub-tile built from v_mfma_f32_16x16x32_bf16 with fp32 accumulators.  A and
+// B tiles live in a 4-deep LDS ring (4 x 32 KiB) filled by direct
+// global->LDS loads (global_load_lds_dwordx4, no staging registers); three
+// k-steps of loads are in flight while the MFMAs consume the fourth, and
+// each step waits only for its own loads (s_waitcnt vmcnt(N)) before one
+// barrier.  LDS rows are 64 B with the 16-byte chunk index XOR-swizzled by
+// the row so that the fragment reads of 16 lanes hit 16 distinct 4-bank
+// groups (measured: zero bank conflicts).  For
 // the up projection the 256 B rows of a tile are 128 gate rows and the same
 // 128 up rows, so every wave holds matching gate/up accumulators and applies
 // SiLU(g)*u in registers before one bf16 rounding.
@@ -33,16 +36,37 @@ namespace moe {
 
 constexpr int kPBM = 256;
 constexpr int kPBN = 256;
-constexpr int kPBK = 64;
+constexpr int kPBK = 32;       // k depth of one pipeline stage
+constexpr int kStages = 4;     // LDS ring depth
 constexpr int kPThreads = 256;
 constexpr int kXcds = 8;
 constexpr int kGroupN = 8;
+// Per wave and stage: 4 A loads + 4 B loads of 1 KiB (16 rows x 64 B).
+constexpr int kLoadsPerStage = 8;
 
 #define GLOBAL_PTR(p) ((const __attribute__((address_space(1))) void*)(p))
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-// Element offset of (row, 16-byte chunk) inside a [rows][64] bf16 LDS tile.
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * kPBK + ((chunk ^ ((row >> 1) & 7)) << 3); }
+// s_waitcnt immediate that waits until at most n vector-memory loads are
+// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
+// lgkmcnt left at their maxima so they are not waited on).
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+
+// The same immediate with lgkmcnt forced to 0 (also wait for LDS reads).
+constexpr int lgkm0_mask() { return ~(0xF << 8); }
+// Wait for every outstanding LDS read only (vmcnt and expcnt at maximum).
+constexpr int kLgkm0Only = 0xF | (0x3 << 14) | (0x7 << 4);
+
+// Workgroup barrier for the LDS ring.  The waits it needs are issued
+// explicitly before it; the empty asm keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Element offset of (row, logical 16-byte chunk) in a [rows][32] bf16 tile.
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * kPBK + ((chunk ^ ((row >> 2) & 3)) << 3); }
 
 // (expert, m-tile, n-tile) of logical tile L; returns false past the end.
 __device__ __forceinline__ bool decode_tile(const int32_t* offs, int L, int n_tiles_n, int* e_out, int* mt_out,
@@ -74,8 +98,8 @@ __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(
 grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ gather, int k_div,
                             const int32_t* __restrict__ offs, const bf16_t* __restrict__ B0,
                             const bf16_t* __restrict__ B1, void* __restrict__ Cout, int N, int K) {
-  __shared__ __align__(16) bf16_t As[2][kPBM * kPBK];
-  __shared__ __align__(16) bf16_t Bs[2][kPBN * kPBK];
+  // One LDS object holds the whole ring: [stage][A tile | B tile].
+  __shared__ __align__(16) bf16_t ring[kStages][(kPBM + kPBN) * kPBK];
 
   // Output columns per tile: 128 (SwiGLU: 128 gate + 128 up B rows) or 256.
   constexpr int TN = SWIGLU ? kPBN / 2 : kPBN;
@@ -99,11 +123,11 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
   const int wm = wave / 2, wn = wave % 2;
   const int l16 = lane % 16, lg = lane / 16;
   // Direct-to-LDS loads: one global_load_lds_dwordx4 writes 64 lanes x 16 B =
-  // 8 rows of a tile.  Wave w fills rows w*64 + j*8 + lane/8 (j = 0..7); the
-  // lane's physical chunk is lane%8, so it fetches the logical chunk that the
-  // swizzle maps there.
-  const int ld_sub = lane / 8;
-  const int ld_pchunk = lane % 8;
+  // 16 rows of 64 B.  Wave w fills rows w*64 + j*16 + lane/4 (j = 0..3); the
+  // lane's physical chunk is lane%4, so it fetches the logical chunk that
+  // the swizzle stores there.
+  const int ld_sub = lane / 4;
+  const int ld_pchunk = lane % 4;
 
   for (int L = beg + slot; L < end; L += slots) {
     int e, mt, nt;
@@ -113,12 +137,12 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
     const int m0 = mt * kPBM;
     const int n0 = nt * TN;
 
-    const bf16_t* a_ptr[8];
-    const bf16_t* b_ptr[8];
+    const bf16_t* a_ptr[4];
+    const bf16_t* b_ptr[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = wave * 64 + j * 8 + ld_sub;
-      const int lchunk = ld_pchunk ^ ((r >> 1) & 7);
+    for (int j = 0; j < 4; ++j) {
+      const int r = wave * 64 + j * 16 + ld_sub;
+      const int lchunk = ld_pchunk ^ ((r >> 2) & 3);
       const int ar = min(m0 + r, rows - 1);  // clamped rows are computed, never stored
       const int64_t g = row_begin + ar;
       const int64_t arow = gather ? static_cast<int64_t>(gather[g] / k_div) : g;
@@ -140,58 +164,100 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
       for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int KT = K / kPBK;
+    auto issue = [&](int kt) {
+      const int buf = kt % kStages;
+      const int koff = kt * kPBK;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r0 = wave * 64 + j * 16;
+        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(a_ptr[j] + koff), LDS_PTR(&ring[buf][r0 * kPBK]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(b_ptr[j] + koff), LDS_PTR(&ring[buf][(kPBM + r0) * kPBK]), 16, 0,
+                                         0);
+      }
+    };
+    // MFMA operands: the 8 token (A) fragments of the current stage and of the
+    // next one, and a sliding pair of weight (B) fragments.
+    bf16x8 fa0[8], fa1[8], fb0, fb1;
+    int b_row[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int r0 = wave * 64 + j * 8;
-      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(a_ptr[j]), LDS_PTR(&As[0][r0 * kPBK]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(GLOBAL_PTR(b_ptr[j]), LDS_PTR(&Bs[0][r0 * kPBK]), 16, 0, 0);
+      if constexpr (SWIGLU)
+        b_row[j] = (j < 4 ? 0 : TN) + wn * 64 + (j % 4) * 16 + l16;
+      else
+        b_row[j] = wn * 128 + j * 16 + l16;
     }
-    __syncthreads();
+#define MOE_A_FRAG(KT_, I_) \
+  (*reinterpret_cast<const bf16x8*>(&ring[(KT_) % kStages][lds_off(wm * 128 + (I_) * 16 + l16, lg)]))
+#define MOE_B_FRAG(KT_, J_) \
+  (*reinterpret_cast<const bf16x8*>(&ring[(KT_) % kStages][kPBM * kPBK + lds_off(b_row[J_], lg)]))
 
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < KT) {
-        const int koff = (kt + 1) * kPBK;
+// One stage k: 8 groups of 8 MFMAs (A fragments 0..7 times B fragment j).
+// Group j first waits for the LDS reads issued by group j-1, then starts the
+// reads for group j+1 (B fragment j+1), so each read has a group of MFMAs
+// (~128 cycles) to land.  At the midpoint the wave waits for stage k+1's
+// loads (WAIT_N = loads allowed to stay in flight) and joins the barrier;
+// after it every wave is done with ring slot k-1, which is refilled with
+// stage k+3 (ISSUE), and the A fragments of stage k+1 are read two per group
+// (NEXT).  The last group reads B fragment 0 of stage k+1.  The flags are
+// compile-time constants so the steady-state loop has no branches.
+#define MOE_STAGE(K_, FA, FA_NXT, FB_CUR, FB_NXT, ISSUE, WAIT_N, NEXT, BARRIER)                     \
+  do {                                                                                              \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                 \
+      __builtin_amdgcn_sched_barrier(0);                                                            \
+      if (j == 4 && (BARRIER)) {                                                                    \
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(WAIT_N) & lgkm0_mask());                               \
+        lds_barrier();                                                                              \
+        if (ISSUE) issue((K_) + 3);                                                                 \
+      } else {                                                                                      \
+        __builtin_amdgcn_s_waitcnt(kLgkm0Only);                                                     \
+      }                                                                                             \
+      if (j < 7) FB_NXT = MOE_B_FRAG((K_), j + 1);                                                  \
+      if (j >= 4 && (NEXT)) {                                                                       \
+        FA_NXT[2 * (j - 4)] = MOE_A_FRAG((K_) + 1, 2 * (j - 4));                                    \
+        FA_NXT[2 * (j - 4) + 1] = MOE_A_FRAG((K_) + 1, 2 * (j - 4) + 1);                            \
+      }                                                                                             \
+      if (j == 7 && (NEXT)) FB_NXT = MOE_B_FRAG((K_) + 1, 0);                                       \
+      _Pragma("unroll") for (int i = 0; i < 8; ++i) acc[i][j] =                                     \
+          __builtin_amdgcn_mfma_f32_16x16x32_bf16(FB_CUR, FA[i], acc[i][j], 0, 0, 0);               \
+      FB_CUR = FB_NXT;                                                                              \
+    }                                                                                               \
+  } while (0)
+
+    // Prologue: stages 0..2 in flight; stage 0's A fragments and B fragment 0.
+    // KT = K/32 is even and >= 4 (K is a multiple of 128).
+    issue(0);
+    issue(1);
+    issue(2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerStage));
+    lds_barrier();
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int r0 = wave * 64 + j * 8;
-          __builtin_amdgcn_global_load_lds(GLOBAL_PTR(a_ptr[j] + koff), LDS_PTR(&As[cur ^ 1][r0 * kPBK]), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(GLOBAL_PTR(b_ptr[j] + koff), LDS_PTR(&Bs[cur ^ 1][r0 * kPBK]), 16, 0, 0);
-        }
-      }
-      const bf16_t* as = As[cur];
-      const bf16_t* bs = Bs[cur];
-#pragma unroll
-      for (int kk = 0; kk < kPBK / 32; ++kk) {
-        const int chunk = kk * 4 + lg;
-        bf16x8 af[8], bfr[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          af[i] = *reinterpret_cast<const bf16x8*>(&as[lds_off(wm * 128 + i * 16 + l16, chunk)]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          int br;
-          if constexpr (SWIGLU)
-            br = (j < 4 ? 0 : TN) + wn * 64 + (j % 4) * 16 + l16;
-          else
-            br = wn * 128 + j * 16 + l16;
-          bfr[j] = *reinterpret_cast<const bf16x8*>(&bs[lds_off(br, chunk)]);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-      }
-      // The barrier waits for this wave's outstanding LDS-DMA loads
-      // (vmcnt(0)) and for every wave to finish reading the current buffer.
-      __syncthreads();
+    for (int i = 0; i < 8; ++i) fa0[i] = MOE_A_FRAG(0, i);
+    fb0 = MOE_B_FRAG(0, 0);
+
+    // Steady state, two stages per trip so the A-fragment sets swap roles
+    // without copies; the last four stages are peeled below.
+    int kt = 0;
+    for (; kt + 6 <= KT; kt += 2) {
+      MOE_STAGE(kt, fa0, fa1, fb0, fb1, true, kLoadsPerStage, true, true);
+      MOE_STAGE(kt + 1, fa1, fa0, fb0, fb1, true, kLoadsPerStage, true, true);
     }
+    // kt == KT - 4 here.
+    MOE_STAGE(kt, fa0, fa1, fb0, fb1, true, kLoadsPerStage, true, true);
+    MOE_STAGE(kt + 1, fa1, fa0, fb0, fb1, false, kLoadsPerStage, true, true);
+    MOE_STAGE(kt + 2, fa0, fa1, fb0, fb1, false, 0, true, true);
+    MOE_STAGE(kt + 3, fa1, fa0, fb0, fb1, false, 0, false, false);
+#undef MOE_STAGE
+#undef MOE_B_FRAG
+#undef MOE_A_FRAG
+    // Every wave is done with the ring before the next tile refills it.
+    __syncthreads();
 
     // Epilogue.  acc[i][j][q] is output row m = wm*128 + i*16 + l16 and
     // column wave_col(j) + 4*lg + q (B rows were MFMA src0).
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      // one 16-row block at a time keeps the accumulators in AGPRs until used
+      __builtin_amdgcn_sched_barrier(0);
       const int m = m0 + wm * 128 + i * 16 + l16;
       if (m >= rows) continue;
       const int64_t orow = row_begin + m;
