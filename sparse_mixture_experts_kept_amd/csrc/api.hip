@@ -51,7 +51,12 @@ moe_status check_dims(const moe_dims* dims) {
   return MOE_OK;
 }
 
+// The prefill kernels pipeline the reduction in 32-wide steps and need at
+// least 8 of them (d, f >= 256); smaller layers always use the decode kernels.
+constexpr int32_t kPrefillMinK = 256;
+
 bool use_decode(const moe_dims* dims) {
+  if (dims->d < kPrefillMinK || dims->f < kPrefillMinK) return true;
   if (dims->variant == MOE_VARIANT_DECODE) return true;
   if (dims->variant == MOE_VARIANT_PREFILL) return false;
   return dims->T <= kDecodeMaxTokens;

@@ -9,16 +9,21 @@
 // for the rows r = offsets[e] .. offsets[e+1]-1 of expert e (tok(r) =
 // sorted_slots[r] / k, the gather fused into the A-tile load).
 //
-// Design (gfx950): persistent workgroups of 256 threads (4 waves, one per
-// SIMD), 256 x 256 block tiles stepped 32 deep in k, each wave a 128 x 128
-// sub-tile built from v_mfma_f32_16x16x32_bf16 with fp32 accumulators.  A and
-// B tiles live in a 4-deep LDS ring (4 x 32 KiB) filled by direct
-// global->LDS loads (global_load_lds_dwordx4, no staging registers); three
-// k-steps of loads are in flight while the MFMAs consume the fourth, and
-// each step waits only for its own loads (s_waitcnt vmcnt(N)) before one
-// barrier.  LDS rows are 64 B with the 16-byte chunk index XOR-swizzled by
-// the row so that the fragment reads of 16 lanes hit 16 distinct 4-bank
-// groups (measured: zero bank conflicts).  For
+// Design (gfx950): persistent workgroups of 512 threads (8 waves, two per
+// SIMD so one wave's LDS reads, loads and barrier waits hide under the other
+// wave's MFMAs), 256 x 256 block tiles stepped 32 deep in k, each wave a
+// 128 x 64 sub-tile built from v_mfma_f32_16x16x32_bf16 with fp32
+// accumulators.  A and B tiles live in a 4-deep LDS ring (4 x 32 KiB) filled
+// by direct global->LDS loads (global_load_lds_dwordx4, no staging
+// registers) up to four k-steps ahead.  The two waves of each SIMD run a
+// ping-pong schedule: one issues its MFMAs while the other refills the ring
+// and reads its next fragments, swapping at every barrier.  Waits are
+// explicit (s_waitcnt vmcnt(N) / lgkmcnt(0) before raw barriers), so the
+// compiler adds none that would serialise the ring.  LDS rows are 64 B with the 16-byte chunk index XOR-swizzled by
+// bits 1..2 of the row; of the layouts measured with the LDS bank-conflict
+// counter for the ds_read_b128 fragment pattern (16 rows x 4 chunks), this
+// one has no conflicts while chunk ^ (row >> 2) and the unswizzled layout
+// are 2-way conflicted.  For
 // the up projection the 256 B rows of a tile are 128 gate rows and the same
 // 128 up rows, so every wave holds matching gate/up accumulators and applies
 // SiLU(g)*u in registers before one bf16 rounding.
@@ -37,12 +42,12 @@ namespace moe {
 constexpr int kPBM = 256;
 constexpr int kPBN = 256;
 constexpr int kPBK = 32;       // k depth of one pipeline stage
-constexpr int kStages = 4;     // LDS ring depth
-constexpr int kPThreads = 256;
+constexpr int kStages = 4;     // LDS ring depth (4 x 32 KiB)
+constexpr int kPThreads = 512;  // 8 waves: two per SIMD
 constexpr int kXcds = 8;
 constexpr int kGroupN = 8;
-// Per wave and stage: 4 A loads + 4 B loads of 1 KiB (16 rows x 64 B).
-constexpr int kLoadsPerStage = 8;
+// Per wave and stage: 2 A loads + 2 B loads of 1 KiB (16 rows x 64 B).
+constexpr int kLoadsPerStage = 4;
 
 #define GLOBAL_PTR(p) ((const __attribute__((address_space(1))) void*)(p))
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
@@ -54,6 +59,11 @@ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4
 
 // The same immediate with lgkmcnt forced to 0 (also wait for LDS reads).
 constexpr int lgkm0_mask() { return ~(0xF << 8); }
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedVmemRead = 0x020;
+constexpr int kSchedDsRead = 0x100;
+
 // Wait for every outstanding LDS read only (vmcnt and expcnt at maximum).
 constexpr int kLgkm0Only = 0xF | (0x3 << 14) | (0x7 << 4);
 
@@ -66,7 +76,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Element offset of (row, logical 16-byte chunk) in a [rows][32] bf16 tile.
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * kPBK + ((chunk ^ ((row >> 2) & 3)) << 3); }
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * kPBK + ((chunk ^ ((row >> 1) & 3)) << 3); }
 
 // (expert, m-tile, n-tile) of logical tile L; returns false past the end.
 __device__ __forceinline__ bool decode_tile(const int32_t* offs, int L, int n_tiles_n, int* e_out, int* mt_out,
@@ -94,7 +104,7 @@ __device__ __forceinline__ bool decode_tile(const int32_t* offs, int L, int n_ti
 }
 
 template <bool SWIGLU>
-__global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ gather, int k_div,
                             const int32_t* __restrict__ offs, const bf16_t* __restrict__ B0,
                             const bf16_t* __restrict__ B1, void* __restrict__ Cout, int N, int K) {
@@ -120,12 +130,13 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
-  const int wm = wave / 2, wn = wave % 2;
+  // 8 waves as 2 (rows) x 4 (columns); each owns a 128 x 64 output block.
+  const int wm = wave / 4, wn = wave % 4;
   const int l16 = lane % 16, lg = lane / 16;
   // Direct-to-LDS loads: one global_load_lds_dwordx4 writes 64 lanes x 16 B =
-  // 16 rows of 64 B.  Wave w fills rows w*64 + j*16 + lane/4 (j = 0..3); the
-  // lane's physical chunk is lane%4, so it fetches the logical chunk that
-  // the swizzle stores there.
+  // 16 rows of 64 B.  Wave w fills A and B rows w*32 + j*16 + lane/4
+  // (j = 0, 1); the lane's physical chunk is lane%4, so it fetches the
+  // logical chunk that the swizzle stores there.
   const int ld_sub = lane / 4;
   const int ld_pchunk = lane % 4;
 
@@ -137,12 +148,12 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
     const int m0 = mt * kPBM;
     const int n0 = nt * TN;
 
-    const bf16_t* a_ptr[4];
-    const bf16_t* b_ptr[4];
+    const bf16_t* a_ptr[2];
+    const bf16_t* b_ptr[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = wave * 64 + j * 16 + ld_sub;
-      const int lchunk = ld_pchunk ^ ((r >> 2) & 3);
+    for (int j = 0; j < 2; ++j) {
+      const int r = wave * 32 + j * 16 + ld_sub;
+      const int lchunk = ld_pchunk ^ ((r >> 1) & 3);
       const int ar = min(m0 + r, rows - 1);  // clamped rows are computed, never stored
       const int64_t g = row_begin + ar;
       const int64_t arow = gather ? static_cast<int64_t>(gather[g] / k_div) : g;
@@ -157,98 +168,92 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
       }
     }
 
-    f32x4 acc[8][8];
+    f32x4 acc[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int KT = K / kPBK;
     auto issue = [&](int kt) {
       const int buf = kt % kStages;
       const int koff = kt * kPBK;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r0 = wave * 64 + j * 16;
+      for (int j = 0; j < 2; ++j) {
+        const int r0 = wave * 32 + j * 16;
         __builtin_amdgcn_global_load_lds(GLOBAL_PTR(a_ptr[j] + koff), LDS_PTR(&ring[buf][r0 * kPBK]), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(GLOBAL_PTR(b_ptr[j] + koff), LDS_PTR(&ring[buf][(kPBM + r0) * kPBK]), 16, 0,
                                          0);
       }
     };
-    // MFMA operands: the 8 token (A) fragments of the current stage and of the
-    // next one, and a sliding pair of weight (B) fragments.
-    bf16x8 fa0[8], fa1[8], fb0, fb1;
-    int b_row[8];
+    // B rows of this wave's 4 weight fragments: SwiGLU = 2 gate + the same 2 up.
+    int b_row[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
       if constexpr (SWIGLU)
-        b_row[j] = (j < 4 ? 0 : TN) + wn * 64 + (j % 4) * 16 + l16;
+        b_row[j] = (j < 2 ? 0 : TN) + wn * 32 + (j % 2) * 16 + l16;
       else
-        b_row[j] = wn * 128 + j * 16 + l16;
+        b_row[j] = wn * 64 + j * 16 + l16;
     }
-#define MOE_A_FRAG(KT_, I_) \
-  (*reinterpret_cast<const bf16x8*>(&ring[(KT_) % kStages][lds_off(wm * 128 + (I_) * 16 + l16, lg)]))
-#define MOE_B_FRAG(KT_, J_) \
-  (*reinterpret_cast<const bf16x8*>(&ring[(KT_) % kStages][kPBM * kPBK + lds_off(b_row[J_], lg)]))
 
-// One stage k: 8 groups of 8 MFMAs (A fragments 0..7 times B fragment j).
-// Group j first waits for the LDS reads issued by group j-1, then starts the
-// reads for group j+1 (B fragment j+1), so each read has a group of MFMAs
-// (~128 cycles) to land.  At the midpoint the wave waits for stage k+1's
-// loads (WAIT_N = loads allowed to stay in flight) and joins the barrier;
-// after it every wave is done with ring slot k-1, which is refilled with
-// stage k+3 (ISSUE), and the A fragments of stage k+1 are read two per group
-// (NEXT).  The last group reads B fragment 0 of stage k+1.  The flags are
-// compile-time constants so the steady-state loop has no branches.
-#define MOE_STAGE(K_, FA, FA_NXT, FB_CUR, FB_NXT, ISSUE, WAIT_N, NEXT, BARRIER)                     \
-  do {                                                                                              \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                 \
-      __builtin_amdgcn_sched_barrier(0);                                                            \
-      if (j == 4 && (BARRIER)) {                                                                    \
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(WAIT_N) & lgkm0_mask());                               \
-        lds_barrier();                                                                              \
-        if (ISSUE) issue((K_) + 3);                                                                 \
-      } else {                                                                                      \
-        __builtin_amdgcn_s_waitcnt(kLgkm0Only);                                                     \
-      }                                                                                             \
-      if (j < 7) FB_NXT = MOE_B_FRAG((K_), j + 1);                                                  \
-      if (j >= 4 && (NEXT)) {                                                                       \
-        FA_NXT[2 * (j - 4)] = MOE_A_FRAG((K_) + 1, 2 * (j - 4));                                    \
-        FA_NXT[2 * (j - 4) + 1] = MOE_A_FRAG((K_) + 1, 2 * (j - 4) + 1);                            \
-      }                                                                                             \
-      if (j == 7 && (NEXT)) FB_NXT = MOE_B_FRAG((K_) + 1, 0);                                       \
-      _Pragma("unroll") for (int i = 0; i < 8; ++i) acc[i][j] =                                     \
-          __builtin_amdgcn_mfma_f32_16x16x32_bf16(FB_CUR, FA[i], acc[i][j], 0, 0, 0);               \
-      FB_CUR = FB_NXT;                                                                              \
-    }                                                                                               \
-  } while (0)
+    // Fragment registers of the current k-step.
+    bf16x8 fa[8], fb[4];
+    auto read_frags = [&](int kt) {
+      const bf16_t* as_ = ring[kt % kStages];
+      const bf16_t* bs_ = as_ + kPBM * kPBK;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(&bs_[lds_off(b_row[j], lg)]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(&as_[lds_off(wm * 128 + i * 16 + l16, lg)]);
+    };
 
-    // Prologue: stages 0..2 in flight; stage 0's A fragments and B fragment 0.
-    // KT = K/32 is even and >= 4 (K is a multiple of 128).
+    // Ping-pong: waves 0-3 (one per SIMD) and waves 4-7 (the other wave of
+    // each SIMD) alternate between a compute phase (32 MFMAs from registers)
+    // and a memory phase (refill a ring slot, read the next fragments, wait),
+    // swapping at every barrier, so each SIMD's matrix pipe always has one
+    // wave feeding it.  Waves 4-7 start one phase late.
+    //   compute(k): MFMAs of step k.
+    //   memory(k):  refill slot k%4 with stage k+4, read step k+1's fragments,
+    //               wait for this wave's loads of stage k+2 and for the reads.
+    // Every wave waits for its own loads of stage k+1 before the barrier that
+    // opens the first memory(k) (end of memory(k-1)), and for its reads of
+    // step k before the barrier that opens the first refill of slot k, so
+    // LDS data is complete when read and slots are free when refilled.
+    // KT = K/32 is a multiple of 4 (K is a multiple of 128) and >= 8.
+    const bool late = wave >= 4;
     issue(0);
     issue(1);
     issue(2);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerStage));
+    issue(3);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * kLoadsPerStage));
     lds_barrier();
+    read_frags(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerStage) & lgkm0_mask());
+    if (late) lds_barrier();
+    for (int kt = 0; kt < KT; ++kt) {
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) fa0[i] = MOE_A_FRAG(0, i);
-    fb0 = MOE_B_FRAG(0, 0);
-
-    // Steady state, two stages per trip so the A-fragment sets swap roles
-    // without copies; the last four stages are peeled below.
-    int kt = 0;
-    for (; kt + 6 <= KT; kt += 2) {
-      MOE_STAGE(kt, fa0, fa1, fb0, fb1, true, kLoadsPerStage, true, true);
-      MOE_STAGE(kt + 1, fa1, fa0, fb0, fb1, true, kLoadsPerStage, true, true);
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      if (kt + 4 < KT) {
+        issue(kt + 4);
+        read_frags(kt + 1);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerStage) & lgkm0_mask());
+      } else if (kt + 3 < KT) {
+        read_frags(kt + 1);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerStage) & lgkm0_mask());
+      } else if (kt + 1 < KT) {
+        read_frags(kt + 1);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & lgkm0_mask());
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
     }
-    // kt == KT - 4 here.
-    MOE_STAGE(kt, fa0, fa1, fb0, fb1, true, kLoadsPerStage, true, true);
-    MOE_STAGE(kt + 1, fa1, fa0, fb0, fb1, false, kLoadsPerStage, true, true);
-    MOE_STAGE(kt + 2, fa0, fa1, fb0, fb1, false, 0, true, true);
-    MOE_STAGE(kt + 3, fa1, fa0, fb0, fb1, false, 0, false, false);
-#undef MOE_STAGE
-#undef MOE_B_FRAG
-#undef MOE_A_FRAG
+    if (!late) lds_barrier();
     // Every wave is done with the ring before the next tile refills it.
     __syncthreads();
 
@@ -256,7 +261,7 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
     // column wave_col(j) + 4*lg + q (B rows were MFMA src0).
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      // one 16-row block at a time keeps the accumulators in AGPRs until used
+      // one 16-row block at a time keeps the accumulators in place until used
       __builtin_amdgcn_sched_barrier(0);
       const int m = m0 + wm * 128 + i * 16 + l16;
       if (m >= rows) continue;
@@ -264,11 +269,11 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
       if constexpr (SWIGLU) {
         bf16_t* C = static_cast<bf16_t*>(Cout);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = n0 + wn * 64 + j * 16 + 4 * lg;
+        for (int j = 0; j < 2; ++j) {
+          const int n = n0 + wn * 32 + j * 16 + 4 * lg;
           if (n >= N) continue;
           const f32x4 g = acc[i][j];
-          const f32x4 u = acc[i][j + 4];
+          const f32x4 u = acc[i][j + 2];
           uint2 p;
           p.x = pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
           p.y = pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
@@ -277,8 +282,8 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
       } else {
         float* C = static_cast<float*>(Cout);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int n = n0 + wn * 128 + j * 16 + 4 * lg;
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + wn * 64 + j * 16 + 4 * lg;
           if (n >= N) continue;
           const f32x4 v = acc[i][j];
           *reinterpret_cast<float4*>(C + orow * N + n) = make_float4(v[0], v[1], v[2], v[3]);
