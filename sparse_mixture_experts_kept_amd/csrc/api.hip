@@ -260,11 +260,28 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
   void* h = ws + plan.h;
   float* y_rows = reinterpret_cast<float*>(ws + plan.y_rows);
 
-  st = run_router(dims, x, w_gate, logit_bias, idx, w, nullptr, s);
-  if (st != MOE_OK) return st;
-  st = hip_status(moe::launch_permute(idx, static_cast<int32_t>(dims->T * dims->k), offs, sorted, rows,
-                                      expert_counts_out, s));
-  if (st != MOE_OK) return st;
+  if (dims->T <= kDecodeMaxTokens) {
+    // Small batch: routing and permutation in one workgroup; with bf16 the
+    // down projection also applies the combine, so y_rows is never written.
+    st = hip_status(moe::launch_route_permute(dims->dtype, x, w_gate, logit_bias, idx, w,
+                                              static_cast<int32_t>(dims->T), dims->d, offs, sorted, rows,
+                                              expert_counts_out, s));
+    if (st != MOE_OK) return st;
+    if (dims->dtype == MOE_BF16 && use_decode(dims)) {
+      st = run_up(dims, x, offs, sorted, w1, w3, h, s);
+      if (st != MOE_OK) return st;
+      return hip_status(moe::launch_down_combine_decode(static_cast<const bf16_t*>(h), offs,
+                                                        static_cast<const bf16_t*>(w2), idx, rows, w,
+                                                        static_cast<bf16_t*>(y), static_cast<int>(dims->T), dims->d,
+                                                        dims->f, s));
+    }
+  } else {
+    st = run_router(dims, x, w_gate, logit_bias, idx, w, nullptr, s);
+    if (st != MOE_OK) return st;
+    st = hip_status(moe::launch_permute(idx, static_cast<int32_t>(dims->T * dims->k), offs, sorted, rows,
+                                        expert_counts_out, s));
+    if (st != MOE_OK) return st;
+  }
   st = run_experts(dims, x, offs, sorted, w1, w3, w2, h, y_rows, s);
   if (st != MOE_OK) return st;
   return run_combine(dims, y_rows, rows, w, y, s);

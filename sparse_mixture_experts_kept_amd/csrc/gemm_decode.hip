@@ -102,6 +102,85 @@ __global__ void __launch_bounds__(kDThreads) grouped_gemm_decode_kernel(
   }
 }
 
+// Down projection fused with the gate-weighted combine, for batches of at
+// most 64 tokens (so no expert has more than 64 rows).  Workgroup b owns
+// output features n0 = 16 b .. n0+15 of every expert: wave w streams w2 rows
+// n0.. of expert w/2 over half w%2 of the reduction (f/2 each) with the same
+// MFMA scheme as above, parks its partial sums in LDS, and after a barrier the
+// workgroup forms y[t, n0+c] = g_t0 (P0 + P1)[r0] + g_t1 (P0 + P1)[r1] for
+// every token in a fixed order (deterministic), rounded once to bf16.
+constexpr int kDcThreads = 1024;   // 16 waves: 8 experts x 2 halves of f
+constexpr int kDcMaxRows = 64;
+
+template <int KU>
+__global__ void __launch_bounds__(kDcThreads) down_combine_decode_kernel(
+    const bf16_t* __restrict__ H, const int32_t* __restrict__ offs, const bf16_t* __restrict__ w2,
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ slot_rows, const float* __restrict__ topk_w,
+    bf16_t* __restrict__ y, int T, int d, int f) {
+  __shared__ float part[kDcThreads / kWave][kDcMaxRows][16];
+  const int lane = threadIdx.x % kWave;
+  const int wave = threadIdx.x / kWave;
+  const int l16 = lane % 16, lg = lane / 16;
+  const int e = wave / 2, half = wave % 2;
+  const int n0 = blockIdx.x * 16;
+  const int row_begin = offs[e];
+  const int rows = offs[e + 1] - row_begin;  // <= kDcMaxRows (T <= 64)
+  const int kh = f / 2;
+
+  if (rows > 0) {
+    const bf16_t* wrow = w2 + (static_cast<int64_t>(e) * d + n0 + l16) * f + half * kh + lg * 8;
+    const int ng = (rows + 15) / 16;
+    const bf16_t* a_ptr[kDMaxGroups];
+#pragma unroll
+    for (int g = 0; g < kDMaxGroups; ++g) {
+      const int m = min(g * 16 + l16, rows - 1);  // clamped rows are computed, never used
+      a_ptr[g] = H + static_cast<int64_t>(row_begin + m) * f + half * kh + lg * 8;
+    }
+    f32x4 acc[kDMaxGroups];
+#pragma unroll
+    for (int g = 0; g < kDMaxGroups; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < kh; k0 += 32 * KU) {
+      bf16x8 wa[KU];
+#pragma unroll
+      for (int u = 0; u < KU; ++u) wa[u] = *reinterpret_cast<const bf16x8*>(wrow + k0 + u * 32);
+#pragma unroll
+      for (int g = 0; g < kDMaxGroups; ++g) {
+        if (g < ng) {
+#pragma unroll
+          for (int u = 0; u < KU; ++u) {
+            const bf16x8 ha = *reinterpret_cast<const bf16x8*>(a_ptr[g] + k0 + u * 32);
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[u], ha, acc[g], 0, 0, 0);
+          }
+        }
+      }
+    }
+    // acc[g][q]: expert row g*16 + l16, feature 4*lg + q
+#pragma unroll
+    for (int g = 0; g < kDMaxGroups; ++g) {
+      const int m = g * 16 + l16;
+      if (g < ng && m < rows) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) part[wave][m][4 * lg + q] = acc[g][q];
+      }
+    }
+  }
+  __syncthreads();
+
+  // Combine: thread (t, c) for token t < T <= 64 and feature column c < 16.
+  const int t = threadIdx.x / 16, c = threadIdx.x % 16;
+  if (t < T) {
+    float o = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kTopK; ++j) {
+      const int ej = topk_idx[kTopK * t + j];
+      const int r = slot_rows[kTopK * t + j] - offs[ej];
+      const float v = part[2 * ej][r][c] + part[2 * ej + 1][r][c];
+      o = (j == 0) ? topk_w[kTopK * t] * v : o + topk_w[kTopK * t + j] * v;
+    }
+    y[static_cast<int64_t>(t) * d + n0 + c] = f32_to_bf16(o);
+  }
+}
+
 template <bool SWIGLU, int KU>
 static hipError_t launch_one_decode(const bf16_t* A, const int32_t* gather, int k_div, const int32_t* offs,
                                     const bf16_t* B0, const bf16_t* B1, void* C, int N, int K, hipStream_t s) {
@@ -118,6 +197,20 @@ hipError_t launch_up_decode(const bf16_t* x, const int32_t* offs, const int32_t*
   // K = d; KU * 32 must divide it (d % 128 == 0, so KU = 4 always works).
   if (d % 256 == 0) return launch_one_decode<true, 8>(x, sorted_slots, kTopK, offs, w1, w3, h, f, d, s);
   return launch_one_decode<true, 4>(x, sorted_slots, kTopK, offs, w1, w3, h, f, d, s);
+}
+
+hipError_t launch_down_combine_decode(const bf16_t* h, const int32_t* offs, const bf16_t* w2, const int32_t* topk_idx,
+                                      const int32_t* slot_rows, const float* topk_w, bf16_t* y, int T, int d, int f,
+                                      hipStream_t s) {
+  // each wave covers f/2 in steps of 32*KU
+  const int kh = f / 2;
+  if (kh % 512 == 0)
+    hipLaunchKernelGGL(down_combine_decode_kernel<16>, dim3(d / 16), dim3(kDcThreads), 0, s, h, offs, w2, topk_idx,
+                       slot_rows, topk_w, y, T, d, f);
+  else
+    hipLaunchKernelGGL(down_combine_decode_kernel<2>, dim3(d / 16), dim3(kDcThreads), 0, s, h, offs, w2, topk_idx,
+                       slot_rows, topk_w, y, T, d, f);
+  return hipGetLastError();
 }
 
 hipError_t launch_down_decode(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,

@@ -34,6 +34,15 @@ hipError_t launch_up_decode(const bf16_t* x, const int32_t* offs, const int32_t*
 hipError_t launch_down_decode(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,
                               hipStream_t s);
 
+// Small batches (T <= 64): routing + permutation in one workgroup, and the
+// decode down projection fused with the combine (y written directly).
+hipError_t launch_route_permute(int dtype, const void* x, const void* wg, const float* bias, int32_t* idx, float* w,
+                                int32_t T, int d, int32_t* offsets, int32_t* sorted_slots, int32_t* slot_rows,
+                                int32_t* counts_out, hipStream_t s);
+hipError_t launch_down_combine_decode(const bf16_t* h, const int32_t* offs, const bf16_t* w2, const int32_t* topk_idx,
+                                      const int32_t* slot_rows, const float* topk_w, bf16_t* y, int T, int d, int f,
+                                      hipStream_t s);
+
 hipError_t launch_combine(int dtype, const float* y_rows, const int32_t* slot_rows, const float* topk_w, void* y,
                           int64_t T, int d, int n_cu, hipStream_t s);
 

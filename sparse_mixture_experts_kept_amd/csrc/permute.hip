@@ -13,82 +13,16 @@
 // an order, so the result is deterministic.
 #include "common.hpp"
 #include "launch.hpp"
+#include "permute_dev.hpp"
 
 namespace moe {
-
-constexpr int kPermThreads = 1024;
-constexpr int kPermWaves = kPermThreads / kWave;
-
-// Ids outside [0, E) are skipped (never used as an index).
-__device__ __forceinline__ int valid_expert(int e) { return (e >= 0 && e < kExperts) ? e : -1; }
 
 __global__ void __launch_bounds__(kPermThreads) permute_kernel(const int32_t* __restrict__ idx, int32_t n_slots,
                                                                int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ sorted_slots,
                                                                int32_t* __restrict__ slot_rows,
                                                                int32_t* __restrict__ counts_out) {
-  __shared__ int32_t hist[kExperts];
-  __shared__ int32_t base[kExperts];
-  __shared__ int32_t wave_cnt[kPermWaves][kExperts];
-
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int wave = tid / kWave;
-  if (tid < kExperts) hist[tid] = 0;
-  __syncthreads();
-
-  // (1) histogram: per-wave ballots, one LDS add per wave and expert.
-  for (int c = 0; c < n_slots; c += kPermThreads) {
-    const int s = c + tid;
-    const int e = s < n_slots ? valid_expert(idx[s]) : -1;
-#pragma unroll
-    for (int ee = 0; ee < kExperts; ++ee) {
-      const unsigned long long m = __ballot(e == ee);
-      if (lane == 0 && m) atomicAdd(&hist[ee], __popcll(m));
-    }
-  }
-  __syncthreads();
-
-  // (2) exclusive scan over the 8 experts.
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < kExperts; ++e) {
-      offsets[e] = run;
-      base[e] = run;
-      if (counts_out) counts_out[e] = hist[e];
-      run += hist[e];
-    }
-    offsets[kExperts] = run;
-  }
-  __syncthreads();
-
-  // (3) stable scatter, chunk by chunk in slot order.
-  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  for (int c = 0; c < n_slots; c += kPermThreads) {
-    const int s = c + tid;
-    const int e = s < n_slots ? valid_expert(idx[s]) : -1;
-    int rank = 0;
-#pragma unroll
-    for (int ee = 0; ee < kExperts; ++ee) {
-      const unsigned long long m = __ballot(e == ee);
-      if (e == ee) rank = __popcll(m & below);
-      if (lane == 0) wave_cnt[wave][ee] = __popcll(m);
-    }
-    __syncthreads();
-    if (e >= 0) {
-      int pos = base[e] + rank;
-      for (int w = 0; w < wave; ++w) pos += wave_cnt[w][e];
-      sorted_slots[pos] = s;
-      slot_rows[s] = pos;
-    }
-    __syncthreads();
-    if (tid < kExperts) {
-      int add = 0;
-      for (int w = 0; w < kPermWaves; ++w) add += wave_cnt[w][tid];
-      base[tid] += add;
-    }
-    __syncthreads();
-  }
+  permute_block(idx, n_slots, offsets, sorted_slots, slot_rows, counts_out);
 }
 
 hipError_t launch_permute(const int32_t* idx, int32_t n_slots, int32_t* offsets, int32_t* sorted_slots,

@@ -2,14 +2,111 @@
 // "Mixtral of Experts" (azimuth.plus), router paragraph: one linear map to 8
 // scores, keep the two largest, all others -inf, softmax over the survivors.
 //
-// One wavefront per token.  The router matrix W_g [8, d] is staged once per
-// workgroup in LDS; each lane accumulates 8 fp32 partial dot products over
-// its share of d, a butterfly (xor-shuffle) sum gives every lane all 8
-// scores, and lane 0 selects the pair in registers and writes it.
+// bf16: the scores are a [T, d] x [d, 8] contraction and run on MFMA (the 8
+// router rows padded to 16), the reduction over d split across waves and
+// summed in LDS in a fixed order; lanes then select the pair per token.
+// fp32: one wavefront per token; the router matrix W_g [8, d] is staged in
+// LDS, each lane accumulates 8 fp32 partial dot products over its share of
+// d, a butterfly (xor-shuffle) sum gives every lane all 8 scores, and lane 0
+// selects the pair.  For small batches one workgroup routes every token and
+// then sorts the slots.
 #include "common.hpp"
 #include "launch.hpp"
+#include "permute_dev.hpp"
 
 namespace moe {
+
+// Route one token with one wavefront: 8 fp32 dot products over d (the
+// router matrix is in LDS), butterfly sums so every lane holds all 8 scores,
+// then lane 0 keeps the two largest (larger first, lower index on ties) and
+// the softmax over that pair.
+template <typename T>
+__device__ __forceinline__ void route_token(const T* __restrict__ xr, const T* wg_s, const float* b, int d, int lane,
+                                            int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                                            float* __restrict__ logits_out) {
+  constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte load
+  // A lane's x chunks are loaded kChunks at a time before any arithmetic, so
+  // a token costs one memory latency per kChunks * 64 * VEC elements.
+  constexpr int kChunks = 8;
+  float acc[kExperts];
+#pragma unroll
+  for (int e = 0; e < kExperts; ++e) acc[e] = 0.0f;
+  for (int base = 0; base < d; base += kChunks * kWave * VEC) {
+    uint4 xv[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c)  // clamped, unconditional: one latency for all
+      xv[c] = *reinterpret_cast<const uint4*>(xr + min(base + (lane + c * kWave) * VEC, d - VEC));
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int i = base + (lane + c * kWave) * VEC;
+      if (i < d) {
+        const T* xe = reinterpret_cast<const T*>(&xv[c]);
+        float xf[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) xf[v] = to_f32<T>(xe[v]);
+#pragma unroll
+        for (int e = 0; e < kExperts; ++e) {
+          const uint4 wv = *reinterpret_cast<const uint4*>(wg_s + e * d + i);
+          const T* we = reinterpret_cast<const T*>(&wv);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) acc[e] = fmaf(xf[v], to_f32<T>(we[v]), acc[e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < kExperts; ++e) acc[e] = wave_sum(acc[e]) + b[e];
+
+  if (lane == 0) {
+    // Two largest, larger first; strict '>' keeps the lower index on ties.
+    int ia = 0;
+    float la = acc[0];
+#pragma unroll
+    for (int e = 1; e < kExperts; ++e)
+      if (acc[e] > la) { la = acc[e]; ia = e; }
+    int ib = -1;
+    float lb = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kExperts; ++e)
+      if (e != ia && (ib < 0 || acc[e] > lb)) { lb = acc[e]; ib = e; }
+    // softmax over {la, lb} with the others at -inf
+    const float r = expf(lb - la);
+    idx_out[0] = ia;
+    idx_out[1] = ib;
+    w_out[0] = 1.0f / (1.0f + r);
+    w_out[1] = r / (1.0f + r);
+  }
+  if (logits_out && lane < kExperts) {
+    float v = acc[0];
+#pragma unroll
+    for (int e = 1; e < kExperts; ++e)
+      if (lane == e) v = acc[e];
+    logits_out[lane] = v;
+  }
+}
+
+// Stage W_g [8, d] in LDS (d a multiple of 128) and the bias in registers.
+template <typename T>
+__device__ __forceinline__ void stage_router(const T* __restrict__ wg, const float* __restrict__ bias, T* wg_s, int d,
+                                             float* b) {
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int kBatch = 8;  // loads in flight per thread before the LDS stores
+  const int n_vec = kExperts * d / VEC;
+  const int step = blockDim.x;
+  for (int base = threadIdx.x; base < n_vec; base += kBatch * step) {
+    uint4 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)  // unconditional (clamped) loads issue back to back
+      v[u] = reinterpret_cast<const uint4*>(wg)[min(base + u * step, n_vec - 1)];
+    // Out-of-range slots load and store the last element (same value), so the
+    // stores need no branch either.
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) reinterpret_cast<uint4*>(wg_s)[min(base + u * step, n_vec - 1)] = v[u];
+  }
+#pragma unroll
+  for (int e = 0; e < kExperts; ++e) b[e] = bias ? bias[e] : 0.0f;
+  __syncthreads();
+}
 
 template <typename T>
 __global__ void __launch_bounds__(256) router_top2_kernel(const T* __restrict__ x, const T* __restrict__ wg,
@@ -18,78 +115,142 @@ __global__ void __launch_bounds__(256) router_top2_kernel(const T* __restrict__ 
                                                           int64_t T_tokens, int d) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* wg_s = reinterpret_cast<T*>(smem_raw);
-  constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte load
-
-  // Stage W_g in LDS (E * d elements, d a multiple of 128).
-  const int n_vec = kExperts * d / VEC;
-  for (int i = threadIdx.x; i < n_vec; i += blockDim.x)
-    reinterpret_cast<uint4*>(wg_s)[i] = reinterpret_cast<const uint4*>(wg)[i];
-  __syncthreads();
-
+  float b[kExperts];
+  stage_router(wg, bias, wg_s, d, b);
   const int lane = threadIdx.x % kWave;
   const int waves_per_block = blockDim.x / kWave;
   const int64_t wave_id = static_cast<int64_t>(blockIdx.x) * waves_per_block + threadIdx.x / kWave;
   const int64_t n_waves = static_cast<int64_t>(gridDim.x) * waves_per_block;
+  for (int64_t t = wave_id; t < T_tokens; t += n_waves)
+    route_token(x + t * d, wg_s, b, d, lane, idx_out + 2 * t, w_out + 2 * t,
+                logits_out ? logits_out + t * kExperts : nullptr);
+}
 
-  float b[kExperts];
-#pragma unroll
-  for (int e = 0; e < kExperts; ++e) b[e] = bias ? bias[e] : 0.0f;
+// bf16 scores on MFMA: one 16-token group times the 8 router rows (padded to
+// 16 with zeros) per v_mfma_f32_16x16x32_bf16, with fp32 accumulation (the
+// bf16 products are exact in fp32, as in the VALU form).  `slices` waves
+// split the reduction over d; their partial scores meet in LDS and are added
+// in slice order.  Returns, in lanes 0..15 of the reducing wave, the 8
+// scores of token (group*16 + lane) in s[0..7].
+__device__ __forceinline__ f32x4 router_scores_partial(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
+                                                       int T, int d, int group, int slice, int slices, int lane) {
+  const int l16 = lane % 16, lg = lane / 16;
+  const int tok = min(group * 16 + l16, T - 1);  // clamped rows are computed, never written
+  const int ks = d / slices;                       // a multiple of 32 (see router_slices)
+  const bf16_t* xp = x + static_cast<int64_t>(tok) * d + slice * ks + lg * 8;
+  const bool real_row = l16 < kExperts;            // rows 8..15 of the padded router are zero
+  const bf16_t* wp = wg + static_cast<int64_t>(real_row ? l16 : 0) * d + slice * ks + lg * 8;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const bf16x8 zero = {};
+  // ks is only a multiple of 32; the unroll keeps loads in flight.
+#pragma unroll 8
+  for (int k0 = 0; k0 < ks; k0 += 32) {
+    const bf16x8 wa = *reinterpret_cast<const bf16x8*>(wp + k0);
+    const bf16x8 xa = *reinterpret_cast<const bf16x8*>(xp + k0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(real_row ? wa : zero, xa, acc, 0, 0, 0);
+  }
+  // acc[q] = score of expert 4*lg + q for token l16 (meaningful for lg < 2)
+  return acc;
+}
 
-  for (int64_t t = wave_id; t < T_tokens; t += n_waves) {
-    const T* xr = x + t * d;
-    float acc[kExperts];
-#pragma unroll
-    for (int e = 0; e < kExperts; ++e) acc[e] = 0.0f;
-    for (int i = lane * VEC; i < d; i += kWave * VEC) {
-      const uint4 xv = *reinterpret_cast<const uint4*>(xr + i);
-      const T* xe = reinterpret_cast<const T*>(&xv);
-      float xf[VEC];
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) xf[v] = to_f32<T>(xe[v]);
-#pragma unroll
-      for (int e = 0; e < kExperts; ++e) {
-        const uint4 wv = *reinterpret_cast<const uint4*>(wg_s + e * d + i);
-        const T* we = reinterpret_cast<const T*>(&wv);
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[e] = fmaf(xf[v], to_f32<T>(we[v]), acc[e]);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < kExperts; ++e) acc[e] = wave_sum(acc[e]) + b[e];
+// Number of d-slices (waves) per 16-token group: the largest power of two up
+// to `cap` with d divisible by 32 * slices (d % 128 == 0 gives at least 4).
+__host__ __device__ inline int router_slices(int d, int cap) {
+  int sl = cap;
+  while (sl > 4 && d % (32 * sl) != 0) sl /= 2;
+  return sl;
+}
 
-    if (lane == 0) {
-      // Two largest, larger first; strict '>' keeps the lower index on ties.
-      int ia = 0;
-      float la = acc[0];
+// Top-2 and pair softmax from the 8 scores (lower index wins ties).
+__device__ __forceinline__ void select_top2(const float* sc, int32_t* idx_out, float* w_out) {
+  int ia = 0;
+  float la = sc[0];
 #pragma unroll
-      for (int e = 1; e < kExperts; ++e)
-        if (acc[e] > la) { la = acc[e]; ia = e; }
-      int ib = -1;
-      float lb = 0.0f;
+  for (int e = 1; e < kExperts; ++e)
+    if (sc[e] > la) { la = sc[e]; ia = e; }
+  int ib = -1;
+  float lb = 0.0f;
 #pragma unroll
-      for (int e = 0; e < kExperts; ++e)
-        if (e != ia && (ib < 0 || acc[e] > lb)) { lb = acc[e]; ib = e; }
-      // softmax over {la, lb} with the others at -inf
-      const float r = expf(lb - la);
-      const float ga = 1.0f / (1.0f + r);
-      const float gb = r / (1.0f + r);
-      idx_out[2 * t] = ia;
-      idx_out[2 * t + 1] = ib;
-      w_out[2 * t] = ga;
-      w_out[2 * t + 1] = gb;
-    }
-    if (logits_out && lane < kExperts) {
-      float v = acc[0];
+  for (int e = 0; e < kExperts; ++e)
+    if (e != ia && (ib < 0 || sc[e] > lb)) { lb = sc[e]; ib = e; }
+  const float r = expf(lb - la);
+  idx_out[0] = ia;
+  idx_out[1] = ib;
+  w_out[0] = 1.0f / (1.0f + r);
+  w_out[1] = r / (1.0f + r);
+}
+
+// Reduce the slice partials of one 16-token group (parked in LDS as
+// part[slice][lane] = f32x4) and route its tokens; run by one wave.
+__device__ __forceinline__ void router_finish_group(const f32x4 (*part)[kWave], int slices, int group, int T,
+                                                    const float* __restrict__ bias, int lane,
+                                                    int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                                                    float* __restrict__ logits_out) {
+  f32x4 sum = part[0][lane];
+  for (int sl = 1; sl < slices; ++sl) {
+    const f32x4 v = part[sl][lane];
+    sum[0] += v[0]; sum[1] += v[1]; sum[2] += v[2]; sum[3] += v[3];
+  }
+  // lane t < 16 holds experts 0..3 of token t, lane t+16 experts 4..7
+  float sc[kExperts];
 #pragma unroll
-      for (int e = 1; e < kExperts; ++e)
-        if (lane == e) v = acc[e];
-      logits_out[t * kExperts + lane] = v;
+  for (int q = 0; q < 4; ++q) {
+    sc[q] = sum[q];
+    sc[4 + q] = __shfl(sum[q], (lane % 16) + 16, kWave);
+  }
+  const int t = group * 16 + lane;
+  if (lane < 16 && t < T) {
+#pragma unroll
+    for (int e = 0; e < kExperts; ++e) sc[e] += bias ? bias[e] : 0.0f;
+    select_top2(sc, idx_out + kTopK * t, w_out + kTopK * t);
+    if (logits_out) {
+#pragma unroll
+      for (int e = 0; e < kExperts; ++e) logits_out[static_cast<int64_t>(t) * kExperts + e] = sc[e];
     }
   }
 }
 
+// Router for bf16: workgroup b routes tokens 16b..16b+15; its 16 waves
+// split d into router_slices(d, 16) slices (idle waves when fewer).
+__global__ void __launch_bounds__(1024) router_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
+                                                           const float* __restrict__ bias,
+                                                           int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                                                           float* __restrict__ logits_out, int T, int d) {
+  __shared__ f32x4 part[16][kWave];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int slices = router_slices(d, 16);
+  if (wave < slices) part[wave][lane] = router_scores_partial(x, wg, T, d, blockIdx.x, wave, slices, lane);
+  __syncthreads();
+  if (wave == 0) router_finish_group(part, slices, blockIdx.x, T, bias, lane, idx_out, w_out, logits_out);
+}
+
+// Small batches: routing and the expert-major permutation in one workgroup
+// (one launch and one global round trip fewer).  16 waves route the tokens,
+// then the same workgroup sorts the slots.
+template <typename T>
+__global__ void __launch_bounds__(kPermThreads) route_permute_kernel(
+    const T* __restrict__ x, const T* __restrict__ wg, const float* __restrict__ bias, int32_t* __restrict__ idx_out,
+    float* __restrict__ w_out, int32_t T_tokens, int d, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_rows, int32_t* __restrict__ counts_out) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* wg_s = reinterpret_cast<T*>(smem_raw);
+  float b[kExperts];
+  stage_router(wg, bias, wg_s, d, b);
+  const int lane = threadIdx.x % kWave;
+  for (int t = threadIdx.x / kWave; t < T_tokens; t += kPermWaves)
+    route_token(x + static_cast<int64_t>(t) * d, wg_s, b, d, lane, idx_out + 2 * t, w_out + 2 * t, nullptr);
+  __syncthreads();  // the ids written above are read back by permute_block
+  permute_block(idx_out, T_tokens * kTopK, offsets, sorted_slots, slot_rows, counts_out);
+}
+
 hipError_t launch_router(int dtype, const void* x, const void* wg, const float* bias, int32_t* idx, float* w,
                          float* logits, int64_t T, int d, int n_cu, hipStream_t s) {
+  if (dtype == kDtypeBF16) {
+    const int64_t groups = (T + 15) / 16;
+    hipLaunchKernelGGL(router_mfma_kernel, dim3(groups), dim3(1024), 0, s, static_cast<const bf16_t*>(x),
+                       static_cast<const bf16_t*>(wg), bias, idx, w, logits, static_cast<int>(T), d);
+    return hipGetLastError();
+  }
   const int threads = 256;
   const size_t elem = dtype == kDtypeBF16 ? 2 : 4;
   const size_t lds = kExperts * static_cast<size_t>(d) * elem;
@@ -110,6 +271,62 @@ hipError_t launch_router(int dtype, const void* x, const void* wg, const float* 
     hipLaunchKernelGGL(router_top2_kernel<float>, dim3(blocks), dim3(threads), lds, s,
                        static_cast<const float*>(x), static_cast<const float*>(wg), bias, idx, w, logits, T, d);
   }
+  return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// bf16 small batches: up to 4 token groups, each on 16/groups waves that
+// split d, then the permutation, all in one workgroup.
+__global__ void __launch_bounds__(kPermThreads) route_permute_mfma_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const float* __restrict__ bias,
+    int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t T_tokens, int d, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_rows, int32_t* __restrict__ counts_out) {
+  __shared__ f32x4 part[kPermWaves][kWave];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int groups = (T_tokens + 15) / 16;                  // 1..4 (T <= 64)
+  const int per_group = groups == 1 ? 16 : (groups == 2 ? 8 : 4);
+  const int slices = router_slices(d, per_group);
+  const int group = wave / per_group, slice = wave % per_group;
+  if (group < groups && slice < slices)
+    part[wave][lane] = router_scores_partial(x, wg, T_tokens, d, group, slice, slices, lane);
+  __syncthreads();
+  if (slice == 0 && group < groups)
+    router_finish_group(&part[wave], slices, group, T_tokens, bias, lane, idx_out, w_out, nullptr);
+  __syncthreads();  // the ids written above are read back by permute_block
+  permute_block(idx_out, T_tokens * kTopK, offsets, sorted_slots, slot_rows, counts_out);
+}
+
+}  // namespace moe
+
+namespace moe {
+
+hipError_t launch_route_permute(int dtype, const void* x, const void* wg, const float* bias, int32_t* idx, float* w,
+                                int32_t T, int d, int32_t* offsets, int32_t* sorted_slots, int32_t* slot_rows,
+                                int32_t* counts_out, hipStream_t s) {
+  if (dtype == kDtypeBF16) {
+    hipLaunchKernelGGL(route_permute_mfma_kernel, dim3(1), dim3(kPermThreads), 0, s, static_cast<const bf16_t*>(x),
+                       static_cast<const bf16_t*>(wg), bias, idx, w, T, d, offsets, sorted_slots, slot_rows,
+                       counts_out);
+    return hipGetLastError();
+  }
+  const size_t lds = kExperts * static_cast<size_t>(d) * (dtype == kDtypeBF16 ? 2 : 4);
+  const void* fn = dtype == kDtypeBF16 ? reinterpret_cast<const void*>(&route_permute_kernel<bf16_t>)
+                                       : reinterpret_cast<const void*>(&route_permute_kernel<float>);
+  if (lds > 64 * 1024) {
+    const hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (err != hipSuccess) return err;
+  }
+  if (dtype == kDtypeBF16)
+    hipLaunchKernelGGL(route_permute_kernel<bf16_t>, dim3(1), dim3(kPermThreads), lds, s,
+                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(wg), bias, idx, w, T, d, offsets,
+                       sorted_slots, slot_rows, counts_out);
+  else
+    hipLaunchKernelGGL(route_permute_kernel<float>, dim3(1), dim3(kPermThreads), lds, s,
+                       static_cast<const float*>(x), static_cast<const float*>(wg), bias, idx, w, T, d, offsets,
+                       sorted_slots, slot_rows, counts_out);
   return hipGetLastError();
 }
 

@@ -178,7 +178,8 @@ def test_batch_split_matches_whole_batch():
 
 
 def test_router_parity():
-    for dtype, T, d in (("bf16", 513, 4096), ("f32", 100, 128), ("bf16", 64, 8192)):
+    for dtype, T, d in (("bf16", 513, 4096), ("f32", 100, 128), ("bf16", 64, 8192), ("bf16", 37, 384),
+                        ("bf16", 100, 128)):
         layer = _layer(T, d, 128, dtype=dtype, seed=15)
         idx, w, logits = moe.router_topk(layer["x"], layer["w_gate"], return_logits=True)
         torch.cuda.synchronize()
