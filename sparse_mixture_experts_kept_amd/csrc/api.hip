@@ -67,7 +67,7 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 size_t align256(size_t v) { return (v + 255) & ~size_t{255}; }
 
 struct Workspace {
-  size_t idx, w, offsets, sorted, rows, h, y_rows, total;
+  size_t idx, w, offsets, sorted, rows, h, y_rows, y_rows2, total;
 };
 
 Workspace plan_workspace(const moe_dims* dims) {
@@ -81,6 +81,7 @@ Workspace plan_workspace(const moe_dims* dims) {
   ws.rows = o; o += align256(slots * 4);
   ws.h = o; o += align256(slots * dims->f * elem_size(dims->dtype));
   ws.y_rows = o; o += align256(slots * dims->d * 4);
+  ws.y_rows2 = o; o += align256(slots * dims->d * 4);  // second partial of the split down projection
   ws.total = o;
   return ws;
 }
@@ -121,7 +122,7 @@ moe_status run_down(const moe_dims* dims, const void* h, const int32_t* offs, co
   int n_cu = 0;
   const moe_status st = cu_count(&n_cu);
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_down_prefill(hb, offs, w2b, y_rows, dims->d, dims->f, n_cu, s));
+  return hip_status(moe::launch_down_prefill(hb, offs, w2b, y_rows, dims->d, dims->f, n_cu, 1, 0, s));
 }
 
 moe_status run_experts(const moe_dims* dims, const void* x, const int32_t* offs, const int32_t* sorted,
@@ -136,7 +137,7 @@ moe_status run_combine(const moe_dims* dims, const float* y_rows, const int32_t*
   int n_cu = 0;
   moe_status st = cu_count(&n_cu);
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_combine(dims->dtype, y_rows, slot_rows, w, y, dims->T, dims->d, n_cu, s));
+  return hip_status(moe::launch_combine(dims->dtype, y_rows, nullptr, slot_rows, w, y, dims->T, dims->d, n_cu, s));
 }
 
 }  // namespace
@@ -281,6 +282,22 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
     st = hip_status(moe::launch_permute(idx, static_cast<int32_t>(dims->T * dims->k), offs, sorted, rows,
                                         expert_counts_out, s));
     if (st != MOE_OK) return st;
+  }
+  if (dims->dtype == MOE_BF16 && !use_decode(dims) && dims->f % 256 == 0) {
+    // Prefill: the down projection's reduction is split in two (twice as many
+    // work units to spread over the CUs); the combine adds the two partial
+    // sums in a fixed order.
+    int n_cu = 0;
+    st = cu_count(&n_cu);
+    if (st != MOE_OK) return st;
+    st = run_up(dims, x, offs, sorted, w1, w3, h, s);
+    if (st != MOE_OK) return st;
+    float* y_rows2 = reinterpret_cast<float*>(ws + plan.y_rows2);
+    st = hip_status(moe::launch_down_prefill(static_cast<const bf16_t*>(h), offs, static_cast<const bf16_t*>(w2),
+                                             y_rows, dims->d, dims->f, n_cu, 2, y_rows2 - y_rows, s));
+    if (st != MOE_OK) return st;
+    return hip_status(
+        moe::launch_combine(dims->dtype, y_rows, y_rows2, rows, w, y, dims->T, dims->d, n_cu, s));
   }
   st = run_experts(dims, x, offs, sorted, w1, w3, w2, h, y_rows, s);
   if (st != MOE_OK) return st;

@@ -15,6 +15,7 @@ namespace moe {
 
 template <typename TO>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ y_rows,
+                                                      const float* __restrict__ y_rows2,
                                                       const int32_t* __restrict__ slot_rows,
                                                       const float* __restrict__ topk_w, TO* __restrict__ y,
                                                       int64_t T, int d) {
@@ -28,8 +29,14 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     const int64_t r1 = slot_rows[2 * t + 1];
     const float g0 = topk_w[2 * t];
     const float g1 = topk_w[2 * t + 1];
-    const float4 a = *reinterpret_cast<const float4*>(y_rows + r0 * d + c);
-    const float4 b = *reinterpret_cast<const float4*>(y_rows + r1 * d + c);
+    float4 a = *reinterpret_cast<const float4*>(y_rows + r0 * d + c);
+    float4 b = *reinterpret_cast<const float4*>(y_rows + r1 * d + c);
+    if (y_rows2) {  // second partial sum of a split reduction, added first
+      const float4 a2 = *reinterpret_cast<const float4*>(y_rows2 + r0 * d + c);
+      const float4 b2 = *reinterpret_cast<const float4*>(y_rows2 + r1 * d + c);
+      a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
+      b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
+    }
     float o[4];
     o[0] = g0 * a.x + g1 * b.x;
     o[1] = g0 * a.y + g1 * b.y;
@@ -46,17 +53,17 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   }
 }
 
-hipError_t launch_combine(int dtype, const float* y_rows, const int32_t* slot_rows, const float* topk_w, void* y,
-                          int64_t T, int d, int n_cu, hipStream_t s) {
+hipError_t launch_combine(int dtype, const float* y_rows, const float* y_rows2, const int32_t* slot_rows,
+                          const float* topk_w, void* y, int64_t T, int d, int n_cu, hipStream_t s) {
   const int64_t total = T * (d / 4);
   int64_t blocks = (total + 255) / 256;
   const int64_t cap = static_cast<int64_t>(n_cu) * 16;
   if (blocks > cap) blocks = cap;
   if (dtype == kDtypeBF16)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, y_rows, slot_rows, topk_w,
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, y_rows, y_rows2, slot_rows, topk_w,
                        static_cast<bf16_t*>(y), T, d);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, s, y_rows, slot_rows, topk_w,
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, s, y_rows, y_rows2, slot_rows, topk_w,
                        static_cast<float*>(y), T, d);
   return hipGetLastError();
 }

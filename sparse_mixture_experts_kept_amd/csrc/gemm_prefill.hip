@@ -103,11 +103,17 @@ __device__ __forceinline__ bool decode_tile(const int32_t* offs, int L, int n_ti
   return false;
 }
 
-template <bool SWIGLU>
+// SPLITK > 1 (down projection only): each tile's reduction is cut into
+// SPLITK equal parts run as separate work units; part s writes its partial
+// sums to Cout + s * split_stride (a separate buffer per part; the consumer
+// adds them in a fixed order).
+template <bool SWIGLU, int SPLITK>
 __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ gather, int k_div,
                             const int32_t* __restrict__ offs, const bf16_t* __restrict__ B0,
-                            const bf16_t* __restrict__ B1, void* __restrict__ Cout, int N, int K) {
+                            const bf16_t* __restrict__ B1, void* __restrict__ Cout, int N, int K,
+                            int64_t split_stride) {
+  static_assert(!SWIGLU || SPLITK == 1, "the SwiGLU epilogue needs the full reduction");
   // One LDS object holds the whole ring: [stage][A tile | B tile].
   __shared__ __align__(16) bf16_t ring[kStages][(kPBM + kPBN) * kPBK];
 
@@ -118,7 +124,7 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
   int total = 0;
 #pragma unroll
   for (int e = 0; e < kExperts; ++e) total += (offs[e + 1] - offs[e] + kPBM - 1) / kPBM;
-  total *= n_tiles_n;
+  total *= n_tiles_n * SPLITK;
 
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
@@ -140,9 +146,11 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
   const int ld_sub = lane / 4;
   const int ld_pchunk = lane % 4;
 
+  const int k_part = K / SPLITK;  // reduction length of one work unit
   for (int L = beg + slot; L < end; L += slots) {
     int e, mt, nt;
-    decode_tile(offs, L, n_tiles_n, &e, &mt, &nt);
+    const int ks = L % SPLITK;
+    decode_tile(offs, L / SPLITK, n_tiles_n, &e, &mt, &nt);
     const int row_begin = offs[e];
     const int rows = offs[e + 1] - row_begin;
     const int m0 = mt * kPBM;
@@ -157,14 +165,14 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
       const int ar = min(m0 + r, rows - 1);  // clamped rows are computed, never stored
       const int64_t g = row_begin + ar;
       const int64_t arow = gather ? static_cast<int64_t>(gather[g] / k_div) : g;
-      a_ptr[j] = A + arow * K + lchunk * 8;
+      a_ptr[j] = A + arow * K + ks * k_part + lchunk * 8;
       if constexpr (SWIGLU) {
         const bf16_t* base = (r < TN) ? B0 : B1;
         const int br = min(n0 + (r % TN), N - 1);
-        b_ptr[j] = base + (static_cast<int64_t>(e) * N + br) * K + lchunk * 8;
+        b_ptr[j] = base + (static_cast<int64_t>(e) * N + br) * K + ks * k_part + lchunk * 8;
       } else {
         const int br = min(n0 + r, N - 1);
-        b_ptr[j] = B0 + (static_cast<int64_t>(e) * N + br) * K + lchunk * 8;
+        b_ptr[j] = B0 + (static_cast<int64_t>(e) * N + br) * K + ks * k_part + lchunk * 8;
       }
     }
 
@@ -174,7 +182,7 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int KT = K / kPBK;
+    const int KT = k_part / kPBK;  // >= 4: K >= 256 and K/SPLITK a multiple of 128
     auto issue = [&](int kt) {
       const int buf = kt % kStages;
       const int koff = kt * kPBK;
@@ -280,7 +288,7 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
           *reinterpret_cast<uint2*>(C + orow * N + n) = p;
         }
       } else {
-        float* C = static_cast<float*>(Cout);
+        float* C = static_cast<float*>(Cout) + ks * split_stride;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int n = n0 + wn * 64 + j * 16 + 4 * lg;
@@ -296,17 +304,22 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
 hipError_t launch_up_prefill(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
                              const bf16_t* w3, bf16_t* h, int d, int f, int n_cu, hipStream_t s) {
   const int grid = (n_cu / kXcds) * kXcds;
-  hipLaunchKernelGGL(grouped_gemm_prefill_kernel<true>, dim3(grid), dim3(kPThreads), 0, s, x, sorted_slots, kTopK,
-                     offs, w1, w3, static_cast<void*>(h), f, d);
+  hipLaunchKernelGGL((grouped_gemm_prefill_kernel<true, 1>), dim3(grid), dim3(kPThreads), 0, s, x, sorted_slots, kTopK,
+                     offs, w1, w3, static_cast<void*>(h), f, d, int64_t{0});
   return hipGetLastError();
 }
 
 hipError_t launch_down_prefill(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,
-                               int n_cu, hipStream_t s) {
+                               int n_cu, int split, int64_t split_stride, hipStream_t s) {
   const int grid = (n_cu / kXcds) * kXcds;
-  hipLaunchKernelGGL(grouped_gemm_prefill_kernel<false>, dim3(grid), dim3(kPThreads), 0, s, h,
-                     static_cast<const int32_t*>(nullptr), 1, offs, w2, static_cast<const bf16_t*>(nullptr),
-                     static_cast<void*>(y_rows), d, f);
+  if (split == 2 && f % 256 == 0)
+    hipLaunchKernelGGL((grouped_gemm_prefill_kernel<false, 2>), dim3(grid), dim3(kPThreads), 0, s, h,
+                       static_cast<const int32_t*>(nullptr), 1, offs, w2, static_cast<const bf16_t*>(nullptr),
+                       static_cast<void*>(y_rows), d, f, split_stride);
+  else
+    hipLaunchKernelGGL((grouped_gemm_prefill_kernel<false, 1>), dim3(grid), dim3(kPThreads), 0, s, h,
+                       static_cast<const int32_t*>(nullptr), 1, offs, w2, static_cast<const bf16_t*>(nullptr),
+                       static_cast<void*>(y_rows), d, f, int64_t{0});
   return hipGetLastError();
 }
 

@@ -26,8 +26,10 @@ hipError_t launch_down_f32(const float* h, const int32_t* offs, const float* w2,
 
 hipError_t launch_up_prefill(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
                              const bf16_t* w3, bf16_t* h, int d, int f, int n_cu, hipStream_t s);
+// split == 2 (needs f % 256 == 0): two partial sums, the second at
+// y_rows + split_stride; otherwise one full sum in y_rows.
 hipError_t launch_down_prefill(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,
-                               int n_cu, hipStream_t s);
+                               int n_cu, int split, int64_t split_stride, hipStream_t s);
 
 hipError_t launch_up_decode(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
                             const bf16_t* w3, bf16_t* h, int d, int f, hipStream_t s);
@@ -43,8 +45,9 @@ hipError_t launch_down_combine_decode(const bf16_t* h, const int32_t* offs, cons
                                       const int32_t* slot_rows, const float* topk_w, bf16_t* y, int T, int d, int f,
                                       hipStream_t s);
 
-hipError_t launch_combine(int dtype, const float* y_rows, const int32_t* slot_rows, const float* topk_w, void* y,
-                          int64_t T, int d, int n_cu, hipStream_t s);
+// y_rows2 (optional): a second partial-sum buffer added to y_rows first.
+hipError_t launch_combine(int dtype, const float* y_rows, const float* y_rows2, const int32_t* slot_rows,
+                          const float* topk_w, void* y, int64_t T, int d, int n_cu, hipStream_t s);
 
 hipError_t launch_rmsnorm_residual(int dtype, float* resid, const void* y_add, void* u, int64_t T, int d, float eps,
                                    hipStream_t s);
