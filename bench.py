@@ -10,7 +10,9 @@ the same JSON line, alternating between two independent weight sets.
 Per-kernel times come from HIP events recorded on the stream the kernels run
 on, around the staged calls (moe_expert_up etc.), in a second timed loop.
 The CPU baseline is the fp64 oracle on a bounded sample of the same prefill
-workload, on this host's cores.
+workload, on this host's cores.  The 32-layer stack (T=8192, 90 GB of expert
+weights resident, RMSNorm + residual between layers) is reported as
+end-to-end tokens/s with per-layer routing histograms.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -42,7 +44,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=4096, help="tokens of the prefill workload the oracle runs")
     p.add_argument("--cpu-repeats", type=int, default=3)
-    p.add_argument("--only", choices=["prefill", "decode", "all"], default="all")
+    p.add_argument("--only", choices=["prefill", "decode", "stack", "all"], default="all")
+    p.add_argument("--stack-steps", type=int, default=3)
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -214,6 +217,31 @@ def main():
             result.update({"value": T / sec, "unit": "tokens/s", "ms_per_step": sec * 1e3,
                            "config": {"workload": "mixtral-moe-ffn-decode", "T": T, "d": d, "f": f, "E": E,
                                       "k": k}, "roofline": dec["roofline"]})
+
+    if args.only in ("stack", "all"):
+        from sparse_mixture_experts_kept_amd.stack import MoEStack
+
+        w = inputs.WORKLOADS["stack"]
+        _log(f"stack: generating {w['layers']} layers ({w['layers'] * A.expert_weight_bytes(d, f, E) / 1e9:.1f} GB)")
+        stack = MoEStack(w["T"], w["d"], w["f"], w["layers"], seed=5)
+        g = torch.Generator(device="cuda").manual_seed(5)
+        x0 = torch.randn((w["T"], w["d"]), generator=g, device="cuda", dtype=torch.float32)
+
+        def stack_step():
+            stack.load_input(x0)
+            stack.forward()
+
+        sec = time_layer(stack_step, args.stack_steps, 1, torch)
+        hist = stack.hist.cpu().tolist()
+        flops = w["layers"] * A.layer_flops(w["T"], d, f, E, k)
+        _log(f"stack: {sec * 1e3:.1f} ms per {w['layers']}-layer pass")
+        result["stack"] = {"workload": "mixtral-moe-ffn-stack", "T": w["T"], "layers": w["layers"],
+                           "ms_per_pass": sec * 1e3, "tokens_per_s": w["T"] / sec,
+                           "ms_per_layer": sec * 1e3 / w["layers"], "frac_of_bf16_peak": flops / sec / A.PEAK_BF16_FLOPS,
+                           "expert_weight_bytes_resident": w["layers"] * A.expert_weight_bytes(d, f, E),
+                           "routing_histograms": hist}
+        del stack
+        torch.cuda.empty_cache()
 
     print(json.dumps(result), flush=True)
 

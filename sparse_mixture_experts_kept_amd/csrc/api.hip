@@ -52,7 +52,8 @@ moe_status check_dims(const moe_dims* dims) {
 }
 
 // The prefill kernels pipeline the reduction in 32-wide steps and need at
-// least 8 of them (d, f >= 256); smaller layers always use the decode kernels.
+// least 8 of them (d, f >= 256, more than the 5-slot LDS ring); smaller
+// layers always use the decode kernels.
 constexpr int32_t kPrefillMinK = 256;
 
 bool use_decode(const moe_dims* dims) {
@@ -283,7 +284,7 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
                                         expert_counts_out, s));
     if (st != MOE_OK) return st;
   }
-  if (dims->dtype == MOE_BF16 && !use_decode(dims) && dims->f % 256 == 0) {
+  if (dims->dtype == MOE_BF16 && !use_decode(dims) && dims->f % 256 == 0 && dims->f >= 512) {
     // Prefill: the down projection's reduction is split in two (twice as many
     // work units to spread over the CUs); the combine adds the two partial
     // sums in a fixed order.

@@ -43,6 +43,7 @@ constexpr int kPBM = 256;
 constexpr int kPBN = 256;
 constexpr int kPBK = 32;       // k depth of one pipeline stage
 constexpr int kStages = 4;     // LDS ring depth (4 x 32 KiB)
+static_assert(kStages >= 4 && kStages <= 5, "the tail waits below cover rings of 4 or 5 slots");
 constexpr int kPThreads = 512;  // 8 waves: two per SIMD
 constexpr int kXcds = 8;
 constexpr int kGroupN = 8;
@@ -182,7 +183,7 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int KT = k_part / kPBK;  // >= 4: K >= 256 and K/SPLITK a multiple of 128
+    const int KT = k_part / kPBK;  // >= kStages (the host guarantees it)
     auto issue = [&](int kt) {
       const int buf = kt % kStages;
       const int koff = kt * kPBK;
@@ -229,14 +230,12 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
     // LDS data is complete when read and slots are free when refilled.
     // KT = K/32 is a multiple of 4 (K is a multiple of 128) and >= 8.
     const bool late = wave >= 4;
-    issue(0);
-    issue(1);
-    issue(2);
-    issue(3);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * kLoadsPerStage));
+#pragma unroll
+    for (int st = 0; st < kStages; ++st) issue(st);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 1) * kLoadsPerStage));
     lds_barrier();
     read_frags(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerStage) & lgkm0_mask());
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * kLoadsPerStage) & lgkm0_mask());
     if (late) lds_barrier();
     for (int kt = 0; kt < KT; ++kt) {
       __builtin_amdgcn_sched_barrier(0);
@@ -247,16 +246,21 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();
-      if (kt + 4 < KT) {
-        issue(kt + 4);
+      // memory(kt): stages issued so far reach min(kt + kStages, KT) - 1; wait
+      // for stage kt+2, i.e. allow the ones after it to stay in flight.
+      if (kt + kStages < KT) {
+        issue(kt + kStages);
         read_frags(kt + 1);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerStage) & lgkm0_mask());
-      } else if (kt + 3 < KT) {
-        read_frags(kt + 1);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerStage) & lgkm0_mask());
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * kLoadsPerStage) & lgkm0_mask());
       } else if (kt + 1 < KT) {
         read_frags(kt + 1);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & lgkm0_mask());
+        const int after = KT - 3 - kt;  // stages issued after kt+2 (< kStages - 2 here)
+        if (after >= 2)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerStage) & lgkm0_mask());
+        else if (after == 1)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerStage) & lgkm0_mask());
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & lgkm0_mask());
       }
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();
@@ -312,7 +316,8 @@ hipError_t launch_up_prefill(const bf16_t* x, const int32_t* offs, const int32_t
 hipError_t launch_down_prefill(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,
                                int n_cu, int split, int64_t split_stride, hipStream_t s) {
   const int grid = (n_cu / kXcds) * kXcds;
-  if (split == 2 && f % 256 == 0)
+  // each work unit needs K/split to be a multiple of 128 and at least kStages k-steps
+  if (split == 2 && f % 256 == 0 && f / 2 >= kStages * kPBK)
     hipLaunchKernelGGL((grouped_gemm_prefill_kernel<false, 2>), dim3(grid), dim3(kPThreads), 0, s, h,
                        static_cast<const int32_t*>(nullptr), 1, offs, w2, static_cast<const bf16_t*>(nullptr),
                        static_cast<void*>(y_rows), d, f, split_stride);

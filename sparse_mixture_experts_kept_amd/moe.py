@@ -216,18 +216,24 @@ def alloc_workspace(T, d, f, dtype, variant=VARIANT_AUTO, device="cuda"):
 
 class FFN:
     """The whole layer with preallocated outputs and workspace, for repeated
-    calls on the same shapes (what the benchmark times)."""
+    calls on the same shapes (what the benchmark times).  ``y``, ``workspace``
+    and ``counts`` may be supplied to share buffers between layers."""
 
-    def __init__(self, x, w_gate, w1, w3, w2, logit_bias=None, variant=VARIANT_AUTO, routing=True):
+    def __init__(self, x, w_gate, w1, w3, w2, logit_bias=None, variant=VARIANT_AUTO, routing=True, y=None,
+                 workspace=None, counts=None):
         self.lib = load_library()
         self.dims = _layer_dims(x, w1, variant)
         T, d = x.shape
         self.args = (x, w_gate, logit_bias, w1, w3, w2)
-        self.y = torch.empty((T, d), dtype=x.dtype, device=x.device)
+        self.y = y if y is not None else torch.empty((T, d), dtype=x.dtype, device=x.device)
         self.idx = torch.empty((T, TOP_K), dtype=torch.int32, device=x.device) if routing else None
         self.w = torch.empty((T, TOP_K), dtype=torch.float32, device=x.device) if routing else None
-        self.counts = torch.empty((E_EXPERTS,), dtype=torch.int32, device=x.device) if routing else None
-        self.ws = alloc_workspace(T, d, w1.shape[1], x.dtype, variant, x.device)
+        if counts is not None:
+            self.counts = counts
+        else:
+            self.counts = torch.empty((E_EXPERTS,), dtype=torch.int32, device=x.device) if routing else None
+        self.ws = workspace if workspace is not None else alloc_workspace(T, d, w1.shape[1], x.dtype, variant,
+                                                                          x.device)
         self.ws_bytes = ctypes.c_size_t(self.ws.numel())
 
     def __call__(self, stream=None):

@@ -307,3 +307,70 @@ def test_prefill_workloads_sampled(name):
     if name == "prefill_skewed":
         c = out["counts"].cpu().numpy() / (2 * layer["dims"]["T"])
         assert c.max() > 0.35 and c.min() < 0.06
+
+
+# --------------------------------------------------------------------------- stacked layers (RMSNorm + residual glue)
+
+
+def _check_stack_layer(stack, layer_idx, u, y, idx, sample):
+    """Teacher-forced check of one stacked layer on sampled tokens: the oracle
+    takes the GPU's own bf16 input u_l of that layer."""
+    lw = stack.weights[layer_idx]
+    us = _cpu(u)[sample]
+    widen = _widen_experts(lw)
+    ref = O.moe_ffn(us, _cpu(lw["w_gate"]), None, None, None, widen_expert=widen)
+    idx_g = idx.cpu().numpy().astype(np.int64)[sample]
+    gap = O.second_third_gap(ref["logits"])
+    clear = gap > GAP
+    np.testing.assert_array_equal(idx_g[clear], ref["idx"][clear])
+    assert O.is_valid_top2(ref["logits"], idx_g, GAP).all()
+    if not np.array_equal(idx_g, ref["idx"]):
+        ref = O.moe_ffn(us, _cpu(lw["w_gate"]), None, None, None, idx=idx_g, widen_expert=widen)
+    yg = O._f64(_cpu(y)[sample])
+    assert np.abs(yg - ref["y"]).max() <= _tol("bf16", ref["y"])
+
+
+def test_stack_small_every_layer():
+    from sparse_mixture_experts_kept_amd.stack import MoEStack
+    T, d, f, L = 300, 256, 512, 4
+    stack = MoEStack(T, d, f, L, seed=31)
+    g = torch.Generator(device="cuda").manual_seed(32)
+    x0 = torch.randn((T, d), generator=g, device="cuda", dtype=torch.float32)
+    stack.load_input(x0)
+    out = stack.forward(capture=tuple(range(L)))
+    torch.cuda.synchronize()
+    # glue: x_L = x_0 + sum_l y_l (fp32), u_0 = RMSNorm(x_0), u_L = RMSNorm(x_L)
+    resid = O._f64(x0.cpu())
+    np.testing.assert_allclose(O._f64(out[0][0].cpu()), O.rmsnorm(resid), rtol=1e-2, atol=1e-2)
+    for layer in range(L):
+        resid = resid + O._f64(out[layer][1].cpu())
+    np.testing.assert_allclose(stack.resid.cpu().numpy(), resid, rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(O._f64(stack.u.cpu()), O.rmsnorm(resid), rtol=1e-2, atol=1e-2)
+    for layer in range(L):
+        u, y, idx = out[layer]
+        _check_stack_layer(stack, layer, u, y, idx, np.arange(T))
+        np.testing.assert_array_equal(stack.hist[layer].cpu().numpy(),
+                                      np.bincount(idx.cpu().numpy().reshape(-1), minlength=8))
+
+
+def test_stack_workload_sampled():
+    """The 32-layer stack at full size (T=8192, d=4096, f=14336; 90 GB of
+    expert weights resident), teacher-forced on sampled tokens of three
+    layers; per-layer routing histograms are complete."""
+    from sparse_mixture_experts_kept_amd.stack import MoEStack
+    w = inputs.WORKLOADS["stack"]
+    stack = MoEStack(w["T"], w["d"], w["f"], w["layers"], seed=5)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    x0 = torch.randn((w["T"], w["d"]), generator=g, device="cuda", dtype=torch.float32)
+    stack.load_input(x0)
+    out = stack.forward(capture=(0, 15, 31))
+    torch.cuda.synchronize()
+    hist = stack.hist.cpu().numpy()
+    assert hist.shape == (32, 8) and (hist.sum(axis=1) == 2 * w["T"]).all()
+    rng = np.random.default_rng(55)
+    for layer in (0, 15, 31):
+        sample = np.sort(rng.choice(w["T"], size=24, replace=False))
+        u, y, idx = out[layer]
+        _check_stack_layer(stack, layer, u, y, idx, sample)
+    del stack, out
+    torch.cuda.empty_cache()
