@@ -93,6 +93,22 @@ def staged_timing(L, steps, torch, moe, variant):
     return out
 
 
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the rocprofv3 FETCH_SIZE and
+    WRITE_SIZE passes stored in data/traffic_<workload>.json, or None when
+    none were taken or the kernel's source changed since they were."""
+    from sparse_mixture_experts_kept_amd import rocprof_summary
+
+    path = os.path.join(ROOT, "sparse_mixture_experts_kept_amd", "data", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)["kernels"].get(kernel)
+    if rec is None or rec["source_sha256"] != rocprof_summary.source_hash(kernel):
+        return None
+    return rec["read_bytes"] + rec["write_bytes"]
+
+
 def cpu_baseline(L, sample_tokens, repeats):
     """The fp64 oracle on `sample_tokens` tokens of the workload (weights
     widened to fp64 beforehand, not timed)."""

@@ -71,3 +71,16 @@ def decode_layer_bytes(T: int, d: int, f: int, E: int, k: int, n_touched: int, e
     touched expert's weights once, the router matrix, x in and y out."""
     return (expert_weight_bytes(d, f, n_touched, elem_bytes) + E * d * elem_bytes
             + 2 * T * d * elem_bytes)
+
+
+def up_bytes(T: int, d: int, f: int, k: int, n_touched: int, elem_bytes: int = 2) -> int:
+    """Algorithmic HBM bytes of the up projection (gate + up + SwiGLU) over
+    one layer: each token row read once per slot, the touched experts' gate
+    and up matrices read once, h [T*k, f] written once."""
+    return (T * k * d + n_touched * 2 * f * d + T * k * f) * elem_bytes
+
+
+def down_bytes(T: int, d: int, f: int, k: int, n_touched: int, elem_bytes: int = 2, out_bytes: int = 4) -> int:
+    """Algorithmic HBM bytes of the down projection: h read once, the
+    touched experts' down matrices read once, fp32 y_rows [T*k, d] written."""
+    return (T * k * f + n_touched * d * f) * elem_bytes + T * k * d * out_bytes

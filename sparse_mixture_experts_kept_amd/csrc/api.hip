@@ -51,13 +51,11 @@ moe_status check_dims(const moe_dims* dims) {
   return MOE_OK;
 }
 
-// The prefill kernels pipeline the reduction in 32-wide steps and need at
-// least 8 of them (d, f >= 256, more than the 5-slot LDS ring); smaller
-// layers always use the decode kernels.
-constexpr int32_t kPrefillMinK = 256;
-
+// The prefill kernels pipeline the reduction in 64-wide stages (d, f >= 256)
+// and address gathered token rows with 32-bit offsets (x below 4 GiB); other
+// layers use the decode kernels.
 bool use_decode(const moe_dims* dims) {
-  if (dims->d < kPrefillMinK || dims->f < kPrefillMinK) return true;
+  if (!moe::prefill_fits(dims->T, dims->d, dims->f)) return true;
   if (dims->variant == MOE_VARIANT_DECODE) return true;
   if (dims->variant == MOE_VARIANT_PREFILL) return false;
   return dims->T <= kDecodeMaxTokens;
@@ -284,7 +282,7 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
                                         expert_counts_out, s));
     if (st != MOE_OK) return st;
   }
-  if (dims->dtype == MOE_BF16 && !use_decode(dims) && dims->f % 256 == 0 && dims->f >= 512) {
+  if (dims->dtype == MOE_BF16 && !use_decode(dims)) {
     // Prefill: the down projection's reduction is split in two (twice as many
     // work units to spread over the CUs); the combine adds the two partial
     // sums in a fixed order.

@@ -24,12 +24,19 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float v) {
   return __builtin_bit_cast(bf16_t, b);
 }
 
-// Two floats -> two packed bf16 (low half = a).
+// Two floats -> two packed bf16 (low half = a), one v_cvt_pk_bf16_f32.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  const bf16x2 v = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU(z) = z * sigmoid(z) with the hardware exp2 and reciprocal (about 1 ulp
+// each, far below the bf16 rounding of h); z -> -inf gives -0, +inf gives z.
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
 
 template <typename T>
 __device__ __forceinline__ float to_f32(T v);

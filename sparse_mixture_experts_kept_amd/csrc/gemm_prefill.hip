@@ -7,86 +7,77 @@
 //   up:   h[r, n]      = SiLU(x[tok(r)] . w1_e[n]) * (x[tok(r)] . w3_e[n])   -> bf16
 //   down: y_rows[r, n] = h[r] . w2_e[n]                                      -> fp32
 // for the rows r = offsets[e] .. offsets[e+1]-1 of expert e (tok(r) =
-// sorted_slots[r] / k, the gather fused into the A-tile load).
+// sorted_slots[r] / 2, the gather fused into the A-tile load).
 //
-// Design (gfx950): persistent workgroups of 512 threads (8 waves, two per
-// SIMD so one wave's LDS reads, loads and barrier waits hide under the other
-// wave's MFMAs), 256 x 256 block tiles stepped 32 deep in k, each wave a
-// 128 x 64 sub-tile built from v_mfma_f32_16x16x32_bf16 with fp32
-// accumulators.  A and B tiles live in a 4-deep LDS ring (4 x 32 KiB) filled
-// by direct global->LDS loads (global_load_lds_dwordx4, no staging
-// registers) up to four k-steps ahead.  The two waves of each SIMD run a
-// ping-pong schedule: one issues its MFMAs while the other refills the ring
-// and reads its next fragments, swapping at every barrier.  Waits are
-// explicit (s_waitcnt vmcnt(N) / lgkmcnt(0) before raw barriers), so the
-// compiler adds none that would serialise the ring.  LDS rows are 64 B with the 16-byte chunk index XOR-swizzled by
-// bits 1..2 of the row; of the layouts measured with the LDS bank-conflict
-// counter for the ds_read_b128 fragment pattern (16 rows x 4 chunks), this
-// one has no conflicts while chunk ^ (row >> 2) and the unswizzled layout
-// are 2-way conflicted.  For
-// the up projection the 256 B rows of a tile are 128 gate rows and the same
-// 128 up rows, so every wave holds matching gate/up accumulators and applies
-// SiLU(g)*u in registers before one bf16 rounding.
-//
-// Tile order: the tiles of one expert are walked in groups of 8 n-tiles x all
-// its m-tiles, so the 32 workgroups running together on one XCD share weight
-// panels (one per n-tile) and token panels (one per m-tile) in that XCD's L2.
-// Workgroup b runs on XCD b % 8 (round-robin dispatch); each XCD owns one
-// contiguous eighth of the tile list.  The host never learns the per-expert
-// counts: every workgroup reads the offsets on the device.
+// Design (gfx950):
+// - Persistent workgroups of 256 threads: 4 waves, one per SIMD.  Block tile
+//   256 (rows) x 256 (weight rows), stepped 64 deep in k so that every row of
+//   a tile is one full 128-byte line.  Each wave owns a 128 x 128 quarter:
+//   8 x 8 tiles of v_mfma_f32_16x16x32_bf16 with fp32 accumulators in the 256
+//   AGPRs.  Against 8 waves of 128 x 64 this reads a third less LDS per flop.
+// - LDS (160 KiB) holds 5 slots of 32 KiB: A tiles in 2 slots, B tiles in 3,
+//   so weight loads run up to two stages ahead and token loads one.  Slots
+//   are filled with direct global->LDS loads (global_load_lds_dwordx4, 1 KiB
+//   = 8 rows per instruction, no staging registers).
+// - Per stage and wave: 128 MFMAs in 16 rows of 8; after each row, two
+//   fragment reads (ds_read_b128) and one load, so the loads and reads are
+//   spread evenly under the MFMAs.  One barrier per stage, between its two
+//   k-halves.  All waits are explicit (s_waitcnt vmcnt(N) before the raw
+//   barrier; the compiler adds the LDS-read waits before the MFMAs).
+// - LDS rows are 128 B with the 16-byte chunk index XOR-swizzled by bits 1..3
+//   of the row; the bank-conflict counter reads zero for the 16 rows x 4
+//   chunks pattern of the fragment reads.
+// - Load addresses are a uniform stage base plus a 32-bit per-lane byte
+//   offset, so a load costs one address add and an M0 write.
+// - Tile order: the tiles of one expert are walked in groups of 4 n-tiles x
+//   all its m-tiles; workgroup b runs on XCD b % 8 and each XCD owns one
+//   contiguous eighth of the tile list, so the 32 workgroups of an XCD share
+//   weight and token panels in that XCD's L2.
+// - For the up projection the B tile is [gate 0-63 | up 0-63 | gate 64-127 |
+//   up 64-127] of 128 output columns, so each wave holds gate and up sums of
+//   the same 64 columns and applies SiLU(g)*u in registers before one bf16
+//   rounding.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace moe {
+namespace {
 
-constexpr int kPBM = 256;
-constexpr int kPBN = 256;
-constexpr int kPBK = 32;       // k depth of one pipeline stage
-constexpr int kStages = 4;     // LDS ring depth (4 x 32 KiB)
-static_assert(kStages >= 4 && kStages <= 5, "the tail waits below cover rings of 4 or 5 slots");
-constexpr int kPThreads = 512;  // 8 waves: two per SIMD
+constexpr int kBM = 256;       // block rows (slots)
+constexpr int kBN = 256;       // block weight rows
+constexpr int kBK = 64;        // k depth of one stage (128 B per row)
+constexpr int kThreads = 256;  // 4 waves
 constexpr int kXcds = 8;
-constexpr int kGroupN = 8;
-// Per wave and stage: 2 A loads + 2 B loads of 1 KiB (16 rows x 64 B).
-constexpr int kLoadsPerStage = 4;
+constexpr int kGroupN = 4;     // n-tiles per group in the tile order
+constexpr int kSlotElems = kBM * kBK;  // one 32 KiB slot (kBM == kBN)
 
 #define GLOBAL_PTR(p) ((const __attribute__((address_space(1))) void*)(p))
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-// s_waitcnt immediate that waits until at most n vector-memory loads are
-// outstanding (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and
-// lgkmcnt left at their maxima so they are not waited on).
+// s_waitcnt immediate: at most n vector-memory ops outstanding (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14), expcnt and lgkmcnt not waited on.
 constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
-
-// The same immediate with lgkmcnt forced to 0 (also wait for LDS reads).
+// ... and every LDS read complete as well.
 constexpr int lgkm0_mask() { return ~(0xF << 8); }
-// Instruction classes of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedVmemRead = 0x020;
-constexpr int kSchedDsRead = 0x100;
 
-// Wait for every outstanding LDS read only (vmcnt and expcnt at maximum).
-constexpr int kLgkm0Only = 0xF | (0x3 << 14) | (0x7 << 4);
-
-// Workgroup barrier for the LDS ring.  The waits it needs are issued
-// explicitly before it; the empty asm keeps the compiler from moving LDS
-// accesses across it.
+// Workgroup barrier for the LDS slots; the waits it needs are issued before
+// it, the empty asm keeps LDS accesses from moving across it.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// Element offset of (row, logical 16-byte chunk) in a [rows][32] bf16 tile.
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * kPBK + ((chunk ^ ((row >> 1) & 3)) << 3); }
+// Element offset of (row, logical 16-byte chunk) in a [rows][64] bf16 tile.
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 3); }
 
-// (expert, m-tile, n-tile) of logical tile L; returns false past the end.
+// (expert, m-tile, n-tile) of logical tile L; false past the end.
 __device__ __forceinline__ bool decode_tile(const int32_t* offs, int L, int n_tiles_n, int* e_out, int* mt_out,
                                             int* nt_out) {
   int acc = 0;
 #pragma unroll
   for (int e = 0; e < kExperts; ++e) {
     const int cnt = offs[e + 1] - offs[e];
-    const int mts = (cnt + kPBM - 1) / kPBM;
+    const int mts = (cnt + kBM - 1) / kBM;
     const int tiles = mts * n_tiles_n;
     if (L < acc + tiles) {
       const int local = L - acc;
@@ -104,27 +95,102 @@ __device__ __forceinline__ bool decode_tile(const int32_t* offs, int L, int n_ti
   return false;
 }
 
+// ---- pieces of the main loop (macros keep the fragment arrays in registers)
+
+// Load j (0..7) of this wave for stage KT: 8 rows of 128 B, A rows go to A
+// slot KT&1, B rows to B slot BSL (0..2).
+#define LOAD_A(KT_, J)                                                                                   \
+  __builtin_amdgcn_global_load_lds(                                                                      \
+      GLOBAL_PTR(reinterpret_cast<const char*>(a_base + static_cast<int64_t>(KT_) * kBK) + a_off[J]),      \
+      LDS_PTR(&ring[(KT_) & 1][(wave * 64 + (J) * 8) * kBK]), 16, 0, 0);
+#define LOAD_B(KT_, J, BSL)                                                                              \
+  __builtin_amdgcn_global_load_lds(                                                                      \
+      GLOBAL_PTR(reinterpret_cast<const char*>(b_base + static_cast<int64_t>((J) * 8) * K +                \
+                                               static_cast<int64_t>(KT_) * kBK) + b_off[(J) & 1]),       \
+      LDS_PTR(&ring[2 + (BSL)][(wave * 64 + (J) * 8) * kBK]), 16, 0, 0);
+
+// Fragments of k-half H (0/1): B block J from B slot BSL, A block I from A slot AS.
+#define READ_B(FB, BSL, H, J) \
+  FB[J] = *reinterpret_cast<const bf16x8*>(&ring[2 + (BSL)][lds_off(wn * 128 + (J) * 16 + l16, (H) * 4 + lg)]);
+#define READ_A(FA, AS, H, I) \
+  FA[I] = *reinterpret_cast<const bf16x8*>(&ring[AS][lds_off(wm * 128 + (I) * 16 + l16, (H) * 4 + lg)]);
+// Pair Q (0..7) of the 16 fragments of a set, B first: MFMA row 0 needs all
+// of B and A block 0.
+// (The "& 7" only keeps the untaken branch's indices in range.)
+#define READ_PAIR(FA, FB, AS, BSL, H, Q)     \
+  if ((Q) < 4) {                             \
+    READ_B(FB, BSL, H, (2 * (Q)) & 7);       \
+    READ_B(FB, BSL, H, (2 * (Q) + 1) & 7);   \
+  } else {                                   \
+    READ_A(FA, AS, H, (2 * (Q) - 8) & 7);    \
+    READ_A(FA, AS, H, (2 * (Q) - 7) & 7);    \
+  }
+
+// MFMA row I: the wave's A block I times its 8 B blocks.
+#define MFMA_ROW(FA, FB, I)                                                                               \
+  _Pragma("unroll") for (int j = 0; j < 8; ++j) acc[I][j] =                                               \
+      __builtin_amdgcn_mfma_f32_16x16x32_bf16(FB[j], FA[I], acc[I][j], 0, 0, 0);
+
+// Stage KT (A in slot KT&1, B in B slot BS = KT%3; BS1, BS2 = (KT+1)%3, (KT+2)%3):
+//   half 0: MFMA rows of set 0; after each row two reads of k-half 1 into
+//           set 1 and (LD) one B load of stage KT+2 into B slot BS2 (free
+//           since the barrier of stage KT-1)
+//   wait until only stage KT+2's B loads are in flight; barrier.  All waves
+//           have read stage KT completely, and stage KT+1 has landed.
+//   half 1: MFMA rows of set 1; after each row (RD) two reads of k-half 0 of
+//           stage KT+1 into set 0 and (LD) one A load of stage KT+2 into A
+//           slot KT&1.
+// Reads are issued one row early at the end of each half so the first MFMAs
+// of the next half find them complete.
+#define STAGE(KT_, BS, BS1, BS2, LD, RD)                                                \
+  {                                                                                     \
+    const int as_ = (KT_) & 1;                                                          \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                     \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      MFMA_ROW(fa0, fb0, i);                                                            \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      if (LD) { LOAD_B((KT_) + 2, i, BS2); }                                            \
+      if (i < 7) { READ_PAIR(fa1, fb1, as_, BS, 1, i); }                                \
+      if (i == 6) { READ_PAIR(fa1, fb1, as_, BS, 1, 7); }                               \
+    }                                                                                   \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
+    if (LD)                                                                             \
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(8) & lgkm0_mask());                          \
+    else                                                                                \
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & lgkm0_mask());                          \
+    lds_barrier();                                                                      \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                     \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      MFMA_ROW(fa1, fb1, i);                                                            \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      if (LD) { LOAD_A((KT_) + 2, i); }                                                 \
+      if ((RD) && i < 7) { READ_PAIR(fa0, fb0, as_ ^ 1, BS1, 0, i); }                   \
+      if ((RD) && i == 6) { READ_PAIR(fa0, fb0, as_ ^ 1, BS1, 0, 7); }                  \
+    }                                                                                   \
+    __builtin_amdgcn_sched_barrier(0);                                                  \
+  }
+
 // SPLITK > 1 (down projection only): each tile's reduction is cut into
 // SPLITK equal parts run as separate work units; part s writes its partial
 // sums to Cout + s * split_stride (a separate buffer per part; the consumer
 // adds them in a fixed order).
 template <bool SWIGLU, int SPLITK>
-__global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ gather, int k_div,
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ gather,
                             const int32_t* __restrict__ offs, const bf16_t* __restrict__ B0,
                             const bf16_t* __restrict__ B1, void* __restrict__ Cout, int N, int K,
                             int64_t split_stride) {
   static_assert(!SWIGLU || SPLITK == 1, "the SwiGLU epilogue needs the full reduction");
-  // One LDS object holds the whole ring: [stage][A tile | B tile].
-  __shared__ __align__(16) bf16_t ring[kStages][(kPBM + kPBN) * kPBK];
+  // One LDS object for all slots: A slots 0-1, B slots 2-4.
+  __shared__ __align__(16) bf16_t ring[5][kSlotElems];
 
   // Output columns per tile: 128 (SwiGLU: 128 gate + 128 up B rows) or 256.
-  constexpr int TN = SWIGLU ? kPBN / 2 : kPBN;
+  constexpr int TN = SWIGLU ? kBN / 2 : kBN;
   const int n_tiles_n = (N + TN - 1) / TN;
 
   int total = 0;
 #pragma unroll
-  for (int e = 0; e < kExperts; ++e) total += (offs[e + 1] - offs[e] + kPBM - 1) / kPBM;
+  for (int e = 0; e < kExperts; ++e) total += (offs[e + 1] - offs[e] + kBM - 1) / kBM;
   total *= n_tiles_n * SPLITK;
 
   const int xcd = blockIdx.x % kXcds;
@@ -134,146 +200,97 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
   const int beg = xcd * per;
   const int end = min(beg + per, total);
 
-  const int tid = threadIdx.x;
-  const int lane = tid % kWave;
-  const int wave = tid / kWave;
-  // 8 waves as 2 (rows) x 4 (columns); each owns a 128 x 64 output block.
-  const int wm = wave / 4, wn = wave % 4;
+  const int lane = threadIdx.x % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wm = wave / 2, wn = wave % 2;  // 2 x 2 waves of 128 x 128
   const int l16 = lane % 16, lg = lane / 16;
-  // Direct-to-LDS loads: one global_load_lds_dwordx4 writes 64 lanes x 16 B =
-  // 16 rows of 64 B.  Wave w fills A and B rows w*32 + j*16 + lane/4
-  // (j = 0, 1); the lane's physical chunk is lane%4, so it fetches the
-  // logical chunk that the swizzle stores there.
-  const int ld_sub = lane / 4;
-  const int ld_pchunk = lane % 4;
+  // Loads: lane -> (row ld_row of the 8, physical chunk pc).  LDS row
+  // r = wave*64 + j*8 + ld_row has swizzle (r >> 1) & 7 = (ld_row >> 1) |
+  // 4*(j & 1), so the logical chunk a lane fetches takes two values.
+  const int ld_row = lane / 8, pc = lane % 8;
+  const int lc_even = (pc ^ (ld_row >> 1)) * 8;
+  const int lc_odd = lc_even ^ 32;
+  const int k_part = K / SPLITK;
+  const int KT = k_part / kBK;  // >= 2 (the host guarantees it)
 
-  const int k_part = K / SPLITK;  // reduction length of one work unit
   for (int L = beg + slot; L < end; L += slots) {
     int e, mt, nt;
     const int ks = L % SPLITK;
     decode_tile(offs, L / SPLITK, n_tiles_n, &e, &mt, &nt);
     const int row_begin = offs[e];
     const int rows = offs[e + 1] - row_begin;
-    const int m0 = mt * kPBM;
+    const int m0 = mt * kBM;
     const int n0 = nt * TN;
 
-    const bf16_t* a_ptr[2];
-    const bf16_t* b_ptr[2];
+    // A: token rows (gathered, up) or this tile's h rows (down), as byte
+    // offsets from a uniform base; clamped rows are computed, never stored.
+    const bf16_t* a_base;
+    uint32_t a_off[8];
+    if constexpr (SWIGLU) {
+      int32_t slot_id[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int r = wave * 32 + j * 16 + ld_sub;
-      const int lchunk = ld_pchunk ^ ((r >> 1) & 3);
-      const int ar = min(m0 + r, rows - 1);  // clamped rows are computed, never stored
-      const int64_t g = row_begin + ar;
-      const int64_t arow = gather ? static_cast<int64_t>(gather[g] / k_div) : g;
-      a_ptr[j] = A + arow * K + ks * k_part + lchunk * 8;
-      if constexpr (SWIGLU) {
-        const bf16_t* base = (r < TN) ? B0 : B1;
-        const int br = min(n0 + (r % TN), N - 1);
-        b_ptr[j] = base + (static_cast<int64_t>(e) * N + br) * K + ks * k_part + lchunk * 8;
-      } else {
-        const int br = min(n0 + r, N - 1);
-        b_ptr[j] = B0 + (static_cast<int64_t>(e) * N + br) * K + ks * k_part + lchunk * 8;
-      }
+      for (int j = 0; j < 8; ++j) slot_id[j] = gather[row_begin + min(m0 + wave * 64 + j * 8 + ld_row, rows - 1)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)  // x is below 4 GiB (the host checks)
+        a_off[j] = ((static_cast<uint32_t>(slot_id[j]) / kTopK) * static_cast<uint32_t>(K) +
+                    ((j & 1) ? lc_odd : lc_even)) * 2u;
+      a_base = A;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        a_off[j] = (static_cast<uint32_t>(min(wave * 64 + j * 8 + ld_row, rows - 1 - m0)) * static_cast<uint32_t>(K) +
+                    ((j & 1) ? lc_odd : lc_even)) * 2u;
+      a_base = A + static_cast<int64_t>(row_begin + m0) * K + ks * k_part;
     }
+    // B: a wave's 64 weight rows are contiguous and all in range or all past
+    // N (N is a multiple of 128), so clamping the block keeps them in range.
+    const bf16_t* bsrc = SWIGLU ? ((wave & 1) ? B1 : B0) : B0;
+    const int brow0 = min(SWIGLU ? n0 + (wave >> 1) * 64 : n0 + wave * 64, N - 64);
+    const bf16_t* b_base = bsrc + (static_cast<int64_t>(e) * N + brow0) * K + ks * k_part;
+    uint32_t b_off[2];
+    b_off[0] = (static_cast<uint32_t>(ld_row) * static_cast<uint32_t>(K) + lc_even) * 2u;
+    b_off[1] = (static_cast<uint32_t>(ld_row) * static_cast<uint32_t>(K) + lc_odd) * 2u;
 
-    f32x4 acc[8][4];
+    f32x4 acc[8][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bf16x8 fa0[8], fb0[8], fa1[8], fb1[8];
 
-    const int KT = k_part / kPBK;  // >= kStages (the host guarantees it)
-    auto issue = [&](int kt) {
-      const int buf = kt % kStages;
-      const int koff = kt * kPBK;
+    // Prologue: stages 0 and 1 (A and B); the steady state then keeps one A
+    // stage and two B stages in flight.
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r0 = wave * 32 + j * 16;
-        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(a_ptr[j] + koff), LDS_PTR(&ring[buf][r0 * kPBK]), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(GLOBAL_PTR(b_ptr[j] + koff), LDS_PTR(&ring[buf][(kPBM + r0) * kPBK]), 16, 0,
-                                         0);
-      }
-    };
-    // B rows of this wave's 4 weight fragments: SwiGLU = 2 gate + the same 2 up.
-    int b_row[4];
+    for (int j = 0; j < 8; ++j) { LOAD_A(0, j); LOAD_B(0, j, 0); }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (SWIGLU)
-        b_row[j] = (j < 2 ? 0 : TN) + wn * 32 + (j % 2) * 16 + l16;
-      else
-        b_row[j] = wn * 64 + j * 16 + l16;
-    }
-
-    // Fragment registers of the current k-step.
-    bf16x8 fa[8], fb[4];
-    auto read_frags = [&](int kt) {
-      const bf16_t* as_ = ring[kt % kStages];
-      const bf16_t* bs_ = as_ + kPBM * kPBK;
+    for (int j = 0; j < 8; ++j) { LOAD_B(1, j, 1); }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fb[j] = *reinterpret_cast<const bf16x8*>(&bs_[lds_off(b_row[j], lg)]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(&as_[lds_off(wm * 128 + i * 16 + l16, lg)]);
-    };
-
-    // Ping-pong: waves 0-3 (one per SIMD) and waves 4-7 (the other wave of
-    // each SIMD) alternate between a compute phase (32 MFMAs from registers)
-    // and a memory phase (refill a ring slot, read the next fragments, wait),
-    // swapping at every barrier, so each SIMD's matrix pipe always has one
-    // wave feeding it.  Waves 4-7 start one phase late.
-    //   compute(k): MFMAs of step k.
-    //   memory(k):  refill slot k%4 with stage k+4, read step k+1's fragments,
-    //               wait for this wave's loads of stage k+2 and for the reads.
-    // Every wave waits for its own loads of stage k+1 before the barrier that
-    // opens the first memory(k) (end of memory(k-1)), and for its reads of
-    // step k before the barrier that opens the first refill of slot k, so
-    // LDS data is complete when read and slots are free when refilled.
-    // KT = K/32 is a multiple of 4 (K is a multiple of 128) and >= 8.
-    const bool late = wave >= 4;
-#pragma unroll
-    for (int st = 0; st < kStages; ++st) issue(st);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 1) * kLoadsPerStage));
+    for (int j = 0; j < 8; ++j) { LOAD_A(1, j); }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));  // this wave's stage-0 loads landed
     lds_barrier();
-    read_frags(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * kLoadsPerStage) & lgkm0_mask());
-    if (late) lds_barrier();
-    for (int kt = 0; kt < KT; ++kt) {
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      lds_barrier();
-      // memory(kt): stages issued so far reach min(kt + kStages, KT) - 1; wait
-      // for stage kt+2, i.e. allow the ones after it to stay in flight.
-      if (kt + kStages < KT) {
-        issue(kt + kStages);
-        read_frags(kt + 1);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * kLoadsPerStage) & lgkm0_mask());
-      } else if (kt + 1 < KT) {
-        read_frags(kt + 1);
-        const int after = KT - 3 - kt;  // stages issued after kt+2 (< kStages - 2 here)
-        if (after >= 2)
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerStage) & lgkm0_mask());
-        else if (after == 1)
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoadsPerStage) & lgkm0_mask());
-        else
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & lgkm0_mask());
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      lds_barrier();
+    for (int q = 0; q < 8; ++q) { READ_PAIR(fa0, fb0, 0, 0, 0, q); }
+    int kt = 0, bs = 0;
+    for (; kt < KT - 2; ++kt) {
+      const int bs1 = bs == 2 ? 0 : bs + 1;
+      const int bs2 = bs1 == 2 ? 0 : bs1 + 1;
+      STAGE(kt, bs, bs1, bs2, true, true);
+      bs = bs1;
     }
-    if (!late) lds_barrier();
-    // Every wave is done with the ring before the next tile refills it.
-    __syncthreads();
+    {
+      const int bs1 = bs == 2 ? 0 : bs + 1;
+      STAGE(kt, bs, bs1, 0, false, true);
+      ++kt;
+      bs = bs1;
+    }
+    // The last stage's barrier also orders every wave's final reads before
+    // the next tile's prologue refills the slots.
+    STAGE(kt, bs, 0, 0, false, false);
 
-    // Epilogue.  acc[i][j][q] is output row m = wm*128 + i*16 + l16 and
-    // column wave_col(j) + 4*lg + q (B rows were MFMA src0).
+    // Epilogue.  acc[i][j][q]: output row m0 + wm*128 + i*16 + l16, B-tile
+    // row wn*128 + j*16 + 4*lg + q (the B rows were MFMA src0).
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      // one 16-row block at a time keeps the accumulators in place until used
       __builtin_amdgcn_sched_barrier(0);
       const int m = m0 + wm * 128 + i * 16 + l16;
       if (m >= rows) continue;
@@ -281,11 +298,10 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
       if constexpr (SWIGLU) {
         bf16_t* C = static_cast<bf16_t*>(Cout);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int n = n0 + wn * 32 + j * 16 + 4 * lg;
-          if (n >= N) continue;
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + wn * 64 + j * 16 + 4 * lg;
           const f32x4 g = acc[i][j];
-          const f32x4 u = acc[i][j + 2];
+          const f32x4 u = acc[i][j + 4];
           uint2 p;
           p.x = pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
           p.y = pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
@@ -294,8 +310,8 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
       } else {
         float* C = static_cast<float*>(Cout) + ks * split_stride;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = n0 + wn * 64 + j * 16 + 4 * lg;
+        for (int j = 0; j < 8; ++j) {
+          const int n = n0 + wn * 128 + j * 16 + 4 * lg;
           if (n >= N) continue;
           const f32x4 v = acc[i][j];
           *reinterpret_cast<float4*>(C + orow * N + n) = make_float4(v[0], v[1], v[2], v[3]);
@@ -305,25 +321,41 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
   }
 }
 
+#undef LOAD_A
+#undef LOAD_B
+#undef READ_B
+#undef READ_A
+#undef READ_PAIR
+#undef MFMA_ROW
+#undef STAGE
+
+}  // namespace
+
+bool prefill_fits(int64_t T, int d, int f) {
+  // K/split a multiple of 64 and at least two stages; gathered token rows
+  // addressed with 32-bit byte offsets.
+  return d % 128 == 0 && f % 128 == 0 && d >= 256 && f >= 256 && T * d * 2 < (int64_t{1} << 32);
+}
+
 hipError_t launch_up_prefill(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
                              const bf16_t* w3, bf16_t* h, int d, int f, int n_cu, hipStream_t s) {
   const int grid = (n_cu / kXcds) * kXcds;
-  hipLaunchKernelGGL((grouped_gemm_prefill_kernel<true, 1>), dim3(grid), dim3(kPThreads), 0, s, x, sorted_slots, kTopK,
-                     offs, w1, w3, static_cast<void*>(h), f, d, int64_t{0});
+  hipLaunchKernelGGL((grouped_gemm_prefill_kernel<true, 1>), dim3(grid), dim3(kThreads), 0, s, x, sorted_slots, offs,
+                     w1, w3, static_cast<void*>(h), f, d, int64_t{0});
   return hipGetLastError();
 }
 
 hipError_t launch_down_prefill(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,
                                int n_cu, int split, int64_t split_stride, hipStream_t s) {
   const int grid = (n_cu / kXcds) * kXcds;
-  // each work unit needs K/split to be a multiple of 128 and at least kStages k-steps
-  if (split == 2 && f % 256 == 0 && f / 2 >= kStages * kPBK)
-    hipLaunchKernelGGL((grouped_gemm_prefill_kernel<false, 2>), dim3(grid), dim3(kPThreads), 0, s, h,
-                       static_cast<const int32_t*>(nullptr), 1, offs, w2, static_cast<const bf16_t*>(nullptr),
+  // each work unit needs K/split to be a multiple of 64 and at least 2 stages
+  if (split == 2 && f % 128 == 0 && f / 2 >= 2 * kBK)
+    hipLaunchKernelGGL((grouped_gemm_prefill_kernel<false, 2>), dim3(grid), dim3(kThreads), 0, s, h,
+                       static_cast<const int32_t*>(nullptr), offs, w2, static_cast<const bf16_t*>(nullptr),
                        static_cast<void*>(y_rows), d, f, split_stride);
   else
-    hipLaunchKernelGGL((grouped_gemm_prefill_kernel<false, 1>), dim3(grid), dim3(kPThreads), 0, s, h,
-                       static_cast<const int32_t*>(nullptr), 1, offs, w2, static_cast<const bf16_t*>(nullptr),
+    hipLaunchKernelGGL((grouped_gemm_prefill_kernel<false, 1>), dim3(grid), dim3(kThreads), 0, s, h,
+                       static_cast<const int32_t*>(nullptr), offs, w2, static_cast<const bf16_t*>(nullptr),
                        static_cast<void*>(y_rows), d, f, int64_t{0});
   return hipGetLastError();
 }

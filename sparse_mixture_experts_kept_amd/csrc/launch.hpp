@@ -24,9 +24,12 @@ hipError_t launch_up_f32(const float* x, const int32_t* offs, const int32_t* sor
 hipError_t launch_down_f32(const float* h, const int32_t* offs, const float* w2, float* y_rows, int64_t n_slots,
                            int d, int f, hipStream_t s);
 
+// The prefill kernels handle the layer: d, f multiples of 128 and >= 256,
+// and x (T x d bf16) smaller than 4 GiB.
+bool prefill_fits(int64_t T, int d, int f);
 hipError_t launch_up_prefill(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
                              const bf16_t* w3, bf16_t* h, int d, int f, int n_cu, hipStream_t s);
-// split == 2 (needs f % 256 == 0): two partial sums, the second at
+// split == 2: two partial sums over the two halves of f, the second at
 // y_rows + split_stride; otherwise one full sum in y_rows.
 hipError_t launch_down_prefill(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,
                                int n_cu, int split, int64_t split_stride, hipStream_t s);

@@ -4,6 +4,12 @@
         per-kernel calls, total and average duration (us)
     python -m sparse_mixture_experts_kept_amd.rocprof_summary pmc DB [DB ...]
         per-kernel mean value of each collected counter per dispatch
+    python -m sparse_mixture_experts_kept_amd.rocprof_summary traffic \
+            FETCH_DB WRITE_DB COPY_FETCH_DB COPY_WRITE_DB COPY_BYTES [OUT.json]
+        HBM bytes per dispatch of every kernel: FETCH_SIZE and WRITE_SIZE
+        (KiB) scaled by what the same counters read for a plain copy of
+        COPY_BYTES bytes; OUT.json (optional) also records a hash of each
+        kernel's source so that stale figures can be recognised
 
 Kernel names are shortened to the text before the argument list.
 """
@@ -49,6 +55,72 @@ def pmc(dbs):
         print(f"| {k} | {n} | " + " | ".join(cells) + " |")
 
 
+def _mean_counter(db, counter):
+    vals = defaultdict(list)
+    con = sqlite3.connect(db)
+    for name, c, value in con.execute("select kernel_name, counter_name, value from counters_collection"):
+        if c == counter:
+            vals[short(name)].append(value)
+    return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+
+
+# Source files each kernel family is compiled from (relative to csrc/).
+KERNEL_SOURCES = {
+    "grouped_gemm_prefill_kernel": ["gemm_prefill.hip", "common.hpp"],
+    "grouped_gemm_decode_kernel": ["gemm_decode.hip", "common.hpp"],
+    "down_combine_decode_kernel": ["gemm_decode.hip", "common.hpp"],
+    "router": ["router.hip", "permute_dev.hpp", "common.hpp"],
+    "route_permute": ["router.hip", "permute_dev.hpp", "common.hpp"],
+    "permute_kernel": ["permute.hip", "permute_dev.hpp", "common.hpp"],
+    "combine_kernel": ["combine.hip", "common.hpp"],
+    "rmsnorm_residual_kernel": ["combine.hip", "common.hpp"],
+}
+
+
+def source_hash(kernel: str):
+    """sha256 over the sources a kernel is built from, or None if unknown."""
+    import hashlib
+    import os
+
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    for prefix, files in KERNEL_SOURCES.items():
+        if kernel.startswith(prefix):
+            h = hashlib.sha256()
+            for fn in files:
+                with open(os.path.join(csrc, fn), "rb") as fh:
+                    h.update(fh.read())
+            return h.hexdigest()
+    return None
+
+
+def traffic(args):
+    import json
+
+    fetch_db, write_db, copy_fetch_db, copy_write_db, copy_bytes = args[:5]
+    out_path = args[5] if len(args) > 5 else None
+    copy_bytes = float(copy_bytes)
+    fetch, n_fetch = _mean_counter(fetch_db, "FETCH_SIZE")
+    write, n_write = _mean_counter(write_db, "WRITE_SIZE")
+    cf, _ = _mean_counter(copy_fetch_db, "FETCH_SIZE")
+    cw, _ = _mean_counter(copy_write_db, "WRITE_SIZE")
+    # The copy probe is the largest kernel in its run.
+    f_factor = copy_bytes / (max(cf.values()) * 1024.0)
+    w_factor = copy_bytes / (max(cw.values()) * 1024.0)
+    print(f"copy probe ({copy_bytes:.0f} B read and written): FETCH_SIZE x{f_factor:.3f}, WRITE_SIZE x{w_factor:.3f}")
+    print("| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read bytes | HBM written bytes |")
+    print("|---|---|---|---|---|---|")
+    table = {}
+    for k in sorted(set(fetch) | set(write)):
+        rd = fetch.get(k, 0.0) * 1024.0 * f_factor
+        wr = write.get(k, 0.0) * 1024.0 * w_factor
+        print(f"| {k} | {n_fetch.get(k, 0)}/{n_write.get(k, 0)} | {fetch.get(k, 0):.6g} | {write.get(k, 0):.6g} "
+              f"| {rd:.6g} | {wr:.6g} |")
+        table[k] = {"read_bytes": rd, "write_bytes": wr, "source_sha256": source_hash(k)}
+    if out_path:
+        with open(out_path, "w") as fh:
+            json.dump({"fetch_factor": f_factor, "write_factor": w_factor, "kernels": table}, fh, indent=1)
+
+
 if __name__ == "__main__":
-    mode, dbs = sys.argv[1], sys.argv[2:]
-    {"trace": trace, "pmc": pmc}[mode](dbs)
+    mode, rest = sys.argv[1], sys.argv[2:]
+    {"trace": trace, "pmc": pmc, "traffic": traffic}[mode](rest)
