@@ -29,6 +29,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s at T=4096 + µs/layer at T=32; % of MFMA/HBM peak"
+# Kernels the roofline entries describe (names as the profiler reports them).
+UP_PREFILL_KERNEL = "moe::grouped_gemm_prefill_kernel<true, 1>"
+UP_DECODE_KERNEL = "moe::grouped_gemm_decode_kernel<true, 8>"
 
 
 def _log(msg):
@@ -104,7 +107,8 @@ def measured_traffic(workload, kernel):
         return None
     with open(path) as fh:
         rec = json.load(fh)["kernels"].get(kernel)
-    if rec is None or rec["source_sha256"] != rocprof_summary.source_hash(kernel):
+    current = rocprof_summary.source_hash(kernel)
+    if rec is None or current is None or rec["source_sha256"] != current:
         return None
     return rec["read_bytes"] + rec["write_bytes"]
 
@@ -191,8 +195,10 @@ def main():
             "stage_ms": stages,
             "roofline": {"kernel": "grouped_gemm_prefill_kernel<SWIGLU=true> (up projection + SwiGLU)",
                          "bound": "mfma", "achieved": up_flops / up_s / 1e12, "peak": A.PEAK_BF16_FLOPS / 1e12,
-                         "unit": "TFLOP/s", "frac": up_flops / up_s / A.PEAK_BF16_FLOPS, "traffic": None,
-                         "algorithmic_per_launch": up_flops},
+                         "unit": "TFLOP/s", "frac": up_flops / up_s / A.PEAK_BF16_FLOPS,
+                         "traffic": measured_traffic("prefill", UP_PREFILL_KERNEL),
+                         "algorithmic_per_launch": up_flops,
+                         "algorithmic_bytes_per_launch": A.up_bytes(T, d, f, k, sum(1 for c in layer.counts.tolist() if c > 0))},
         })
         if not args.no_cpu_baseline:
             _log("cpu baseline: running the fp64 oracle on a token sample")
@@ -226,7 +232,8 @@ def main():
                "roofline": {"kernel": "grouped_gemm_decode_kernel<SWIGLU=true> (up projection + SwiGLU)",
                             "bound": "hbm", "achieved": up_bytes / (stages["up"] * 1e-3) / 1e9,
                             "peak": A.PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
-                            "frac": up_bytes / (stages["up"] * 1e-3) / A.PEAK_HBM_BYTES, "traffic": None,
+                            "frac": up_bytes / (stages["up"] * 1e-3) / A.PEAK_HBM_BYTES,
+                            "traffic": measured_traffic("decode", UP_DECODE_KERNEL),
                             "algorithmic_per_launch": up_bytes}}
         result["decode"] = dec
         if "value" not in result:

@@ -23,8 +23,9 @@ from collections import defaultdict
 
 
 def short(name: str) -> str:
-    name = re.sub(r"\(.*", "", name)
-    return name.replace("void ", "")
+    """Kernel name without return type, anonymous namespace and arguments."""
+    name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+    return re.sub(r"\(.*", "", name)
 
 
 def trace(dbs):
@@ -83,8 +84,9 @@ def source_hash(kernel: str):
     import os
 
     csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    bare = kernel.split("::")[-1] if "<" not in kernel else kernel[: kernel.index("<")].split("::")[-1] + kernel[kernel.index("<"):]
     for prefix, files in KERNEL_SOURCES.items():
-        if kernel.startswith(prefix):
+        if bare.startswith(prefix):
             h = hashlib.sha256()
             for fn in files:
                 with open(os.path.join(csrc, fn), "rb") as fh:
