@@ -49,6 +49,7 @@ constexpr int kBK = 64;        // k depth of one stage (128 B per row)
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kXcds = 8;
 constexpr int kGroupN = 4;     // n-tiles per group in the tile order
+constexpr int kThinRows = 32;  // m-tiles with at most this many rows take the thin path
 constexpr int kSlotElems = kBM * kBK;  // one 32 KiB slot (kBM == kBN)
 
 #define GLOBAL_PTR(p) ((const __attribute__((address_space(1))) void*)(p))
@@ -213,6 +214,10 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
   const int k_part = K / SPLITK;
   const int KT = k_part / kBK;  // >= 2 (the host guarantees it)
 
+  // Slot s of an XCD takes every slots-th tile of the XCD's range, so the
+  // workgroups of an XCD run neighbouring tiles side by side.  (Claiming
+  // tiles dynamically from a counter measured slower: it lets the
+  // workgroups drift apart and share less in L2.)
   for (int L = beg + slot; L < end; L += slots) {
     int e, mt, nt;
     const int ks = L % SPLITK;
@@ -250,6 +255,117 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
     uint32_t b_off[2];
     b_off[0] = (static_cast<uint32_t>(ld_row) * static_cast<uint32_t>(K) + lc_even) * 2u;
     b_off[1] = (static_cast<uint32_t>(ld_row) * static_cast<uint32_t>(K) + lc_odd) * 2u;
+
+    if (rows - m0 <= kThinRows) {
+      // Thin tile: an expert's last m-tile with at most 32 rows.  The four
+      // waves split the 256 weight rows instead (32 rows x 64 weight rows
+      // each: 2 x 4 MFMA tiles), so the tile costs its loads, not 256 rows of
+      // MFMAs.  Same slots and B loads as below; only 32 A rows are loaded,
+      // wave w filling LDS rows 8w..8w+7.  Loads run one stage ahead for A
+      // and two for B; each stage waits for its own loads, then a barrier.
+      uint32_t ta_off;
+      {
+        const int lc = (wave & 1) ? lc_odd : lc_even;  // swizzle of LDS row 8*wave + ld_row
+        if constexpr (SWIGLU)
+          ta_off = ((static_cast<uint32_t>(gather[row_begin + min(m0 + wave * 8 + ld_row, rows - 1)]) / kTopK) *
+                        static_cast<uint32_t>(K) + lc) * 2u;
+        else
+          ta_off = (static_cast<uint32_t>(min(wave * 8 + ld_row, rows - 1 - m0)) * static_cast<uint32_t>(K) + lc) * 2u;
+      }
+#define LOAD_A_THIN(KT_)                                                                                 \
+  __builtin_amdgcn_global_load_lds(                                                                      \
+      GLOBAL_PTR(reinterpret_cast<const char*>(a_base + static_cast<int64_t>(KT_) * kBK) + ta_off),        \
+      LDS_PTR(&ring[(KT_) & 1][(wave * 8) * kBK]), 16, 0, 0);
+      // this wave's B-tile rows: SwiGLU = 32 gate rows and the matching 32 up rows
+      int tb_row[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (SWIGLU)
+          tb_row[j] = (wave >> 1) * 128 + (j >= 2 ? 64 : 0) + (wave & 1) * 32 + (j & 1) * 16 + l16;
+        else
+          tb_row[j] = wave * 64 + j * 16 + l16;
+      }
+      f32x4 tacc[2][4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { LOAD_B(0, j, 0); }
+      LOAD_A_THIN(0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { LOAD_B(1, j, 1); }
+      int bs = 0;
+      for (int kt = 0; kt < KT; ++kt) {
+        // Issue order: B(0) A(0) B(1) | A(1) B(2) | A(2) B(3) ...: after
+        // stage kt's last load only B(kt+1) was issued.
+        if (kt + 1 < KT)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        lds_barrier();  // stage kt landed for all waves; stage kt-1 fully read
+        const int bs1 = bs == 2 ? 0 : bs + 1;
+        const int bs2 = bs1 == 2 ? 0 : bs1 + 1;
+        if (kt + 1 < KT) { LOAD_A_THIN(kt + 1); }
+        if (kt + 2 < KT) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) { LOAD_B(kt + 2, j, bs2); }
+        }
+        bf16x8 ta[2][2], tb[2][4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            tb[hh][j] = *reinterpret_cast<const bf16x8*>(&ring[2 + bs][lds_off(tb_row[j], hh * 4 + lg)]);
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+            ta[hh][i] = *reinterpret_cast<const bf16x8*>(&ring[kt & 1][lds_off(i * 16 + l16, hh * 4 + lg)]);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              tacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tb[hh][j], ta[hh][i], tacc[i][j], 0, 0, 0);
+        bs = bs1;
+      }
+#undef LOAD_A_THIN
+      // every wave's reads of the last stage are done before the next tile refills the slots
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & lgkm0_mask());
+      lds_barrier();
+      // Epilogue: tacc[i][j][q] is row m0 + i*16 + l16, B-tile row tb_row[j]'s
+      // block at 4*lg + q.
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int m = m0 + i * 16 + l16;
+        if (m >= rows) continue;
+        const int64_t orow = row_begin + m;
+        if constexpr (SWIGLU) {
+          bf16_t* C = static_cast<bf16_t*>(Cout);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int n = n0 + (wave >> 1) * 64 + (wave & 1) * 32 + j * 16 + 4 * lg;
+            const f32x4 g = tacc[i][j];
+            const f32x4 u = tacc[i][j + 2];
+            uint2 p;
+            p.x = pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
+            p.y = pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
+            *reinterpret_cast<uint2*>(C + orow * N + n) = p;
+          }
+        } else {
+          float* C = static_cast<float*>(Cout) + ks * split_stride;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = n0 + wave * 64 + j * 16 + 4 * lg;
+            if (n >= N) continue;
+            const f32x4 v = tacc[i][j];
+            *reinterpret_cast<float4*>(C + orow * N + n) = make_float4(v[0], v[1], v[2], v[3]);
+          }
+        }
+      }
+      continue;
+    }
 
     f32x4 acc[8][8];
 #pragma unroll

@@ -99,10 +99,13 @@ def test_fp32_shapes(T, d, f):
     run_and_check(_layer(T, d, f, dtype="f32", seed=T))
 
 
-@pytest.mark.parametrize("T,d,f", [(1200, 512, 1024), (1500, 256, 512), (777, 384, 640), (300, 256, 384)])
+@pytest.mark.parametrize("T,d,f", [(1200, 512, 1024), (1500, 256, 512), (777, 384, 640), (300, 256, 384),
+                                   (1030, 256, 512), (2100, 256, 256)])
 def test_bf16_prefill_kernels(T, d, f):
     # several m-tiles per expert with ragged tails; d=384 leaves a half-empty
-    # n-tile in the down projection; f=640 an odd number of k-steps
+    # n-tile in the down projection; f=640 an odd number of k-stages; T=1030
+    # leaves last m-tiles of a few rows (the thin-tile path); f=256 gives the
+    # split down projection the minimum of two k-stages per half
     run_and_check(_layer(T, d, f, seed=T), variant=moe.VARIANT_PREFILL)
 
 
@@ -250,6 +253,40 @@ def test_staged_path_under_the_oracle_assignment(variant):
     assert np.abs(y_rows.cpu().numpy() - yr_ref).max() <= 1e-4 * np.abs(yr_ref).max()
     yg = O._f64(y.cpu())
     assert np.abs(yg - ref["y"]).max() <= _tol("bf16", ref["y"])
+
+
+def test_prefill_crafted_expert_sizes():
+    """Per-expert row counts chosen to hit every m-tile shape of the prefill
+    GEMMs: 1, 32 (thin path), 33 (full path, mostly padding), 256 (exactly
+    one tile), 289 (full tile + 33), 0 (empty expert), 520 (two tiles + a
+    thin tail of 8), 269 (full + thin 13).  h and y_rows are checked element
+    by element against the oracle's SwiGLU and down projection."""
+    counts = [1, 32, 33, 256, 289, 0, 520, 269]
+    T, d, f = sum(counts) // 2, 256, 512
+    layer = _layer(T, d, f, seed=21)
+    rng = np.random.default_rng(21)
+    ids = rng.permutation(np.repeat(np.arange(8), counts)).astype(np.int32).reshape(T, 2)
+    idx = torch.from_numpy(ids).cuda()
+    offs, sorted_slots, slot_rows = moe.permute(idx, d, f)
+    h, y_rows = moe.grouped_swiglu(layer["x"], offs, sorted_slots, layer["w1"], layer["w3"], layer["w2"],
+                                   variant=moe.VARIANT_PREFILL)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(np.diff(offs.cpu().numpy()), counts)
+    xc, w1c, w3c, w2c = (_cpu(layer[k]) for k in ("x", "w1", "w3", "w2"))
+    _, es, _ = O.expert_permutation(ids, 8)
+    tok = es // 2
+    exp_of_row = ids.reshape(-1)[es]
+    hg = O._f64(h.cpu())
+    h_ref = np.zeros((T * 2, f))
+    yr_ref = np.zeros((T * 2, d))
+    for e in range(8):
+        rows = np.nonzero(exp_of_row == e)[0]
+        if rows.size == 0:
+            continue
+        h_ref[rows] = O.swiglu_hidden(xc[tok[rows]], w1c[e], w3c[e])
+        yr_ref[rows] = hg[rows] @ O._f64(w2c[e]).T
+    assert np.abs(hg - h_ref).max() <= 2e-2 * np.abs(h_ref).max() + 2e-3
+    assert np.abs(y_rows.cpu().numpy() - yr_ref).max() <= 1e-4 * np.abs(yr_ref).max()
 
 
 def test_rmsnorm_residual():
