@@ -103,7 +103,8 @@ moe_status run_up(const moe_dims* dims, const void* x, const int32_t* offs, cons
   const bf16_t* w1b = static_cast<const bf16_t*>(w1);
   const bf16_t* w3b = static_cast<const bf16_t*>(w3);
   bf16_t* hb = static_cast<bf16_t*>(h);
-  if (use_decode(dims)) return hip_status(moe::launch_up_decode(xb, offs, sorted, w1b, w3b, hb, dims->d, dims->f, s));
+  if (use_decode(dims))
+    return hip_status(moe::launch_up_decode(xb, offs, sorted, w1b, w3b, hb, dims->T, dims->d, dims->f, s));
   int n_cu = 0;
   const moe_status st = cu_count(&n_cu);
   if (st != MOE_OK) return st;
@@ -117,7 +118,8 @@ moe_status run_down(const moe_dims* dims, const void* h, const int32_t* offs, co
                                            dims->T * dims->k, dims->d, dims->f, s));
   const bf16_t* hb = static_cast<const bf16_t*>(h);
   const bf16_t* w2b = static_cast<const bf16_t*>(w2);
-  if (use_decode(dims)) return hip_status(moe::launch_down_decode(hb, offs, w2b, y_rows, dims->d, dims->f, s));
+  if (use_decode(dims))
+    return hip_status(moe::launch_down_decode(hb, offs, w2b, y_rows, dims->T, dims->d, dims->f, 1, 0, s));
   int n_cu = 0;
   const moe_status st = cu_count(&n_cu);
   if (st != MOE_OK) return st;
@@ -268,12 +270,19 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
                                               expert_counts_out, s));
     if (st != MOE_OK) return st;
     if (dims->dtype == MOE_BF16 && use_decode(dims)) {
+      // Decode: up projection, down projection with its reduction split in
+      // two (partials in y_rows and y_rows2), combine adding both in order.
       st = run_up(dims, x, offs, sorted, w1, w3, h, s);
       if (st != MOE_OK) return st;
-      return hip_status(moe::launch_down_combine_decode(static_cast<const bf16_t*>(h), offs,
-                                                        static_cast<const bf16_t*>(w2), idx, rows, w,
-                                                        static_cast<bf16_t*>(y), static_cast<int>(dims->T), dims->d,
-                                                        dims->f, s));
+      float* y_rows2 = reinterpret_cast<float*>(ws + plan.y_rows2);
+      st = hip_status(moe::launch_down_decode(static_cast<const bf16_t*>(h), offs, static_cast<const bf16_t*>(w2),
+                                              y_rows, dims->T, dims->d, dims->f, 2, y_rows2 - y_rows, s));
+      if (st != MOE_OK) return st;
+      int n_cu = 0;
+      st = cu_count(&n_cu);
+      if (st != MOE_OK) return st;
+      return hip_status(moe::launch_combine(dims->dtype, y_rows, dims->f % 256 == 0 ? y_rows2 : nullptr, rows, w, y,
+                                            dims->T, dims->d, n_cu, s));
     }
   } else {
     st = run_router(dims, x, w_gate, logit_bias, idx, w, nullptr, s);

@@ -8,31 +8,41 @@
 // With ~8 rows per expert the layer is bound by streaming the touched
 // experts' weights from HBM once ("Mixtral of Experts", azimuth.plus,
 // paragraph on active versus stored parameters: memory scales with the total
-// parameters).  Each wavefront owns 16 weight rows (output features) of one
-// expert over the whole reduction and streams them straight from HBM into
-// registers as the MFMA src0 operand (16 rows x 32 k per
-// v_mfma_f32_16x16x32_bf16); the expert's tokens, padded to groups of 16,
-// are the src1 operand, read from L2.  Weights are never staged in LDS: no
-// element is used twice by the same wave.  KU k-steps of weight loads are
-// issued back to back to keep enough bytes in flight per CU.  Up to 4 token
-// groups (64 rows) share one pass over the weights; more rows take more
-// passes.
+// parameters).  Each wavefront owns 32 weight rows of one expert (up: 16 gate
+// rows and the same 16 up rows; down: two blocks of 16) over its share of the
+// reduction and streams them straight from HBM into registers as the MFMA
+// src0 operand (16 rows x 32 k per v_mfma_f32_16x16x32_bf16); the expert's
+// tokens, padded to groups of 16, are the src1 operand, read from L2 and
+// shared by both row blocks.  Weights are never staged in LDS: no element is
+// used twice by the same wave.  KU k-steps of weight loads are issued back to
+// back to keep bytes in flight.  At most MAXG token groups (16 rows each)
+// share one pass over the weights; an expert with more rows takes more
+// passes.  Up projection: MAXG = 2 when T <= 32 (no expert can then hold
+// more than 32 rows of a top-2 routing); the smaller register footprint
+// measured 10% faster than MAXG = 4.  The down
+// projection splits the reduction over S waves (S = 2: twice the waves in
+// flight) writing separate partial sums; the combine adds them in order.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace moe {
+namespace {
 
 constexpr int kDThreads = 256;
-constexpr int kDMaxGroups = 4;
+constexpr int kDWaves = kDThreads / kWave;
 
-template <bool SWIGLU, int KU>
-__global__ void __launch_bounds__(kDThreads) grouped_gemm_decode_kernel(
-    const bf16_t* __restrict__ A, const int32_t* __restrict__ gather, int k_div, const int32_t* __restrict__ offs,
-    const bf16_t* __restrict__ B0, const bf16_t* __restrict__ B1, void* __restrict__ Cout, int N, int K) {
+// Up projection: wave = (expert, 16-row block of w1/w3).
+template <int KU, int MAXG>
+__global__ void __launch_bounds__(kDThreads) up_decode_kernel(const bf16_t* __restrict__ x,
+                                                                const int32_t* __restrict__ sorted_slots,
+                                                                const int32_t* __restrict__ offs,
+                                                                const bf16_t* __restrict__ w1,
+                                                                const bf16_t* __restrict__ w3, bf16_t* __restrict__ h,
+                                                                int f, int d) {
   const int lane = threadIdx.x % kWave;
   const int l16 = lane % 16, lg = lane / 16;
-  const int fgroups = N / 16;
-  const int wid = blockIdx.x * (kDThreads / kWave) + threadIdx.x / kWave;
+  const int fgroups = f / 16;
+  const int wid = blockIdx.x * kDWaves + threadIdx.x / kWave;
   const int e = wid / fgroups;
   if (e >= kExperts) return;
   const int fg = wid - e * fgroups;
@@ -41,182 +51,160 @@ __global__ void __launch_bounds__(kDThreads) grouped_gemm_decode_kernel(
   if (rows <= 0) return;
 
   const int n_row = fg * 16 + l16;  // weight row this lane streams
-  const bf16_t* w0 = B0 + (static_cast<int64_t>(e) * N + n_row) * K + lg * 8;
-  const bf16_t* w1 = SWIGLU ? B1 + (static_cast<int64_t>(e) * N + n_row) * K + lg * 8 : nullptr;
+  const bf16_t* pg = w1 + (static_cast<int64_t>(e) * f + n_row) * d + lg * 8;
+  const bf16_t* pu = w3 + (static_cast<int64_t>(e) * f + n_row) * d + lg * 8;
 
-  for (int base = 0; base < rows; base += 16 * kDMaxGroups) {
-    const int ng = min(kDMaxGroups, (rows - base + 15) / 16);
-    const bf16_t* a_ptr[kDMaxGroups];
+  for (int base = 0; base < rows; base += 16 * MAXG) {
+    const int ng = min(MAXG, (rows - base + 15) / 16);
+    const bf16_t* a_ptr[MAXG];
 #pragma unroll
-    for (int g = 0; g < kDMaxGroups; ++g) {
+    for (int g = 0; g < MAXG; ++g) {
       const int m = min(base + g * 16 + l16, rows - 1);  // clamped rows are computed, never stored
-      const int64_t gr = row_begin + m;
-      const int64_t arow = gather ? static_cast<int64_t>(gather[gr] / k_div) : gr;
-      a_ptr[g] = A + arow * K + lg * 8;
+      a_ptr[g] = x + static_cast<int64_t>(sorted_slots[row_begin + m] / kTopK) * d + lg * 8;
     }
-    f32x4 acc0[kDMaxGroups], acc1[kDMaxGroups];
+    f32x4 acc_g[MAXG], acc_u[MAXG];
 #pragma unroll
-    for (int g = 0; g < kDMaxGroups; ++g) {
-      acc0[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-      acc1[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < MAXG; ++g) {
+      acc_g[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc_u[g] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-
-    for (int k0 = 0; k0 < K; k0 += 32 * KU) {
-      bf16x8 wa[KU], wb[KU];
+    for (int k0 = 0; k0 < d; k0 += 32 * KU) {
+      bf16x8 wg[KU], wu[KU];
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
-        wa[u] = *reinterpret_cast<const bf16x8*>(w0 + k0 + u * 32);
-        if constexpr (SWIGLU) wb[u] = *reinterpret_cast<const bf16x8*>(w1 + k0 + u * 32);
+        wg[u] = *reinterpret_cast<const bf16x8*>(pg + k0 + u * 32);
+        wu[u] = *reinterpret_cast<const bf16x8*>(pu + k0 + u * 32);
       }
 #pragma unroll
-      for (int g = 0; g < kDMaxGroups; ++g) {
+      for (int g = 0; g < MAXG; ++g) {
         if (g < ng) {
 #pragma unroll
           for (int u = 0; u < KU; ++u) {
             const bf16x8 xa = *reinterpret_cast<const bf16x8*>(a_ptr[g] + k0 + u * 32);
-            acc0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[u], xa, acc0[g], 0, 0, 0);
-            if constexpr (SWIGLU) acc1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[u], xa, acc1[g], 0, 0, 0);
+            acc_g[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wg[u], xa, acc_g[g], 0, 0, 0);
+            acc_u[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wu[u], xa, acc_u[g], 0, 0, 0);
           }
         }
       }
     }
-
-    // acc[g][q]: token row m = base + g*16 + l16, feature n = fg*16 + 4*lg + q.
+    // acc[g][q]: row base + g*16 + l16, feature fg*16 + 4*lg + q.
     const int n = fg * 16 + 4 * lg;
 #pragma unroll
-    for (int g = 0; g < kDMaxGroups; ++g) {
+    for (int g = 0; g < MAXG; ++g) {
       const int m = base + g * 16 + l16;
       if (g >= ng || m >= rows) continue;
-      const int64_t orow = row_begin + m;
-      if constexpr (SWIGLU) {
-        const f32x4 a = acc0[g], b = acc1[g];
-        uint2 p;
-        p.x = pack_bf16x2(silu(a[0]) * b[0], silu(a[1]) * b[1]);
-        p.y = pack_bf16x2(silu(a[2]) * b[2], silu(a[3]) * b[3]);
-        *reinterpret_cast<uint2*>(static_cast<bf16_t*>(Cout) + orow * N + n) = p;
-      } else {
-        const f32x4 a = acc0[g];
-        *reinterpret_cast<float4*>(static_cast<float*>(Cout) + orow * N + n) = make_float4(a[0], a[1], a[2], a[3]);
-      }
+      const f32x4 a = acc_g[g], b = acc_u[g];
+      uint2 p;
+      p.x = pack_bf16x2(silu(a[0]) * b[0], silu(a[1]) * b[1]);
+      p.y = pack_bf16x2(silu(a[2]) * b[2], silu(a[3]) * b[3]);
+      *reinterpret_cast<uint2*>(h + static_cast<int64_t>(row_begin + m) * f + n) = p;
     }
   }
 }
 
-// Down projection fused with the gate-weighted combine, for batches of at
-// most 64 tokens (so no expert has more than 64 rows).  Workgroup b owns
-// output features n0 = 16 b .. n0+15 of every expert: wave w streams w2 rows
-// n0.. of expert w/2 over half w%2 of the reduction (f/2 each) with the same
-// MFMA scheme as above, parks its partial sums in LDS, and after a barrier the
-// workgroup forms y[t, n0+c] = g_t0 (P0 + P1)[r0] + g_t1 (P0 + P1)[r1] for
-// every token in a fixed order (deterministic), rounded once to bf16.
-constexpr int kDcThreads = 1024;   // 16 waves: 8 experts x 2 halves of f
-constexpr int kDcMaxRows = 64;
-
-template <int KU>
-__global__ void __launch_bounds__(kDcThreads) down_combine_decode_kernel(
-    const bf16_t* __restrict__ H, const int32_t* __restrict__ offs, const bf16_t* __restrict__ w2,
-    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ slot_rows, const float* __restrict__ topk_w,
-    bf16_t* __restrict__ y, int T, int d, int f) {
-  __shared__ float part[kDcThreads / kWave][kDcMaxRows][16];
+// Down projection: wave = (expert, 32-row block of w2, part s of the
+// reduction); part s writes y_rows + s * split_stride.
+template <int KU, int MAXG, int S>
+__global__ void __launch_bounds__(kDThreads) down_decode_kernel(const bf16_t* __restrict__ h,
+                                                                  const int32_t* __restrict__ offs,
+                                                                  const bf16_t* __restrict__ w2,
+                                                                  float* __restrict__ y_rows, int d, int f,
+                                                                  int64_t split_stride) {
   const int lane = threadIdx.x % kWave;
-  const int wave = threadIdx.x / kWave;
   const int l16 = lane % 16, lg = lane / 16;
-  const int e = wave / 2, half = wave % 2;
-  const int n0 = blockIdx.x * 16;
+  const int nrb = d / 32;
+  const int wid = blockIdx.x * kDWaves + threadIdx.x / kWave;
+  const int e = wid / (nrb * S);
+  if (e >= kExperts) return;
+  const int rb = (wid / S) % nrb, s = wid % S;
   const int row_begin = offs[e];
-  const int rows = offs[e + 1] - row_begin;  // <= kDcMaxRows (T <= 64)
-  const int kh = f / 2;
+  const int rows = offs[e + 1] - row_begin;
+  if (rows <= 0) return;
+  const int kp = f / S, k_beg = s * kp;
 
-  if (rows > 0) {
-    const bf16_t* wrow = w2 + (static_cast<int64_t>(e) * d + n0 + l16) * f + half * kh + lg * 8;
-    const int ng = (rows + 15) / 16;
-    const bf16_t* a_ptr[kDMaxGroups];
+  const bf16_t* p0 = w2 + (static_cast<int64_t>(e) * d + rb * 32 + l16) * f + k_beg + lg * 8;
+  const bf16_t* p1 = p0 + static_cast<int64_t>(16) * f;
+  float* out = y_rows + s * split_stride;
+
+  for (int base = 0; base < rows; base += 16 * MAXG) {
+    const int ng = min(MAXG, (rows - base + 15) / 16);
+    const bf16_t* a_ptr[MAXG];
 #pragma unroll
-    for (int g = 0; g < kDMaxGroups; ++g) {
-      const int m = min(g * 16 + l16, rows - 1);  // clamped rows are computed, never used
-      a_ptr[g] = H + static_cast<int64_t>(row_begin + m) * f + half * kh + lg * 8;
+    for (int g = 0; g < MAXG; ++g)
+      a_ptr[g] = h + static_cast<int64_t>(row_begin + min(base + g * 16 + l16, rows - 1)) * f + k_beg + lg * 8;
+    f32x4 acc0[MAXG], acc1[MAXG];
+#pragma unroll
+    for (int g = 0; g < MAXG; ++g) {
+      acc0[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc1[g] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    f32x4 acc[kDMaxGroups];
+    for (int k0 = 0; k0 < kp; k0 += 32 * KU) {
+      bf16x8 b0[KU], b1[KU];
 #pragma unroll
-    for (int g = 0; g < kDMaxGroups; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < kh; k0 += 32 * KU) {
-      bf16x8 wa[KU];
+      for (int u = 0; u < KU; ++u) {
+        b0[u] = *reinterpret_cast<const bf16x8*>(p0 + k0 + u * 32);
+        b1[u] = *reinterpret_cast<const bf16x8*>(p1 + k0 + u * 32);
+      }
 #pragma unroll
-      for (int u = 0; u < KU; ++u) wa[u] = *reinterpret_cast<const bf16x8*>(wrow + k0 + u * 32);
-#pragma unroll
-      for (int g = 0; g < kDMaxGroups; ++g) {
+      for (int g = 0; g < MAXG; ++g) {
         if (g < ng) {
 #pragma unroll
           for (int u = 0; u < KU; ++u) {
             const bf16x8 ha = *reinterpret_cast<const bf16x8*>(a_ptr[g] + k0 + u * 32);
-            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[u], ha, acc[g], 0, 0, 0);
+            acc0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b0[u], ha, acc0[g], 0, 0, 0);
+            acc1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b1[u], ha, acc1[g], 0, 0, 0);
           }
         }
       }
     }
-    // acc[g][q]: expert row g*16 + l16, feature 4*lg + q
+    // acc0[g][q]: row base + g*16 + l16, feature rb*32 + 4*lg + q (acc1: + 16).
+    const int n = rb * 32 + 4 * lg;
 #pragma unroll
-    for (int g = 0; g < kDMaxGroups; ++g) {
-      const int m = g * 16 + l16;
-      if (g < ng && m < rows) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) part[wave][m][4 * lg + q] = acc[g][q];
-      }
+    for (int g = 0; g < MAXG; ++g) {
+      const int m = base + g * 16 + l16;
+      if (g >= ng || m >= rows) continue;
+      float* o = out + static_cast<int64_t>(row_begin + m) * d + n;
+      *reinterpret_cast<float4*>(o) = make_float4(acc0[g][0], acc0[g][1], acc0[g][2], acc0[g][3]);
+      *reinterpret_cast<float4*>(o + 16) = make_float4(acc1[g][0], acc1[g][1], acc1[g][2], acc1[g][3]);
     }
-  }
-  __syncthreads();
-
-  // Combine: thread (t, c) for token t < T <= 64 and feature column c < 16.
-  const int t = threadIdx.x / 16, c = threadIdx.x % 16;
-  if (t < T) {
-    float o = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kTopK; ++j) {
-      const int ej = topk_idx[kTopK * t + j];
-      const int r = slot_rows[kTopK * t + j] - offs[ej];
-      const float v = part[2 * ej][r][c] + part[2 * ej + 1][r][c];
-      o = (j == 0) ? topk_w[kTopK * t] * v : o + topk_w[kTopK * t + j] * v;
-    }
-    y[static_cast<int64_t>(t) * d + n0 + c] = f32_to_bf16(o);
   }
 }
 
-template <bool SWIGLU, int KU>
-static hipError_t launch_one_decode(const bf16_t* A, const int32_t* gather, int k_div, const int32_t* offs,
-                                    const bf16_t* B0, const bf16_t* B1, void* C, int N, int K, hipStream_t s) {
-  const int waves = kExperts * (N / 16);
-  const int per_block = kDThreads / kWave;
-  const int blocks = (waves + per_block - 1) / per_block;
-  hipLaunchKernelGGL((grouped_gemm_decode_kernel<SWIGLU, KU>), dim3(blocks), dim3(kDThreads), 0, s, A, gather, k_div,
-                     offs, B0, B1, C, N, K);
+template <int KU, int MAXG>
+hipError_t launch_up(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
+                     const bf16_t* w3, bf16_t* h, int d, int f, hipStream_t s) {
+  const int waves = kExperts * (f / 16);
+  hipLaunchKernelGGL((up_decode_kernel<KU, MAXG>), dim3((waves + kDWaves - 1) / kDWaves), dim3(kDThreads), 0, s, x,
+                     sorted_slots, offs, w1, w3, h, f, d);
   return hipGetLastError();
 }
 
+template <int KU, int MAXG, int S>
+hipError_t launch_down(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,
+                       int64_t split_stride, hipStream_t s) {
+  const int waves = kExperts * (d / 32) * S;
+  hipLaunchKernelGGL((down_decode_kernel<KU, MAXG, S>), dim3((waves + kDWaves - 1) / kDWaves), dim3(kDThreads), 0, s,
+                     h, offs, w2, y_rows, d, f, split_stride);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// KU = 4 needs the reduction (d, or f / S) to be a multiple of 128: d and f
+// are multiples of 128 (checked at the boundary), and S = 2 is used only when
+// f is a multiple of 256.
 hipError_t launch_up_decode(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
-                            const bf16_t* w3, bf16_t* h, int d, int f, hipStream_t s) {
-  // K = d; KU * 32 must divide it (d % 128 == 0, so KU = 4 always works).
-  if (d % 256 == 0) return launch_one_decode<true, 8>(x, sorted_slots, kTopK, offs, w1, w3, h, f, d, s);
-  return launch_one_decode<true, 4>(x, sorted_slots, kTopK, offs, w1, w3, h, f, d, s);
+                            const bf16_t* w3, bf16_t* h, int64_t T, int d, int f, hipStream_t s) {
+  if (T <= 32) return launch_up<4, 2>(x, offs, sorted_slots, w1, w3, h, d, f, s);
+  return launch_up<4, 4>(x, offs, sorted_slots, w1, w3, h, d, f, s);
 }
 
-hipError_t launch_down_combine_decode(const bf16_t* h, const int32_t* offs, const bf16_t* w2, const int32_t* topk_idx,
-                                      const int32_t* slot_rows, const float* topk_w, bf16_t* y, int T, int d, int f,
-                                      hipStream_t s) {
-  // each wave covers f/2 in steps of 32*KU
-  const int kh = f / 2;
-  if (kh % 512 == 0)
-    hipLaunchKernelGGL(down_combine_decode_kernel<16>, dim3(d / 16), dim3(kDcThreads), 0, s, h, offs, w2, topk_idx,
-                       slot_rows, topk_w, y, T, d, f);
-  else
-    hipLaunchKernelGGL(down_combine_decode_kernel<2>, dim3(d / 16), dim3(kDcThreads), 0, s, h, offs, w2, topk_idx,
-                       slot_rows, topk_w, y, T, d, f);
-  return hipGetLastError();
-}
-
-hipError_t launch_down_decode(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,
-                              hipStream_t s) {
-  if (f % 512 == 0) return launch_one_decode<false, 16>(h, nullptr, 1, offs, w2, nullptr, y_rows, d, f, s);
-  return launch_one_decode<false, 4>(h, nullptr, 1, offs, w2, nullptr, y_rows, d, f, s);
+hipError_t launch_down_decode(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int64_t T, int d,
+                              int f, int split, int64_t split_stride, hipStream_t s) {
+  // (MAXG = 4 measured faster here than 2, whatever T.)
+  (void)T;
+  if (split == 2 && f % 256 == 0) return launch_down<4, 4, 2>(h, offs, w2, y_rows, d, f, split_stride, s);
+  return launch_down<4, 4, 1>(h, offs, w2, y_rows, d, f, 0, s);
 }
 
 }  // namespace moe

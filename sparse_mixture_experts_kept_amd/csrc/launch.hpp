@@ -34,19 +34,19 @@ hipError_t launch_up_prefill(const bf16_t* x, const int32_t* offs, const int32_t
 hipError_t launch_down_prefill(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,
                                int n_cu, int split, int64_t split_stride, hipStream_t s);
 
+// Decode (few rows per expert).  T bounds the rows per expert of a top-2
+// routing (any routing stays correct, more rows only take more passes).
 hipError_t launch_up_decode(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
-                            const bf16_t* w3, bf16_t* h, int d, int f, hipStream_t s);
-hipError_t launch_down_decode(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,
-                              hipStream_t s);
+                            const bf16_t* w3, bf16_t* h, int64_t T, int d, int f, hipStream_t s);
+// split == 2 (f a multiple of 256): two partial sums, the second at
+// y_rows + split_stride; otherwise one full sum in y_rows.
+hipError_t launch_down_decode(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int64_t T, int d,
+                              int f, int split, int64_t split_stride, hipStream_t s);
 
-// Small batches (T <= 64): routing + permutation in one workgroup, and the
-// decode down projection fused with the combine (y written directly).
+// Small batches (T <= 64): routing + permutation in one workgroup.
 hipError_t launch_route_permute(int dtype, const void* x, const void* wg, const float* bias, int32_t* idx, float* w,
                                 int32_t T, int d, int32_t* offsets, int32_t* sorted_slots, int32_t* slot_rows,
                                 int32_t* counts_out, hipStream_t s);
-hipError_t launch_down_combine_decode(const bf16_t* h, const int32_t* offs, const bf16_t* w2, const int32_t* topk_idx,
-                                      const int32_t* slot_rows, const float* topk_w, bf16_t* y, int T, int d, int f,
-                                      hipStream_t s);
 
 // y_rows2 (optional): a second partial-sum buffer added to y_rows first.
 hipError_t launch_combine(int dtype, const float* y_rows, const float* y_rows2, const int32_t* slot_rows,

@@ -68,8 +68,8 @@ def _mean_counter(db, counter):
 # Source files each kernel family is compiled from (relative to csrc/).
 KERNEL_SOURCES = {
     "grouped_gemm_prefill_kernel": ["gemm_prefill.hip", "common.hpp"],
-    "grouped_gemm_decode_kernel": ["gemm_decode.hip", "common.hpp"],
-    "down_combine_decode_kernel": ["gemm_decode.hip", "common.hpp"],
+    "up_decode_kernel": ["gemm_decode.hip", "common.hpp"],
+    "down_decode_kernel": ["gemm_decode.hip", "common.hpp"],
     "router": ["router.hip", "permute_dev.hpp", "common.hpp"],
     "route_permute": ["router.hip", "permute_dev.hpp", "common.hpp"],
     "permute_kernel": ["permute.hip", "permute_dev.hpp", "common.hpp"],
