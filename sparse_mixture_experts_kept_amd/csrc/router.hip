@@ -278,25 +278,82 @@ hipError_t launch_router(int dtype, const void* x, const void* wg, const float* 
 
 namespace moe {
 
-// bf16 small batches: up to 4 token groups, each on 16/groups waves that
-// split d, then the permutation, all in one workgroup.
+// bf16 small batches (T <= 64): every wave takes one d-slice of all token
+// groups (up to 4 groups of 16), so one router fragment per k-step serves
+// every group and all 16 waves share the reduction whatever T is.  Partial
+// scores meet in LDS and are added in slice order; each group's pairs go to
+// global memory and to LDS, and the same workgroup then sorts the slots from
+// the LDS copy (no round trip through global memory).
 __global__ void __launch_bounds__(kPermThreads) route_permute_mfma_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const float* __restrict__ bias,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t T_tokens, int d, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_rows, int32_t* __restrict__ counts_out) {
-  __shared__ f32x4 part[kPermWaves][kWave];
+  constexpr int kGroups = 4;  // T <= 64
+  __shared__ f32x4 part[kPermWaves][kGroups][kWave];
+  __shared__ int32_t idx_s[kGroups * 16 * kTopK];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int groups = (T_tokens + 15) / 16;                  // 1..4 (T <= 64)
-  const int per_group = groups == 1 ? 16 : (groups == 2 ? 8 : 4);
-  const int slices = router_slices(d, per_group);
-  const int group = wave / per_group, slice = wave % per_group;
-  if (group < groups && slice < slices)
-    part[wave][lane] = router_scores_partial(x, wg, T_tokens, d, group, slice, slices, lane);
+  const int l16 = lane % 16, lg = lane / 16;
+  const int groups = (T_tokens + 15) / 16;
+  const int slices = router_slices(d, kPermWaves);
+  if (wave < slices) {
+    const int ks = d / slices;  // a multiple of 32
+    const bool real_row = l16 < kExperts;  // rows 8..15 of the padded router are zero
+    const bf16_t* wp = wg + static_cast<int64_t>(real_row ? l16 : 0) * d + wave * ks + lg * 8;
+    const bf16_t* xp[kGroups];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)  // clamped rows are computed, never written
+      xp[g] = x + static_cast<int64_t>(min(g * 16 + l16, T_tokens - 1)) * d + wave * ks + lg * 8;
+    f32x4 acc[kGroups];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bf16x8 zero = {};
+#pragma unroll 4
+    for (int k0 = 0; k0 < ks; k0 += 32) {
+      const bf16x8 wa = *reinterpret_cast<const bf16x8*>(wp + k0);
+#pragma unroll
+      for (int g = 0; g < kGroups; ++g) {
+        if (g < groups) {
+          const bf16x8 xa = *reinterpret_cast<const bf16x8*>(xp[g] + k0);
+          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(real_row ? wa : zero, xa, acc[g], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g)
+      if (g < groups) part[wave][g][lane] = acc[g];
+  }
   __syncthreads();
-  if (slice == 0 && group < groups)
-    router_finish_group(&part[wave], slices, group, T_tokens, bias, lane, idx_out, w_out, nullptr);
-  __syncthreads();  // the ids written above are read back by permute_block
-  permute_block(idx_out, T_tokens * kTopK, offsets, sorted_slots, slot_rows, counts_out);
+  if (wave < groups) {
+    // acc[q] of lane t (< 16): expert q of token group*16 + t; lane t+16: expert 4+q
+    const int g = wave;
+    f32x4 sum = part[0][g][lane];
+    for (int sl = 1; sl < slices; ++sl) {
+      const f32x4 v = part[sl][g][lane];
+      sum[0] += v[0]; sum[1] += v[1]; sum[2] += v[2]; sum[3] += v[3];
+    }
+    float sc[kExperts];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      sc[q] = sum[q];
+      sc[4 + q] = __shfl(sum[q], (lane % 16) + 16, kWave);
+    }
+    const int t = g * 16 + lane;
+    if (lane < 16 && t < T_tokens) {
+#pragma unroll
+      for (int e = 0; e < kExperts; ++e) sc[e] += bias ? bias[e] : 0.0f;
+      int32_t pair[kTopK];
+      float gate[kTopK];
+      select_top2(sc, pair, gate);
+      idx_out[kTopK * t] = pair[0];
+      idx_out[kTopK * t + 1] = pair[1];
+      w_out[kTopK * t] = gate[0];
+      w_out[kTopK * t + 1] = gate[1];
+      idx_s[kTopK * t] = pair[0];
+      idx_s[kTopK * t + 1] = pair[1];
+    }
+  }
+  __syncthreads();
+  permute_block(idx_s, T_tokens * kTopK, offsets, sorted_slots, slot_rows, counts_out);
 }
 
 }  // namespace moe
