@@ -71,29 +71,120 @@ __device__ __forceinline__ void lds_barrier() {
 // Element offset of (row, logical 16-byte chunk) in a [rows][64] bf16 tile.
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * kBK + ((chunk ^ ((row >> 1) & 7)) << 3); }
 
-// (expert, m-tile, n-tile) of logical tile L; false past the end.
-__device__ __forceinline__ bool decode_tile(const int32_t* offs, int L, int n_tiles_n, int* e_out, int* mt_out,
-                                            int* nt_out) {
-  int acc = 0;
+// Work units and their deal.  An expert with c rows has ceil(c / 256)
+// m-tiles; when its last one holds at most kThinRows rows and it is not the
+// only one, that tile is "thin" (cheap: see the thin path below).  Units are
+// (expert, m-tile, n-tile, k-part).  Full units are listed expert by expert,
+// each expert's in groups of kGroupN n-tiles x all its full m-tiles (x
+// SPLITK, innermost), and split into 8 equal contiguous ranges, one per XCD;
+// within an XCD, slot s takes every 32nd full unit, so every workgroup gets
+// the same number of full units.  A thin unit (expert, group, n-tile, part)
+// is anchored at the full unit (expert, group, last full m-tile, same n-tile,
+// same part), which shares its weight panel, and is dealt by the XCD that
+// owns its anchor (slots offset by half a round, so thin units and the last
+// full units of a round land on different workgroups); a workgroup runs its
+// thin units interleaved with its full units in anchor order.
+// (Everything below is recomputed from the offsets with unrolled loops: no
+// private arrays indexed at run time, which would live in scratch memory.)
+__device__ __forceinline__ void expert_shape(const int32_t* offs, int e, int* full_m, bool* thin) {
+  const int cnt = offs[e + 1] - offs[e];
+  const int mts = (cnt + kBM - 1) / kBM;
+  *thin = mts >= 2 && cnt - (mts - 1) * kBM <= kThinRows;
+  *full_m = mts - (*thin ? 1 : 0);
+}
+
+// Total full units and thin units.
+template <int SPLITK>
+__device__ __forceinline__ void unit_counts(const int32_t* offs, int n_tiles_n, int* n_full, int* n_thin) {
+  int nf = 0, nt = 0;
 #pragma unroll
   for (int e = 0; e < kExperts; ++e) {
-    const int cnt = offs[e + 1] - offs[e];
-    const int mts = (cnt + kBM - 1) / kBM;
-    const int tiles = mts * n_tiles_n;
-    if (L < acc + tiles) {
-      const int local = L - acc;
-      const int group = mts * kGroupN;
-      const int ng = local / group;
-      const int rem = local - ng * group;
-      const int gw = min(kGroupN, n_tiles_n - ng * kGroupN);
-      *e_out = e;
-      *mt_out = rem / gw;
-      *nt_out = ng * kGroupN + rem % gw;
-      return true;
-    }
-    acc += tiles;
+    int fm;
+    bool th;
+    expert_shape(offs, e, &fm, &th);
+    nf += fm * n_tiles_n * SPLITK;
+    nt += th ? n_tiles_n * SPLITK : 0;
   }
-  return false;
+  *n_full = nf;
+  *n_thin = nt;
+}
+
+// Full unit u -> (expert, m-tile, n-tile, part).
+template <int SPLITK>
+__device__ __forceinline__ void full_unit(const int32_t* offs, int n_tiles_n, int u, int* e_out, int* mt, int* nt,
+                                          int* ks) {
+  int pre = 0, e_sel = 0, pre_sel = 0, fm_sel = 0;
+#pragma unroll
+  for (int e = 0; e < kExperts; ++e) {
+    int fm;
+    bool th;
+    expert_shape(offs, e, &fm, &th);
+    const int n = fm * n_tiles_n * SPLITK;
+    if (u >= pre && u < pre + n) {
+      e_sel = e;
+      pre_sel = pre;
+      fm_sel = fm;
+    }
+    pre += n;
+  }
+  const int local = u - pre_sel;
+  const int per_group = fm_sel * kGroupN * SPLITK;  // every group but the last is full width
+  const int g = local / per_group;
+  const int rem = local - g * per_group;
+  const int gw = min(kGroupN, n_tiles_n - g * kGroupN);
+  const int r2 = rem / SPLITK;
+  *e_out = e_sel;
+  *ks = rem - r2 * SPLITK;
+  *mt = r2 / gw;
+  *nt = g * kGroupN + r2 % gw;
+}
+
+// Thin unit t -> (expert, its m-tile, n-tile, part); returns the full unit it
+// is anchored at.
+template <int SPLITK>
+__device__ __forceinline__ int thin_unit(const int32_t* offs, int n_tiles_n, int t, int* e_out, int* mt, int* nt,
+                                         int* ks) {
+  int tpre = 0, fpre = 0, e_sel = 0, tpre_sel = 0, fpre_sel = 0, fm_sel = 0;
+#pragma unroll
+  for (int e = 0; e < kExperts; ++e) {
+    int fm;
+    bool th;
+    expert_shape(offs, e, &fm, &th);
+    const int n = th ? n_tiles_n * SPLITK : 0;
+    if (t >= tpre && t < tpre + n) {
+      e_sel = e;
+      tpre_sel = tpre;
+      fpre_sel = fpre;
+      fm_sel = fm;
+    }
+    tpre += n;
+    fpre += fm * n_tiles_n * SPLITK;
+  }
+  const int local = t - tpre_sel;
+  const int g = local / (kGroupN * SPLITK);
+  const int rem = local - g * kGroupN * SPLITK;
+  const int j = rem / SPLITK;
+  const int gw = min(kGroupN, n_tiles_n - g * kGroupN);
+  *e_out = e_sel;
+  *ks = rem - j * SPLITK;
+  *mt = fm_sel;
+  *nt = g * kGroupN + j;
+  return fpre_sel + g * fm_sel * kGroupN * SPLITK + ((fm_sel - 1) * gw + j) * SPLITK + *ks;
+}
+
+// First thin unit whose anchor is at or past full unit u (anchors rise with t).
+template <int SPLITK>
+__device__ __forceinline__ int first_thin_from(const int32_t* offs, int n_tiles_n, int n_thin, int u) {
+  int lo = 0, hi = n_thin;
+  while (lo < hi) {
+    const int mid = (lo + hi) / 2;
+    int e, mt, nt, ks;
+    if (thin_unit<SPLITK>(offs, n_tiles_n, mid, &e, &mt, &nt, &ks) < u)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  return lo;
 }
 
 // ---- pieces of the main loop (macros keep the fragment arrays in registers)
@@ -189,17 +280,16 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
   constexpr int TN = SWIGLU ? kBN / 2 : kBN;
   const int n_tiles_n = (N + TN - 1) / TN;
 
-  int total = 0;
-#pragma unroll
-  for (int e = 0; e < kExperts; ++e) total += (offs[e + 1] - offs[e] + kBM - 1) / kBM;
-  total *= n_tiles_n * SPLITK;
-
+  int n_full, n_thin;
+  unit_counts<SPLITK>(offs, n_tiles_n, &n_full, &n_thin);
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int slots = gridDim.x / kXcds;
-  const int per = (total + kXcds - 1) / kXcds;
-  const int beg = xcd * per;
-  const int end = min(beg + per, total);
+  const int per = (n_full + kXcds - 1) / kXcds;
+  const int fbeg = min(xcd * per, n_full);
+  const int fend = min(fbeg + per, n_full);
+  const int tbeg = first_thin_from<SPLITK>(offs, n_tiles_n, n_thin, fbeg);
+  const int tend = first_thin_from<SPLITK>(offs, n_tiles_n, n_thin, fend);
 
   const int lane = threadIdx.x % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -214,14 +304,30 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
   const int k_part = K / SPLITK;
   const int KT = k_part / kBK;  // >= 2 (the host guarantees it)
 
-  // Slot s of an XCD takes every slots-th tile of the XCD's range, so the
-  // workgroups of an XCD run neighbouring tiles side by side.  (Claiming
-  // tiles dynamically from a counter measured slower: it lets the
-  // workgroups drift apart and share less in L2.)
-  for (int L = beg + slot; L < end; L += slots) {
-    int e, mt, nt;
-    const int ks = L % SPLITK;
-    decode_tile(offs, L / SPLITK, n_tiles_n, &e, &mt, &nt);
+  // This workgroup's full units fbeg + slot + i*slots and thin units
+  // tbeg + (slot + slots/2) % slots + i*slots, merged in anchor order.
+  int u = fbeg + slot;
+  int t = tbeg + (slot + slots / 2) % slots;
+  while (u < fend || t < tend) {
+    int e, mt, nt, ks;
+    bool take_thin = false;
+    if (t < tend) {
+      int te, tmt, tnt, tks;
+      const int anchor = thin_unit<SPLITK>(offs, n_tiles_n, t, &te, &tmt, &tnt, &tks);
+      if (u >= fend || anchor < u) {
+        take_thin = true;
+        e = te;
+        mt = tmt;
+        nt = tnt;
+        ks = tks;
+      }
+    }
+    if (take_thin) {
+      t += slots;
+    } else {
+      full_unit<SPLITK>(offs, n_tiles_n, u, &e, &mt, &nt, &ks);
+      u += slots;
+    }
     const int row_begin = offs[e];
     const int rows = offs[e + 1] - row_begin;
     const int m0 = mt * kBM;
@@ -260,9 +366,11 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
       // Thin tile: an expert's last m-tile with at most 32 rows.  The four
       // waves split the 256 weight rows instead (32 rows x 64 weight rows
       // each: 2 x 4 MFMA tiles), so the tile costs its loads, not 256 rows of
-      // MFMAs.  Same slots and B loads as below; only 32 A rows are loaded,
-      // wave w filling LDS rows 8w..8w+7.  Loads run one stage ahead for A
-      // and two for B; each stage waits for its own loads, then a barrier.
+      // MFMAs.  With little arithmetic to hide them behind, loads run three
+      // stages ahead: the weight tiles in slots 1-4 (32 KiB each), the 32
+      // token rows (4 KiB per stage, wave w filling rows 8w..8w+7) in 8
+      // sub-slots of slot 0.  Each stage waits for its own loads, then a
+      // barrier (which also frees the slots of the stage before).
       uint32_t ta_off;
       {
         const int lc = (wave & 1) ? lc_odd : lc_even;  // swizzle of LDS row 8*wave + ld_row
@@ -270,12 +378,23 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
           ta_off = ((static_cast<uint32_t>(gather[row_begin + min(m0 + wave * 8 + ld_row, rows - 1)]) / kTopK) *
                         static_cast<uint32_t>(K) + lc) * 2u;
         else
-          ta_off = (static_cast<uint32_t>(min(wave * 8 + ld_row, rows - 1 - m0)) * static_cast<uint32_t>(K) + lc) * 2u;
+          ta_off = (static_cast<uint32_t>(min(wave * 8 + ld_row, rows - 1 - m0)) * static_cast<uint32_t>(K) + lc) *
+                   2u;
       }
-#define LOAD_A_THIN(KT_)                                                                                 \
-  __builtin_amdgcn_global_load_lds(                                                                      \
-      GLOBAL_PTR(reinterpret_cast<const char*>(a_base + static_cast<int64_t>(KT_) * kBK) + ta_off),        \
-      LDS_PTR(&ring[(KT_) & 1][(wave * 8) * kBK]), 16, 0, 0);
+      constexpr int kThinSub = kThinRows * kBK;  // elements of one token sub-slot
+      constexpr int kThinLoads = 9;              // loads per wave and stage: 8 weight + 1 token
+#define LOAD_THIN(KT_)                                                                                   \
+  {                                                                                                      \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                      \
+      __builtin_amdgcn_global_load_lds(                                                                  \
+          GLOBAL_PTR(reinterpret_cast<const char*>(b_base + static_cast<int64_t>(j * 8) * K +              \
+                                                   static_cast<int64_t>(KT_) * kBK) + b_off[j & 1]),     \
+          LDS_PTR(&ring[1 + ((KT_) & 3)][(wave * 64 + j * 8) * kBK]), 16, 0, 0);                         \
+    }                                                                                                    \
+    __builtin_amdgcn_global_load_lds(                                                                    \
+        GLOBAL_PTR(reinterpret_cast<const char*>(a_base + static_cast<int64_t>(KT_) * kBK) + ta_off),      \
+        LDS_PTR(&ring[0][((KT_) & 7) * kThinSub + (wave * 8) * kBK]), 16, 0, 0);                         \
+  }
       // this wave's B-tile rows: SwiGLU = 32 gate rows and the matching 32 up rows
       int tb_row[4];
 #pragma unroll
@@ -290,36 +409,28 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) tacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) { LOAD_B(0, j, 0); }
-      LOAD_A_THIN(0);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) { LOAD_B(1, j, 1); }
-      int bs = 0;
+      for (int st = 0; st < 3 && st < KT; ++st) LOAD_THIN(st);
       for (int kt = 0; kt < KT; ++kt) {
-        // Issue order: B(0) A(0) B(1) | A(1) B(2) | A(2) B(3) ...: after
-        // stage kt's last load only B(kt+1) was issued.
-        if (kt + 1 < KT)
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+        // stages kt+1 and kt+2 (if any) may stay in flight
+        const int after = min(2, KT - 1 - kt);
+        if (after == 2)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kThinLoads));
+        else if (after == 1)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kThinLoads));
         else
           __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         lds_barrier();  // stage kt landed for all waves; stage kt-1 fully read
-        const int bs1 = bs == 2 ? 0 : bs + 1;
-        const int bs2 = bs1 == 2 ? 0 : bs1 + 1;
-        if (kt + 1 < KT) { LOAD_A_THIN(kt + 1); }
-        if (kt + 2 < KT) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) { LOAD_B(kt + 2, j, bs2); }
-        }
+        if (kt + 3 < KT) LOAD_THIN(kt + 3);  // into the slots of stage kt-1
         bf16x8 ta[2][2], tb[2][4];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            tb[hh][j] = *reinterpret_cast<const bf16x8*>(&ring[2 + bs][lds_off(tb_row[j], hh * 4 + lg)]);
+            tb[hh][j] = *reinterpret_cast<const bf16x8*>(&ring[1 + (kt & 3)][lds_off(tb_row[j], hh * 4 + lg)]);
 #pragma unroll
           for (int i = 0; i < 2; ++i)
-            ta[hh][i] = *reinterpret_cast<const bf16x8*>(&ring[kt & 1][lds_off(i * 16 + l16, hh * 4 + lg)]);
+            ta[hh][i] = *reinterpret_cast<const bf16x8*>(
+                &ring[0][(kt & 7) * kThinSub + lds_off(i * 16 + l16, hh * 4 + lg)]);
         }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
@@ -328,9 +439,8 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               tacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tb[hh][j], ta[hh][i], tacc[i][j], 0, 0, 0);
-        bs = bs1;
       }
-#undef LOAD_A_THIN
+#undef LOAD_THIN
       // every wave's reads of the last stage are done before the next tile refills the slots
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & lgkm0_mask());
       lds_barrier();
