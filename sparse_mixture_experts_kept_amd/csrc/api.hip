@@ -292,17 +292,21 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
     if (st != MOE_OK) return st;
   }
   if (dims->dtype == MOE_BF16 && !use_decode(dims)) {
-    // Prefill: the down projection's reduction is split in two (twice as many
-    // work units to spread over the CUs); the combine adds the two partial
-    // sums in a fixed order.
+    // Prefill.  The down projection's reduction is split in two when the
+    // layer has fewer than two full 256 x 256 tiles per CU (twice the work
+    // units to spread); the combine then adds the two partial sums in a
+    // fixed order.
     int n_cu = 0;
     st = cu_count(&n_cu);
     if (st != MOE_OK) return st;
     st = run_up(dims, x, offs, sorted, w1, w3, h, s);
     if (st != MOE_OK) return st;
-    float* y_rows2 = reinterpret_cast<float*>(ws + plan.y_rows2);
+    const int64_t full_units = (dims->T * dims->k / 256) * (dims->d / 256);
+    const int split = full_units >= 2 * n_cu ? 1 : 2;
+    float* y_rows2 = split == 2 ? reinterpret_cast<float*>(ws + plan.y_rows2) : nullptr;
     st = hip_status(moe::launch_down_prefill(static_cast<const bf16_t*>(h), offs, static_cast<const bf16_t*>(w2),
-                                             y_rows, dims->d, dims->f, n_cu, 2, y_rows2 - y_rows, s));
+                                             y_rows, dims->d, dims->f, n_cu, split,
+                                             split == 2 ? y_rows2 - y_rows : 0, s));
     if (st != MOE_OK) return st;
     return hip_status(
         moe::launch_combine(dims->dtype, y_rows, y_rows2, rows, w, y, dims->T, dims->d, n_cu, s));

@@ -5,25 +5,158 @@
 // "Mixtral & Sparse MoE (2024) > The Solution" (routing paragraph) and
 // changes no value.
 //
-// One workgroup of 1024 threads: (1) LDS histogram of the expert ids,
-// (2) exclusive scan over the 8 counts -> offsets, (3) a stable scatter: the
-// slots are taken in chunks of 1024 in slot order; inside a chunk, a slot's
-// rank among earlier slots of the same expert is the popcount of a wave
-// ballot below its lane plus the counts of earlier waves.  No atomics decide
-// an order, so the result is deterministic.
+// One workgroup of 1024 threads; thread i owns 8 consecutive slots of each
+// chunk of 8192.  Pass 1: per-thread counts per expert, summed over the
+// workgroup -> offsets (exclusive scan over the 8 experts).  Pass 2, chunk by
+// chunk in slot order: per-thread counts packed two experts per 32-bit word
+// (16 bits each; at most 8192 per chunk), an exclusive scan over the lanes
+// of each wave (shuffles) and over the 16 waves (LDS) gives every thread the
+// number of earlier slots of each expert, and the thread places its 8 slots
+// in order.  Stable (slot order within an expert) and free of atomics, so the
+// result is deterministic.
 #include "common.hpp"
 #include "launch.hpp"
 #include "permute_dev.hpp"
 
 namespace moe {
+namespace {
+
+constexpr int kSlotsPerThread = 8;
+constexpr int kChunk = kPermThreads * kSlotsPerThread;  // 8192 slots
+
+// The 8 expert ids of this thread's slots s0..s0+7 (-1 past the end or invalid).
+__device__ __forceinline__ void load_ids(const int32_t* __restrict__ idx, int32_t n_slots, int s0, int* ids) {
+  if (s0 + kSlotsPerThread <= n_slots) {
+    const int4 a = *reinterpret_cast<const int4*>(idx + s0);
+    const int4 b = *reinterpret_cast<const int4*>(idx + s0 + 4);
+    ids[0] = a.x; ids[1] = a.y; ids[2] = a.z; ids[3] = a.w;
+    ids[4] = b.x; ids[5] = b.y; ids[6] = b.z; ids[7] = b.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < kSlotsPerThread; ++i) ids[i] = s0 + i < n_slots ? idx[s0 + i] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < kSlotsPerThread; ++i) ids[i] = valid_expert(ids[i]);
+}
 
 __global__ void __launch_bounds__(kPermThreads) permute_kernel(const int32_t* __restrict__ idx, int32_t n_slots,
                                                                int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ sorted_slots,
                                                                int32_t* __restrict__ slot_rows,
                                                                int32_t* __restrict__ counts_out) {
-  permute_block(idx, n_slots, offsets, sorted_slots, slot_rows, counts_out);
+  __shared__ int32_t wave_sum[kPermWaves][kExperts];
+  __shared__ uint32_t wave_pk[kPermWaves][kExperts / 2];
+  __shared__ int32_t base_s[kExperts];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+
+  // Pass 1: counts per expert.
+  int cnt[kExperts];
+#pragma unroll
+  for (int e = 0; e < kExperts; ++e) cnt[e] = 0;
+  for (int c = 0; c < n_slots; c += kChunk) {
+    int ids[kSlotsPerThread];
+    load_ids(idx, n_slots, c + tid * kSlotsPerThread, ids);
+#pragma unroll
+    for (int i = 0; i < kSlotsPerThread; ++i)
+#pragma unroll
+      for (int e = 0; e < kExperts; ++e) cnt[e] += ids[i] == e ? 1 : 0;
+  }
+#pragma unroll
+  for (int e = 0; e < kExperts; ++e) {
+    int v = cnt[e];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    if (lane == 0) wave_sum[wave][e] = v;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int e = 0; e < kExperts; ++e) {
+      int tot = 0;
+      for (int w = 0; w < kPermWaves; ++w) tot += wave_sum[w][e];
+      offsets[e] = run;
+      base_s[e] = run;
+      if (counts_out) counts_out[e] = tot;
+      run += tot;
+    }
+    offsets[kExperts] = run;
+  }
+  __syncthreads();
+
+  // Pass 2: stable scatter, chunk by chunk.
+  for (int c = 0; c < n_slots; c += kChunk) {
+    const int s0 = c + tid * kSlotsPerThread;
+    int ids[kSlotsPerThread];
+    load_ids(idx, n_slots, s0, ids);
+    // packed counts: word k holds experts 2k (low half) and 2k+1 (high half)
+    uint32_t pk[kExperts / 2];
+#pragma unroll
+    for (int k = 0; k < kExperts / 2; ++k) pk[k] = 0;
+#pragma unroll
+    for (int i = 0; i < kSlotsPerThread; ++i)
+#pragma unroll
+      for (int k = 0; k < kExperts / 2; ++k)
+        pk[k] += (ids[i] == 2 * k ? 1u : 0u) + (ids[i] == 2 * k + 1 ? 0x10000u : 0u);
+    // inclusive scan over the lanes of the wave
+    uint32_t inc[kExperts / 2];
+#pragma unroll
+    for (int k = 0; k < kExperts / 2; ++k) {
+      uint32_t v = pk[k];
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const uint32_t u = __shfl_up(v, o, kWave);
+        if (lane >= o) v += u;
+      }
+      inc[k] = v;
+    }
+    if (lane == kWave - 1) {
+#pragma unroll
+      for (int k = 0; k < kExperts / 2; ++k) wave_pk[wave][k] = inc[k];
+    }
+    __syncthreads();
+    // earlier waves' counts, and this chunk's totals
+    uint32_t before[kExperts / 2], total[kExperts / 2];
+#pragma unroll
+    for (int k = 0; k < kExperts / 2; ++k) {
+      before[k] = 0;
+      total[k] = 0;
+    }
+    for (int w = 0; w < kPermWaves; ++w) {
+#pragma unroll
+      for (int k = 0; k < kExperts / 2; ++k) {
+        const uint32_t v = wave_pk[w][k];
+        if (w < wave) before[k] += v;
+        total[k] += v;
+      }
+    }
+    int next[kExperts];  // position of this thread's next slot of each expert
+#pragma unroll
+    for (int k = 0; k < kExperts / 2; ++k) {
+      const uint32_t ex = before[k] + inc[k] - pk[k];  // exclusive prefix
+      next[2 * k] = base_s[2 * k] + static_cast<int>(ex & 0xFFFFu);
+      next[2 * k + 1] = base_s[2 * k + 1] + static_cast<int>(ex >> 16);
+    }
+#pragma unroll
+    for (int i = 0; i < kSlotsPerThread; ++i) {
+      const int e = ids[i];
+      if (e < 0) continue;
+      int pos = 0;
+#pragma unroll
+      for (int ee = 0; ee < kExperts; ++ee)
+        if (e == ee) pos = next[ee]++;
+      sorted_slots[pos] = s0 + i;
+      slot_rows[s0 + i] = pos;
+    }
+    __syncthreads();  // every thread has read base_s and wave_pk of this chunk
+    if (tid < kExperts) {
+      const uint32_t t = total[tid / 2];
+      base_s[tid] += static_cast<int>((tid & 1) ? (t >> 16) : (t & 0xFFFFu));
+    }
+    __syncthreads();
+  }
 }
+
+}  // namespace
 
 hipError_t launch_permute(const int32_t* idx, int32_t n_slots, int32_t* offsets, int32_t* sorted_slots,
                           int32_t* slot_rows, int32_t* counts_out, hipStream_t s) {
