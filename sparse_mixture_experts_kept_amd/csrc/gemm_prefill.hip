@@ -51,6 +51,8 @@ constexpr int kXcds = 8;
 constexpr int kGroupN = 4;     // n-tiles per group in the tile order
 constexpr int kThinRows = 32;  // m-tiles with at most this many rows take the thin path
 constexpr int kSlotElems = kBM * kBK;  // one 32 KiB slot (kBM == kBN)
+// Word 3 of a raw buffer resource on gfx9 (no format conversion).
+constexpr int kBufferFlags = 0x00020000;
 
 #define GLOBAL_PTR(p) ((const __attribute__((address_space(1))) void*)(p))
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
@@ -190,16 +192,15 @@ __device__ __forceinline__ int first_thin_from(const int32_t* offs, int n_tiles_
 // ---- pieces of the main loop (macros keep the fragment arrays in registers)
 
 // Load j (0..7) of this wave for stage KT: 8 rows of 128 B, A rows go to A
-// slot KT&1, B rows to B slot BSL (0..2).
+// slot KT&1, B rows to B slot BSL (0..2).  Buffer loads: a per-tile scalar
+// resource, a 32-bit per-lane byte offset fixed for the tile and the stage's
+// byte offset as the scalar offset, so a load needs no address arithmetic.
 #define LOAD_A(KT_, J)                                                                                   \
-  __builtin_amdgcn_global_load_lds(                                                                      \
-      GLOBAL_PTR(reinterpret_cast<const char*>(a_base + static_cast<int64_t>(KT_) * kBK) + a_off[J]),      \
-      LDS_PTR(&ring[(KT_) & 1][(wave * 64 + (J) * 8) * kBK]), 16, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, LDS_PTR(&ring[(KT_) & 1][(wave * 64 + (J) * 8) * kBK]), 16, \
+                                           a_off[J], (KT_) * (kBK * 2), 0, 0);
 #define LOAD_B(KT_, J, BSL)                                                                              \
-  __builtin_amdgcn_global_load_lds(                                                                      \
-      GLOBAL_PTR(reinterpret_cast<const char*>(b_base + static_cast<int64_t>((J) * 8) * K +                \
-                                               static_cast<int64_t>(KT_) * kBK) + b_off[(J) & 1]),       \
-      LDS_PTR(&ring[2 + (BSL)][(wave * 64 + (J) * 8) * kBK]), 16, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, LDS_PTR(&ring[2 + (BSL)][(wave * 64 + (J) * 8) * kBK]), 16, \
+                                           b_off[J], (KT_) * (kBK * 2), 0, 0);
 
 // Fragments of k-half H (0/1): B block J from B slot BSL, A block I from A slot AS.
 #define READ_B(FB, BSL, H, J) \
@@ -358,9 +359,15 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
     const bf16_t* bsrc = SWIGLU ? ((wave & 1) ? B1 : B0) : B0;
     const int brow0 = min(SWIGLU ? n0 + (wave >> 1) * 64 : n0 + wave * 64, N - 64);
     const bf16_t* b_base = bsrc + (static_cast<int64_t>(e) * N + brow0) * K + ks * k_part;
-    uint32_t b_off[2];
-    b_off[0] = (static_cast<uint32_t>(ld_row) * static_cast<uint32_t>(K) + lc_even) * 2u;
-    b_off[1] = (static_cast<uint32_t>(ld_row) * static_cast<uint32_t>(K) + lc_odd) * 2u;
+    uint32_t b_off[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      b_off[j] = (static_cast<uint32_t>(j * 8 + ld_row) * static_cast<uint32_t>(K) + ((j & 1) ? lc_odd : lc_even)) * 2u;
+    // Raw buffer resources (stride 0; loads past num_records would read zero).
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a_base), 0, 0x7FFFFFFF,
+                                                                           kBufferFlags);
+    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(b_base), 0, 0x7FFFFFFF,
+                                                                           kBufferFlags);
 
     if (rows - m0 <= kThinRows) {
       // Thin tile: an expert's last m-tile with at most 32 rows.  The four
@@ -386,14 +393,11 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
 #define LOAD_THIN(KT_)                                                                                   \
   {                                                                                                      \
     _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                      \
-      __builtin_amdgcn_global_load_lds(                                                                  \
-          GLOBAL_PTR(reinterpret_cast<const char*>(b_base + static_cast<int64_t>(j * 8) * K +              \
-                                                   static_cast<int64_t>(KT_) * kBK) + b_off[j & 1]),     \
-          LDS_PTR(&ring[1 + ((KT_) & 3)][(wave * 64 + j * 8) * kBK]), 16, 0, 0);                         \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, LDS_PTR(&ring[1 + ((KT_) & 3)][(wave * 64 + j * 8) * kBK]), \
+                                               16, b_off[j], (KT_) * (kBK * 2), 0, 0);                  \
     }                                                                                                    \
-    __builtin_amdgcn_global_load_lds(                                                                    \
-        GLOBAL_PTR(reinterpret_cast<const char*>(a_base + static_cast<int64_t>(KT_) * kBK) + ta_off),      \
-        LDS_PTR(&ring[0][((KT_) & 7) * kThinSub + (wave * 8) * kBK]), 16, 0, 0);                         \
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, LDS_PTR(&ring[0][((KT_) & 7) * kThinSub + (wave * 8) * kBK]), \
+                                             16, ta_off, (KT_) * (kBK * 2), 0, 0);                       \
   }
       // this wave's B-tile rows: SwiGLU = 32 gate rows and the matching 32 up rows
       int tb_row[4];

@@ -5,7 +5,8 @@
 // "Mixtral & Sparse MoE (2024) > The Solution" (routing paragraph) and
 // changes no value.
 //
-// One workgroup of 1024 threads; thread i owns 8 consecutive slots of each
+// Up to 1024 slots: one slot per thread, wave ballots (permute_dev.hpp).
+// More: one workgroup of 1024 threads; thread i owns 8 consecutive slots of each
 // chunk of 8192.  Pass 1: per-thread counts per expert, summed over the
 // workgroup -> offsets (exclusive scan over the 8 experts).  Pass 2, chunk by
 // chunk in slot order: per-thread counts packed two experts per 32-bit word
@@ -156,12 +157,25 @@ __global__ void __launch_bounds__(kPermThreads) permute_kernel(const int32_t* __
   }
 }
 
+// Up to one slot per thread: the ballot form of permute_dev.hpp, fewer passes.
+__global__ void __launch_bounds__(kPermThreads) permute_small_kernel(const int32_t* __restrict__ idx, int32_t n_slots,
+                                                                     int32_t* __restrict__ offsets,
+                                                                     int32_t* __restrict__ sorted_slots,
+                                                                     int32_t* __restrict__ slot_rows,
+                                                                     int32_t* __restrict__ counts_out) {
+  permute_block(idx, n_slots, offsets, sorted_slots, slot_rows, counts_out);
+}
+
 }  // namespace
 
 hipError_t launch_permute(const int32_t* idx, int32_t n_slots, int32_t* offsets, int32_t* sorted_slots,
                           int32_t* slot_rows, int32_t* counts_out, hipStream_t s) {
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, idx, n_slots, offsets, sorted_slots,
-                     slot_rows, counts_out);
+  if (n_slots <= kPermThreads)
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kPermThreads), 0, s, idx, n_slots, offsets, sorted_slots,
+                       slot_rows, counts_out);
+  else
+    hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, idx, n_slots, offsets, sorted_slots,
+                       slot_rows, counts_out);
   return hipGetLastError();
 }
 

@@ -73,6 +73,7 @@ KERNEL_SOURCES = {
     "router": ["router.hip", "permute_dev.hpp", "common.hpp"],
     "route_permute": ["router.hip", "permute_dev.hpp", "common.hpp"],
     "permute_kernel": ["permute.hip", "permute_dev.hpp", "common.hpp"],
+    "permute_small_kernel": ["permute.hip", "permute_dev.hpp", "common.hpp"],
     "combine_kernel": ["combine.hip", "common.hpp"],
     "rmsnorm_residual_kernel": ["combine.hip", "common.hpp"],
 }
