@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s at T=4096 + µs/layer at T=32; % of MFMA/HBM peak"
 # Kernels the roofline entries describe (names as the profiler reports them).
 UP_PREFILL_KERNEL = "moe::grouped_gemm_prefill_kernel<true, 1>"
-UP_DECODE_KERNEL = "moe::up_decode_kernel<4, 2>"
+UP_DECODE_KERNEL = "moe::decode_stream_kernel<true, 2, 4>"
 
 
 def _log(msg):
@@ -229,7 +229,7 @@ def main():
         dec = {"workload": "mixtral-moe-ffn-decode", "T": T, "us_per_layer": sec * 1e6, "tokens_per_s": T / sec,
                "experts_touched": touched, "layer_bytes": nbytes,
                "layer_frac_of_hbm_peak": nbytes / sec / A.PEAK_HBM_BYTES, "stage_ms": stages,
-               "roofline": {"kernel": "up_decode_kernel (up projection + SwiGLU)",
+               "roofline": {"kernel": "decode_stream_kernel<UP> (up projection + SwiGLU)",
                             "bound": "hbm", "achieved": up_bytes / (stages["up"] * 1e-3) / 1e9,
                             "peak": A.PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                             "frac": up_bytes / (stages["up"] * 1e-3) / A.PEAK_HBM_BYTES,

@@ -103,11 +103,14 @@ moe_status run_up(const moe_dims* dims, const void* x, const int32_t* offs, cons
   const bf16_t* w1b = static_cast<const bf16_t*>(w1);
   const bf16_t* w3b = static_cast<const bf16_t*>(w3);
   bf16_t* hb = static_cast<bf16_t*>(h);
-  if (use_decode(dims))
-    return hip_status(moe::launch_up_decode(xb, offs, sorted, w1b, w3b, hb, dims->T, dims->d, dims->f, s));
   int n_cu = 0;
   const moe_status st = cu_count(&n_cu);
   if (st != MOE_OK) return st;
+  if (use_decode(dims)) {
+    if (dims->T <= kDecodeMaxTokens)
+      return hip_status(moe::launch_up_decode_stream(xb, offs, sorted, w1b, w3b, hb, dims->T, dims->d, dims->f, n_cu, s));
+    return hip_status(moe::launch_up_decode(xb, offs, sorted, w1b, w3b, hb, dims->T, dims->d, dims->f, s));
+  }
   return hip_status(moe::launch_up_prefill(xb, offs, sorted, w1b, w3b, hb, dims->d, dims->f, n_cu, s));
 }
 
@@ -118,11 +121,14 @@ moe_status run_down(const moe_dims* dims, const void* h, const int32_t* offs, co
                                            dims->T * dims->k, dims->d, dims->f, s));
   const bf16_t* hb = static_cast<const bf16_t*>(h);
   const bf16_t* w2b = static_cast<const bf16_t*>(w2);
-  if (use_decode(dims))
-    return hip_status(moe::launch_down_decode(hb, offs, w2b, y_rows, dims->T, dims->d, dims->f, 1, 0, s));
   int n_cu = 0;
   const moe_status st = cu_count(&n_cu);
   if (st != MOE_OK) return st;
+  if (use_decode(dims)) {
+    if (dims->T <= kDecodeMaxTokens)
+      return hip_status(moe::launch_down_decode_stream(hb, offs, w2b, y_rows, dims->T, dims->d, dims->f, n_cu, s));
+    return hip_status(moe::launch_down_decode(hb, offs, w2b, y_rows, dims->T, dims->d, dims->f, 1, 0, s));
+  }
   return hip_status(moe::launch_down_prefill(hb, offs, w2b, y_rows, dims->d, dims->f, n_cu, 1, 0, s));
 }
 
@@ -263,27 +269,13 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
   float* y_rows = reinterpret_cast<float*>(ws + plan.y_rows);
 
   if (dims->T <= kDecodeMaxTokens) {
-    // Small batch: routing and permutation in one workgroup; with bf16 the
-    // down projection also applies the combine, so y_rows is never written.
+    // Small batch: routing and permutation in one workgroup.
     st = hip_status(moe::launch_route_permute(dims->dtype, x, w_gate, logit_bias, idx, w,
                                               static_cast<int32_t>(dims->T), dims->d, offs, sorted, rows,
                                               expert_counts_out, s));
     if (st != MOE_OK) return st;
-    if (dims->dtype == MOE_BF16 && use_decode(dims)) {
-      // Decode: up projection, down projection with its reduction split in
-      // two (partials in y_rows and y_rows2), combine adding both in order.
-      st = run_up(dims, x, offs, sorted, w1, w3, h, s);
-      if (st != MOE_OK) return st;
-      float* y_rows2 = reinterpret_cast<float*>(ws + plan.y_rows2);
-      st = hip_status(moe::launch_down_decode(static_cast<const bf16_t*>(h), offs, static_cast<const bf16_t*>(w2),
-                                              y_rows, dims->T, dims->d, dims->f, 2, y_rows2 - y_rows, s));
-      if (st != MOE_OK) return st;
-      int n_cu = 0;
-      st = cu_count(&n_cu);
-      if (st != MOE_OK) return st;
-      return hip_status(moe::launch_combine(dims->dtype, y_rows, dims->f % 256 == 0 ? y_rows2 : nullptr, rows, w, y,
-                                            dims->T, dims->d, n_cu, s));
-    }
+    // (bf16 decode then runs the streaming up and down projections through
+    // run_experts below.)
   } else {
     st = run_router(dims, x, w_gate, logit_bias, idx, w, nullptr, s);
     if (st != MOE_OK) return st;

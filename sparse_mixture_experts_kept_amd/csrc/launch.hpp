@@ -43,6 +43,15 @@ hipError_t launch_up_decode(const bf16_t* x, const int32_t* offs, const int32_t*
 hipError_t launch_down_decode(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int64_t T, int d,
                               int f, int split, int64_t split_stride, hipStream_t s);
 
+// Decode batches of at most 64 tokens (rows per expert <= T): the weight
+// streams of the touched experts through per-wave LDS rings, 2 * n_cu
+// single-wave workgroups.  Returns hipErrorInvalidValue for T > 64.
+hipError_t launch_up_decode_stream(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots,
+                                   const bf16_t* w1, const bf16_t* w3, bf16_t* h, int64_t T, int d, int f, int n_cu,
+                                   hipStream_t s);
+hipError_t launch_down_decode_stream(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int64_t T,
+                                     int d, int f, int n_cu, hipStream_t s);
+
 // Small batches (T <= 64): routing + permutation in one workgroup.
 hipError_t launch_route_permute(int dtype, const void* x, const void* wg, const float* bias, int32_t* idx, float* w,
                                 int32_t T, int d, int32_t* offsets, int32_t* sorted_slots, int32_t* slot_rows,

@@ -70,6 +70,7 @@ KERNEL_SOURCES = {
     "grouped_gemm_prefill_kernel": ["gemm_prefill.hip", "common.hpp"],
     "up_decode_kernel": ["gemm_decode.hip", "common.hpp"],
     "down_decode_kernel": ["gemm_decode.hip", "common.hpp"],
+    "decode_stream_kernel": ["gemm_decode_stream.hip", "common.hpp"],
     "router": ["router.hip", "permute_dev.hpp", "common.hpp"],
     "route_permute": ["router.hip", "permute_dev.hpp", "common.hpp"],
     "permute_kernel": ["permute.hip", "permute_dev.hpp", "common.hpp"],

@@ -114,9 +114,25 @@ def test_bf16_prefill_kernels_tiny_batches(T):
     run_and_check(_layer(T, 256, 512, seed=100 + T), variant=moe.VARIANT_PREFILL)
 
 
-@pytest.mark.parametrize("T,d,f", [(32, 512, 1024), (64, 256, 512), (1, 256, 512), (7, 128, 256)])
+@pytest.mark.parametrize("T,d,f", [(32, 512, 1024), (64, 256, 512), (1, 256, 512), (7, 128, 256), (48, 384, 640),
+                                   (33, 128, 128)])
 def test_bf16_decode_kernels(T, d, f):
+    # T <= 64: the streaming kernels (token groups of 16: two up to T=32,
+    # four above); d=128 or f=128 give units of a single stage, d=384 / f=640
+    # odd stage counts
     run_and_check(_layer(T, d, f, seed=200 + T), variant=moe.VARIANT_DECODE)
+
+
+@pytest.mark.parametrize("T", [64, 29])
+def test_decode_streaming_two_experts_full(T):
+    # every token on experts 3 and 6: two experts with T rows each (the
+    # largest token-group count of the streaming kernels), six experts empty
+    layer = _layer(T, 256, 512, seed=17 + T)
+    b = torch.zeros(8, dtype=torch.float32)
+    b[3], b[6] = 60.0, 40.0
+    layer["logit_bias"] = b.cuda()
+    out = run_and_check(layer, variant=moe.VARIANT_DECODE)
+    np.testing.assert_array_equal(out["counts"].cpu().numpy(), [0, 0, 0, T, 0, 0, T, 0])
 
 
 @pytest.mark.parametrize("T", [200, 600])
