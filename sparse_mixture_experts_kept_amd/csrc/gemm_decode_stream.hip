@@ -10,23 +10,23 @@
 // experts' weights ("Mixtral of Experts", azimuth.plus, paragraph on active
 // versus stored parameters), so the design is about the access pattern:
 // - Weights go from HBM straight into LDS (buffer_load ... lds, nontemporal)
-//   in runs of 256 contiguous bytes per row: each load instruction moves 4
-//   rows x 256 B = 1 KiB.  Measured on MI355X, such loads sustain about
-//   6.4-6.7 TB/s where the 64-byte pieces of 16 rows that a register-direct
-//   MFMA operand load touches reach about 5.5 TB/s.
+//   in runs of W = 256 or 512 contiguous bytes per row; each load
+//   instruction moves 1 KiB (1024/W rows).  Measured on MI355X, such loads
+//   sustain 6.4-6.8 TB/s where the 64-byte pieces of 16 rows that a
+//   register-direct MFMA operand load touches reach about 5.5 TB/s.
 // - One wavefront per workgroup, two workgroups per CU, persistent: wave w
 //   takes work units w, w + G, ... (G workgroups) and streams them as one
 //   continuous sequence of stages, S stages in flight in a private LDS ring
 //   (no workgroup barrier anywhere; each wave reads only what it loaded).
-// - A stage is 128 reduction elements: for the up projection 16 rows of w1
-//   and the same 16 rows of w3, for the down projection 32 rows of w2, plus
-//   the unit's token rows (MAXG groups of 16, 256 B each, loaded the same
-//   way; the up projection gathers x rows through the permutation).  Every
-//   stage issues the same number of loads, so "this stage has landed" is
-//   one s_waitcnt vmcnt with a constant.
-// - LDS rows are 256 B with the 16-byte chunk index XOR the row (mod 16), set
-//   by which chunk each lane loads; the MFMA fragment reads (16 rows x one
-//   chunk) then touch 16 distinct bank groups.
+// - A stage is W/2 reduction elements of each of the unit's weight rows
+//   (NB blocks of 16: the up projection's gate rows and the same up rows,
+//   or consecutive rows of w2) plus its token rows (groups of 16, loaded the
+//   same way; the up projection gathers x rows through the permutation).
+//   Every stage issues the same number of loads, so "this stage has landed"
+//   is one s_waitcnt vmcnt with a constant, at most 63 loads in flight.
+// - LDS rows are W bytes with the 16-byte chunk index XOR the row (mod 16),
+//   set by which chunk each lane loads; the MFMA fragment reads (16 rows x
+//   one chunk) then touch 16 distinct bank groups.
 // - MFMA v_mfma_f32_16x16x32_bf16: weights as src0 (16 rows = output
 //   features), tokens as src1, fp32 accumulators; SwiGLU or the fp32 store at
 //   the end of each unit.
@@ -36,10 +36,6 @@
 namespace moe {
 namespace {
 
-constexpr int kRowBytes = 256;                 // bytes of a row per stage
-constexpr int kStageK = kRowBytes / 2;         // reduction elements per stage
-constexpr int kBlockElems = 16 * kStageK;      // one 16-row block of a stage (4 KiB)
-constexpr int kChunks = kRowBytes / 16;        // 16-byte chunks per LDS row
 constexpr int kBufferFlags = 0x00020000;       // word 3 of a raw buffer resource on gfx9
 constexpr int kNontemporal = 2;                // cache-policy bits of the weight loads
 
@@ -51,118 +47,152 @@ constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4
 // ... and lgkmcnt(0) alone.
 constexpr int lgkm0_imm() { return 0xF | (0x3 << 14) | (0x7 << 4); }
 
-// Work unit u of the non-empty experts (each has `per_expert` units) -> expert, index within it.
-__device__ __forceinline__ void unit_of(const int* o, int per_expert, int u, int* e_out, int* r_out) {
+// Passes over an expert's weights: one per `rows_per_pass` of its rows.
+__device__ __forceinline__ int passes_of(int rows, int rows_per_pass) {
+  return (rows + rows_per_pass - 1) / rows_per_pass;
+}
+
+// Work unit u -> expert, weight-row block r, pass.  Expert e contributes
+// per_expert * passes(e) units (none if it has no rows).
+__device__ __forceinline__ void unit_of(const int* o, int per_expert, int rows_per_pass, int u, int* e_out, int* r_out,
+                                        int* p_out) {
   int pre = 0, e_sel = 0, pre_sel = 0;
 #pragma unroll
   for (int e = 0; e < kExperts; ++e) {
-    const int n = o[e + 1] > o[e] ? per_expert : 0;
+    const int n = per_expert * passes_of(o[e + 1] - o[e], rows_per_pass);
     if (u >= pre && u < pre + n) {
       e_sel = e;
       pre_sel = pre;
     }
     pre += n;
   }
+  const int local = u - pre_sel;
   *e_out = e_sel;
-  *r_out = u - pre_sel;
+  *p_out = local / per_expert;
+  *r_out = local - *p_out * per_expert;
 }
 
-// UP: units (expert, 16 rows of w1 and w3), act = x, out = h (bf16).
-// DOWN: units (expert, 32 rows of w2), act = h, out = y_rows (fp32).
-template <bool UP, int MAXG, int S>
+// UP: units (expert, 8*NB rows of w1 and the same rows of w3: NB/2 blocks
+// of 16 each, pass), act = x (T rows), out = h (bf16).
+// DOWN: units (expert, 16*NB rows of w2, pass), act = h (n_slots rows),
+// out = y_rows (fp32).
+// A stage covers W bytes (W/2 reduction elements) of each row.  A pass
+// handles up to 16*MAXG of the expert's rows; an expert with more rows
+// streams its weights once per pass.  Token group g of a unit is loaded only
+// if it holds one of the expert's rows; the loads of the other groups use an
+// offset past the end of the buffer, which the buffer hardware answers with
+// zeros and no memory traffic (the instruction count, and so the wait,
+// stays fixed).
+template <bool UP, int W, int NB, int MAXG, int S>
 __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __restrict__ act,
                                                               const int32_t* __restrict__ sorted_slots,
                                                               const int32_t* __restrict__ offs,
                                                               const bf16_t* __restrict__ wa,
                                                               const bf16_t* __restrict__ wb, void* __restrict__ out,
-                                                              int d, int f, int n_slots) {
-  constexpr int kStageElems = (2 + MAXG) * kBlockElems;
-  constexpr int kLoads = 8 + 4 * MAXG;  // load instructions per stage
+                                                              int d, int f, int act_rows) {
+  constexpr int kStageK = W / 2;                  // reduction elements per stage
+  constexpr int kChunks = W / 16;                 // 16-byte chunks per LDS row
+  constexpr int kBlockElems = 16 * kStageK;       // one 16-row block of a stage
+  constexpr int kRowsPerLoad = 1024 / W;          // rows one 1 KiB load instruction covers
+  constexpr int kLoadsPerBlock = 16 / kRowsPerLoad;
+  constexpr int kStageElems = (NB + MAXG) * kBlockElems;
+  constexpr int kLoads = kLoadsPerBlock * (NB + MAXG);  // load instructions per stage
+  constexpr int kRowsPerPass = 16 * MAXG;
+  static_assert(W == 256 || W == 512, "row run per stage");
+  static_assert(NB % 2 == 0 && NB <= 4 && MAXG <= 2, "unit shape");
+  static_assert((S - 1) * kLoads <= 63, "vmcnt holds at most 63 loads in flight");
   __shared__ __align__(16) bf16_t ring[S][kStageElems];
 
   const int lane = threadIdx.x;
   const int l16 = lane % 16, lg = lane / 16;
-  const int K = UP ? d : f;                      // reduction length
-  const int per_expert = UP ? f / 16 : d / 32;   // units per expert
-  const int KS = K / kStageK;                    // stages per unit (>= 1)
+  const int ld_row = lane / kChunks, ld_chunk = lane % kChunks;  // a load lane's row and physical chunk
+  const int K = UP ? d : f;                                      // reduction length
+  const int unit_rows = UP ? 8 * NB : 16 * NB;                   // weight rows per unit and matrix
+  const int per_expert = (UP ? f : d) / unit_rows;               // weight-row blocks per expert
+  const int KS = K / kStageK;                                    // stages per unit (>= 1)
+  const uint32_t act_bytes = static_cast<uint32_t>(act_rows) * static_cast<uint32_t>(K * 2);
   int o[kExperts + 1];
 #pragma unroll
   for (int e = 0; e <= kExperts; ++e) o[e] = offs[e];
   int n_units = 0;
 #pragma unroll
-  for (int e = 0; e < kExperts; ++e) n_units += o[e + 1] > o[e] ? per_expert : 0;
+  for (int e = 0; e < kExperts; ++e) n_units += per_expert * passes_of(o[e + 1] - o[e], kRowsPerPass);
   const int G = gridDim.x;
   if (static_cast<int>(blockIdx.x) >= n_units) return;
   const int total = (n_units - static_cast<int>(blockIdx.x) + G - 1) / G * KS;
 
-  // Weight loads: instruction i of a 16-row block puts rows 4i..4i+3 (row
-  // 4i + lg for this lane) into 1 KiB of LDS, this lane's 16 bytes at
-  // physical chunk l16, i.e. logical chunk l16 ^ row.
-  uint32_t w_off[4];
+  // Loads: instruction i of a 16-row block puts rows kRowsPerLoad*i .. +
+  // kRowsPerLoad-1 into 1 KiB of LDS, this lane's 16 bytes at physical
+  // chunk ld_chunk of row kRowsPerLoad*i + ld_row, which holds logical chunk
+  // ld_chunk ^ row: the fragment reads (16 rows x one logical chunk) then hit
+  // 16 distinct bank groups.
+  uint32_t w_off[8];  // kLoadsPerBlock <= 8 (fixed extent: see t_off below)
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rr = 4 * i + lg;
-    w_off[i] = static_cast<uint32_t>(rr * K * 2 + ((l16 ^ rr) * 16));
+  for (int i = 0; i < kLoadsPerBlock; ++i) {
+    const int rr = kRowsPerLoad * i + ld_row;
+    w_off[i] = static_cast<uint32_t>(rr * K * 2 + ((ld_chunk ^ rr) * 16));
   }
 
   // Issue side: unit, stage within it, buffer resources and token offsets.
   int iu = blockIdx.x, iks = 0;
   __amdgpu_buffer_rsrc_t ra, rb;
-  // (A fixed extent: an array sized by the template parameter, passed to
-  // the buffer-load builtin, keeps clang from emitting the launch stub.)
-  static_assert(MAXG <= 4, "at most 64 rows per expert");
-  uint32_t t_off[4][4];
+  // (Fixed extents: an array sized by a template parameter and passed to
+  // the buffer-load builtin keeps clang from emitting the launch stub.)
+  uint32_t t_off[2][8];
   const __amdgpu_buffer_rsrc_t rt =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(act), 0, 0x7FFFFFFF, kBufferFlags);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(act), 0, act_bytes, kBufferFlags);
 #define SET_ISSUE_UNIT(U_)                                                                                   \
   {                                                                                                        \
-    int e_, r_;                                                                                            \
-    unit_of(o, per_expert, (U_), &e_, &r_);                                                                \
+    int e_, r_, p_;                                                                                        \
+    unit_of(o, per_expert, kRowsPerPass, (U_), &e_, &r_, &p_);                                             \
     const int row_begin = o[e_], rows = o[e_ + 1] - o[e_];                                                 \
     const bf16_t* a0;                                                                                      \
     const bf16_t* b0;                                                                                      \
     if constexpr (UP) {                                                                                    \
-      a0 = wa + (static_cast<int64_t>(e_) * f + r_ * 16) * d;                                              \
-      b0 = wb + (static_cast<int64_t>(e_) * f + r_ * 16) * d;                                              \
+      a0 = wa + (static_cast<int64_t>(e_) * f + r_ * unit_rows) * d;                                       \
+      b0 = wb + (static_cast<int64_t>(e_) * f + r_ * unit_rows) * d;                                       \
     } else {                                                                                               \
-      a0 = wa + (static_cast<int64_t>(e_) * d + r_ * 32) * f;                                              \
-      b0 = a0 + static_cast<int64_t>(16) * f;                                                              \
+      a0 = wa + (static_cast<int64_t>(e_) * d + r_ * unit_rows) * f;                                       \
+      b0 = a0;                                                                                             \
     }                                                                                                      \
     ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a0), 0, 0x7FFFFFFF, kBufferFlags);          \
     rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(b0), 0, 0x7FFFFFFF, kBufferFlags);          \
-    _Pragma("unroll") for (int g = 0; g < MAXG; ++g) _Pragma("unroll") for (int q = 0; q < 4; ++q) {       \
-      const int rr = 4 * q + lg; /* row within the 16-row group; clamped rows are loaded, never stored */  \
+    _Pragma("unroll") for (int g = 0; g < MAXG; ++g) _Pragma("unroll") for (int q = 0; q < kLoadsPerBlock; ++q) { \
+      const int rr = kRowsPerLoad * q + ld_row; /* row of the group; clamped rows are loaded, not stored */ \
+      const int m0 = p_ * kRowsPerPass + 16 * g; /* the group's first row */                               \
       int tok;                                                                                             \
       if constexpr (UP) {                                                                                  \
         /* slot ids through the scalar cache (uniform addresses, lgkmcnt): a vector load here would be     \
            ordered behind the weight loads in flight, and waiting for it would drain them; the select is   \
-           arithmetic so that all four loads stay unconditional */                                         \
-        const int b = 16 * g + 4 * q;                                                                      \
-        const int s0 = sorted_slots[row_begin + min(b, rows - 1)];                                         \
-        const int s1 = sorted_slots[row_begin + min(b + 1, rows - 1)];                                     \
-        const int s2 = sorted_slots[row_begin + min(b + 2, rows - 1)];                                     \
-        const int s3 = sorted_slots[row_begin + min(b + 3, rows - 1)];                                     \
-        tok = (s0 + (lg >= 1) * (s1 - s0) + (lg >= 2) * (s2 - s1) + (lg >= 3) * (s3 - s2)) / kTopK;         \
+           arithmetic so that all the loads stay unconditional */                                          \
+        const int b = m0 + kRowsPerLoad * q;                                                               \
+        int sel = sorted_slots[row_begin + min(b, rows - 1)];                                              \
+        _Pragma("unroll") for (int k = 1; k < kRowsPerLoad; ++k)                                           \
+          sel += (ld_row >= k) * (sorted_slots[row_begin + min(b + k, rows - 1)] -                         \
+                                  sorted_slots[row_begin + min(b + k - 1, rows - 1)]);                     \
+        tok = sel / kTopK;                                                                                 \
       } else {                                                                                             \
-        tok = row_begin + min(16 * g + rr, rows - 1);                                                      \
+        tok = row_begin + min(m0 + rr, rows - 1);                                                          \
       }                                                                                                    \
-      t_off[g][q] = static_cast<uint32_t>(tok) * static_cast<uint32_t>(K * 2) +                           \
-                    static_cast<uint32_t>((l16 ^ rr) * 16);                                                \
+      const uint32_t chunk = static_cast<uint32_t>((ld_chunk ^ rr) * 16);                                  \
+      t_off[g][q] = m0 < rows ? static_cast<uint32_t>(tok) * static_cast<uint32_t>(K * 2) + chunk         \
+                              : act_bytes + chunk; /* past the end: zeros, no traffic */                   \
     }                                                                                                      \
   }
 #define ISSUE(SLOT_)                                                                                       \
   {                                                                                                        \
     bf16_t* st_ = ring[SLOT_];                                                                             \
-    const int so = iks * kRowBytes;                                                                        \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                          \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, LDS_PTR(st_ + i * 4 * kStageK), 16, w_off[i], so, 0,    \
-                                               kNontemporal);                                              \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                          \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, LDS_PTR(st_ + kBlockElems + i * 4 * kStageK), 16,       \
-                                               w_off[i], so, 0, kNontemporal);                             \
-    _Pragma("unroll") for (int g = 0; g < MAXG; ++g) _Pragma("unroll") for (int q = 0; q < 4; ++q)         \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, LDS_PTR(st_ + (2 + g) * kBlockElems + q * 4 * kStageK), \
-                                               16, t_off[g][q], so, 0, 0);                                 \
+    const int so = iks * W;                                                                                \
+    _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                                       \
+      const int bo = (UP ? b % (NB / 2) : b) * 16 * K * 2; /* block's first row */                         \
+      _Pragma("unroll") for (int i = 0; i < kLoadsPerBlock; ++i)                                           \
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(UP && b >= NB / 2 ? rb : ra,                              \
+                                                 LDS_PTR(st_ + b * kBlockElems + i * 512), 16, w_off[i],   \
+                                                 so + bo, 0, kNontemporal);                                \
+    }                                                                                                      \
+    _Pragma("unroll") for (int g = 0; g < MAXG; ++g) _Pragma("unroll") for (int q = 0; q < kLoadsPerBlock; ++q) \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, LDS_PTR(st_ + (NB + g) * kBlockElems + q * 512), 16,    \
+                                               t_off[g][q], so, 0, 0);                                     \
     if (++iks == KS) {                                                                                     \
       iks = 0;                                                                                             \
       iu += G;                                                                                             \
@@ -179,15 +209,13 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
 
   // Compute side.
   int cu = blockIdx.x, cks = 0, cslot = 0;
-  int ce, cr;
-  unit_of(o, per_expert, cu, &ce, &cr);
-  int c_begin = o[ce], c_rows = o[ce + 1] - o[ce];
-  f32x4 acc0[MAXG], acc1[MAXG];
+  int ce, cr, cp;
+  unit_of(o, per_expert, kRowsPerPass, cu, &ce, &cr, &cp);
+  f32x4 acc[NB][MAXG];
 #pragma unroll
-  for (int g = 0; g < MAXG; ++g) {
-    acc0[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc1[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int g = 0; g < MAXG; ++g) acc[b][g] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < total; ++j) {
     if (j + S - 1 < total) {
       // the slot being refilled was read by the previous stage's MFMAs
@@ -203,48 +231,49 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
 #pragma unroll
     for (int s = 0; s < kStageK / 32; ++s) {
       const int off = l16 * kStageK + (((4 * s + lg) ^ l16) & (kChunks - 1)) * 8;
-      const bf16x8 fa = *reinterpret_cast<const bf16x8*>(st + off);
-      const bf16x8 fb = *reinterpret_cast<const bf16x8*>(st + kBlockElems + off);
+      bf16x8 w[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) w[b] = *reinterpret_cast<const bf16x8*>(st + b * kBlockElems + off);
 #pragma unroll
       for (int g = 0; g < MAXG; ++g) {  // all groups: MFMA time is free here, a branch is not
-        const bf16x8 t = *reinterpret_cast<const bf16x8*>(st + (2 + g) * kBlockElems + off);
-        acc0[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa, t, acc0[g], 0, 0, 0);
-        acc1[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb, t, acc1[g], 0, 0, 0);
+        const bf16x8 t = *reinterpret_cast<const bf16x8*>(st + (NB + g) * kBlockElems + off);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[b][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w[b], t, acc[b][g], 0, 0, 0);
       }
     }
     cslot = cslot == S - 1 ? 0 : cslot + 1;
     if (++cks == KS) {
-      // acc[g][q]: unit row 16g + l16, output feature 4*lg + q of the block
-      // (down: acc0 rows 0-15 of the unit, acc1 rows 16-31).
+      // acc[b][g][q]: expert row cp*16*MAXG + 16g + l16, feature 4*lg + q of
+      // weight block b (up: blocks < NB/2 gate, the rest up, same features).
+      const int c_begin = o[ce], c_rows = o[ce + 1] - o[ce];
 #pragma unroll
       for (int g = 0; g < MAXG; ++g) {
-        const int m = 16 * g + l16;
+        const int m = cp * kRowsPerPass + 16 * g + l16;
         if (m >= c_rows) continue;
         const int64_t orow = c_begin + m;
         if constexpr (UP) {
-          const f32x4 a = acc0[g], b = acc1[g];
-          uint2 p;
-          p.x = pack_bf16x2(silu(a[0]) * b[0], silu(a[1]) * b[1]);
-          p.y = pack_bf16x2(silu(a[2]) * b[2], silu(a[3]) * b[3]);
-          *reinterpret_cast<uint2*>(static_cast<bf16_t*>(out) + orow * f + cr * 16 + 4 * lg) = p;
+#pragma unroll
+          for (int b = 0; b < NB / 2; ++b) {
+            const f32x4 a = acc[b][g], u = acc[b + NB / 2][g];
+            uint2 p;
+            p.x = pack_bf16x2(silu(a[0]) * u[0], silu(a[1]) * u[1]);
+            p.y = pack_bf16x2(silu(a[2]) * u[2], silu(a[3]) * u[3]);
+            *reinterpret_cast<uint2*>(static_cast<bf16_t*>(out) + orow * f + cr * unit_rows + b * 16 + 4 * lg) = p;
+          }
         } else {
-          float* y = static_cast<float*>(out) + orow * d + cr * 32 + 4 * lg;
-          *reinterpret_cast<float4*>(y) = make_float4(acc0[g][0], acc0[g][1], acc0[g][2], acc0[g][3]);
-          *reinterpret_cast<float4*>(y + 16) = make_float4(acc1[g][0], acc1[g][1], acc1[g][2], acc1[g][3]);
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            *reinterpret_cast<float4*>(static_cast<float*>(out) + orow * d + cr * unit_rows + b * 16 + 4 * lg) =
+                make_float4(acc[b][g][0], acc[b][g][1], acc[b][g][2], acc[b][g][3]);
         }
       }
 #pragma unroll
-      for (int g = 0; g < MAXG; ++g) {
-        acc0[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc1[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int g = 0; g < MAXG; ++g) acc[b][g] = f32x4{0.f, 0.f, 0.f, 0.f};
       cks = 0;
       cu += G;
-      if (cu < n_units) {
-        unit_of(o, per_expert, cu, &ce, &cr);
-        c_begin = o[ce];
-        c_rows = o[ce + 1] - o[ce];
-      }
+      if (cu < n_units) unit_of(o, per_expert, kRowsPerPass, cu, &ce, &cr, &cp);
     }
   }
 }
@@ -253,34 +282,42 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
 #undef ISSUE
 #undef LDS_PTR
 
-template <bool UP, int MAXG, int S>
+// GM workgroups (single waves) per CU.
+template <bool UP, int W, int NB, int MAXG, int S, int GM = 2>
 hipError_t launch_stream(const bf16_t* act, const int32_t* sorted_slots, const int32_t* offs, const bf16_t* wa,
-                         const bf16_t* wb, void* out, int d, int f, int n_slots, int n_cu, hipStream_t s) {
-  hipLaunchKernelGGL((decode_stream_kernel<UP, MAXG, S>), dim3(2 * n_cu), dim3(kWave), 0, s, act, sorted_slots, offs,
-                     wa, wb, out, d, f, n_slots);
+                         const bf16_t* wb, void* out, int d, int f, int act_rows, int n_cu, hipStream_t s) {
+  hipLaunchKernelGGL((decode_stream_kernel<UP, W, NB, MAXG, S>), dim3(GM * n_cu), dim3(kWave), 0, s, act,
+                     sorted_slots, offs, wa, wb, out, d, f, act_rows);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Rows per expert are at most T (top-2 picks two different experts), so
-// MAXG = ceil(T / 16) groups of 16 hold them all: 2 for T <= 32 (4 stages
-// in flight, 64 KiB of LDS), 4 for T <= 64 (3 stages, 72 KiB).
+// T <= 32: one token group per pass (16 rows; an expert with more takes a
+// second pass, rare with 8 rows per expert on average); T <= 64: two groups
+// per pass.  Shapes measured at d=4096, f=14336, T=32 on MI355X (alternating
+// launches in one process): up projection with 512-byte row runs, 3 stages
+// (277 us; 256-byte runs, 6 stages: 292 us), down projection with units of
+// 64 rows of w2, 3 stages (138-144 us; 32-row units: 159-163 us).  d and f
+// are multiples of 128 (checked at the boundary): 512-byte runs need d to be
+// a multiple of 256, the other shapes divide any such d and f.
 hipError_t launch_up_decode_stream(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots,
                                    const bf16_t* w1, const bf16_t* w3, bf16_t* h, int64_t T, int d, int f, int n_cu,
                                    hipStream_t s) {
   if (T > 64) return hipErrorInvalidValue;
-  const int n_slots = static_cast<int>(T) * kTopK;
-  if (T <= 32) return launch_stream<true, 2, 4>(x, sorted_slots, offs, w1, w3, h, d, f, n_slots, n_cu, s);
-  return launch_stream<true, 4, 3>(x, sorted_slots, offs, w1, w3, h, d, f, n_slots, n_cu, s);
+  if (T <= 32) {
+    if (d % 256 == 0) return launch_stream<true, 512, 2, 1, 3>(x, sorted_slots, offs, w1, w3, h, d, f, T, n_cu, s);
+    return launch_stream<true, 256, 2, 1, 6>(x, sorted_slots, offs, w1, w3, h, d, f, T, n_cu, s);
+  }
+  return launch_stream<true, 256, 2, 2, 4>(x, sorted_slots, offs, w1, w3, h, d, f, T, n_cu, s);
 }
 
 hipError_t launch_down_decode_stream(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int64_t T,
                                      int d, int f, int n_cu, hipStream_t s) {
   if (T > 64) return hipErrorInvalidValue;
   const int n_slots = static_cast<int>(T) * kTopK;
-  if (T <= 32) return launch_stream<false, 2, 4>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s);
-  return launch_stream<false, 4, 3>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s);
+  if (T <= 32) return launch_stream<false, 256, 4, 1, 3>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s);
+  return launch_stream<false, 256, 2, 2, 4>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s);
 }
 
 }  // namespace moe
