@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s at T=4096 + µs/layer at T=32; % of MFMA/HBM peak"
 # Kernels the roofline entries describe (names as the profiler reports them).
 UP_PREFILL_KERNEL = "moe::grouped_gemm_prefill_kernel<true, 1>"
-UP_DECODE_KERNEL = "moe::decode_stream_kernel<true, 2, 4>"
+UP_DECODE_KERNEL = "moe::decode_stream_kernel<true, 512, 2, 1, 3>"
 
 
 def _log(msg):
