@@ -63,6 +63,36 @@ bool use_decode(const moe_dims* dims) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Prefill projections hand the short expert tails (the rows past an expert's
+// last full 256-row tile, when at most 32) to the streaming kernels, which
+// spread each tail's weight stream over the whole chip; inside the prefill
+// GEMM such a tile is bound by one CU's load latency (a down-projection tail
+// tile costs 0.58 of a full tile there).  The streaming kernels address x and
+// h with 31-bit byte offsets.
+constexpr bool kUpTailsStreamed = true;
+bool tails_streamable(const moe_dims* dims) {
+  const int64_t limit = int64_t{1} << 31;
+  return dims->T * dims->k * dims->f * 2 < limit && dims->T * dims->d * 2 < limit;
+}
+
+moe_status up_prefill(const moe_dims* dims, const bf16_t* x, const int32_t* offs, const int32_t* sorted,
+                      const bf16_t* w1, const bf16_t* w3, bf16_t* h, int n_cu, hipStream_t s) {
+  const bool tails = kUpTailsStreamed && tails_streamable(dims);
+  moe_status st = hip_status(moe::launch_up_prefill(x, offs, sorted, w1, w3, h, dims->d, dims->f, n_cu, tails, s));
+  if (st != MOE_OK || !tails) return st;
+  return hip_status(moe::launch_up_tail_stream(x, offs, sorted, w1, w3, h, dims->T, dims->d, dims->f, n_cu, s));
+}
+
+// split == 2 keeps the tails in the GEMM (their second partial sum must exist).
+moe_status down_prefill(const moe_dims* dims, const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows,
+                        int n_cu, int split, int64_t split_stride, hipStream_t s) {
+  const bool tails = split == 1 && tails_streamable(dims);
+  moe_status st = hip_status(
+      moe::launch_down_prefill(h, offs, w2, y_rows, dims->d, dims->f, n_cu, split, split_stride, tails, s));
+  if (st != MOE_OK || !tails) return st;
+  return hip_status(moe::launch_down_tail_stream(h, offs, w2, y_rows, dims->T, dims->d, dims->f, n_cu, s));
+}
+
 size_t align256(size_t v) { return (v + 255) & ~size_t{255}; }
 
 struct Workspace {
@@ -111,7 +141,7 @@ moe_status run_up(const moe_dims* dims, const void* x, const int32_t* offs, cons
       return hip_status(moe::launch_up_decode_stream(xb, offs, sorted, w1b, w3b, hb, dims->T, dims->d, dims->f, n_cu, s));
     return hip_status(moe::launch_up_decode(xb, offs, sorted, w1b, w3b, hb, dims->T, dims->d, dims->f, s));
   }
-  return hip_status(moe::launch_up_prefill(xb, offs, sorted, w1b, w3b, hb, dims->d, dims->f, n_cu, s));
+  return up_prefill(dims, xb, offs, sorted, w1b, w3b, hb, n_cu, s);
 }
 
 moe_status run_down(const moe_dims* dims, const void* h, const int32_t* offs, const void* w2, float* y_rows,
@@ -129,7 +159,7 @@ moe_status run_down(const moe_dims* dims, const void* h, const int32_t* offs, co
       return hip_status(moe::launch_down_decode_stream(hb, offs, w2b, y_rows, dims->T, dims->d, dims->f, n_cu, s));
     return hip_status(moe::launch_down_decode(hb, offs, w2b, y_rows, dims->T, dims->d, dims->f, 1, 0, s));
   }
-  return hip_status(moe::launch_down_prefill(hb, offs, w2b, y_rows, dims->d, dims->f, n_cu, 1, 0, s));
+  return down_prefill(dims, hb, offs, w2b, y_rows, n_cu, 1, 0, s);
 }
 
 moe_status run_experts(const moe_dims* dims, const void* x, const int32_t* offs, const int32_t* sorted,
@@ -296,9 +326,8 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
     const int64_t full_units = (dims->T * dims->k / 256) * (dims->d / 256);
     const int split = full_units >= 2 * n_cu ? 1 : 2;
     float* y_rows2 = split == 2 ? reinterpret_cast<float*>(ws + plan.y_rows2) : nullptr;
-    st = hip_status(moe::launch_down_prefill(static_cast<const bf16_t*>(h), offs, static_cast<const bf16_t*>(w2),
-                                             y_rows, dims->d, dims->f, n_cu, split,
-                                             split == 2 ? y_rows2 - y_rows : 0, s));
+    st = down_prefill(dims, static_cast<const bf16_t*>(h), offs, static_cast<const bf16_t*>(w2), y_rows, n_cu, split,
+                      split == 2 ? y_rows2 - y_rows : 0, s);
     if (st != MOE_OK) return st;
     return hip_status(
         moe::launch_combine(dims->dtype, y_rows, y_rows2, rows, w, y, dims->T, dims->d, n_cu, s));

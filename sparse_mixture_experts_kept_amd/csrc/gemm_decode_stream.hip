@@ -38,6 +38,8 @@ namespace {
 
 constexpr int kBufferFlags = 0x00020000;       // word 3 of a raw buffer resource on gfx9
 constexpr int kNontemporal = 2;                // cache-policy bits of the weight loads
+constexpr int kTailTile = 256;                 // the prefill GEMM's row tile
+constexpr int kTailRows = 32;                  // tails up to this many rows are left to this kernel
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -52,14 +54,14 @@ __device__ __forceinline__ int passes_of(int rows, int rows_per_pass) {
   return (rows + rows_per_pass - 1) / rows_per_pass;
 }
 
-// Work unit u -> expert, weight-row block r, pass.  Expert e contributes
-// per_expert * passes(e) units (none if it has no rows).
-__device__ __forceinline__ void unit_of(const int* o, int per_expert, int rows_per_pass, int u, int* e_out, int* r_out,
+// Work unit u -> expert, weight-row block r, pass.  Expert e (rc[e] rows)
+// contributes per_expert * passes(e) units (none if it has no rows).
+__device__ __forceinline__ void unit_of(const int* rc, int per_expert, int rows_per_pass, int u, int* e_out, int* r_out,
                                         int* p_out) {
   int pre = 0, e_sel = 0, pre_sel = 0;
 #pragma unroll
   for (int e = 0; e < kExperts; ++e) {
-    const int n = per_expert * passes_of(o[e + 1] - o[e], rows_per_pass);
+    const int n = per_expert * passes_of(rc[e], rows_per_pass);
     if (u >= pre && u < pre + n) {
       e_sel = e;
       pre_sel = pre;
@@ -76,6 +78,9 @@ __device__ __forceinline__ void unit_of(const int* o, int per_expert, int rows_p
 // of 16 each, pass), act = x (T rows), out = h (bf16).
 // DOWN: units (expert, 16*NB rows of w2, pass), act = h (n_slots rows),
 // out = y_rows (fp32).
+// TAIL: only the rows of each expert past its last multiple of 256, for
+// the experts whose last 256-row tile holds at most kTailRows of them (the
+// rows the prefill GEMM leaves out; see its deal); otherwise all its rows.
 // A stage covers W bytes (W/2 reduction elements) of each row.  A pass
 // handles up to 16*MAXG of the expert's rows; an expert with more rows
 // streams its weights once per pass.  Token group g of a unit is loaded only
@@ -83,7 +88,7 @@ __device__ __forceinline__ void unit_of(const int* o, int per_expert, int rows_p
 // offset past the end of the buffer, which the buffer hardware answers with
 // zeros and no memory traffic (the instruction count, and so the wait,
 // stays fixed).
-template <bool UP, int W, int NB, int MAXG, int S>
+template <bool UP, bool TAIL, int W, int NB, int MAXG, int S>
 __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __restrict__ act,
                                                               const int32_t* __restrict__ sorted_slots,
                                                               const int32_t* __restrict__ offs,
@@ -111,12 +116,23 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
   const int per_expert = (UP ? f : d) / unit_rows;               // weight-row blocks per expert
   const int KS = K / kStageK;                                    // stages per unit (>= 1)
   const uint32_t act_bytes = static_cast<uint32_t>(act_rows) * static_cast<uint32_t>(K * 2);
-  int o[kExperts + 1];
+  int e_begin[kExperts], e_rows[kExperts];  // each expert's first row and row count here
 #pragma unroll
-  for (int e = 0; e <= kExperts; ++e) o[e] = offs[e];
+  for (int e = 0; e < kExperts; ++e) {
+    const int b = offs[e], c = offs[e + 1] - b;
+    if constexpr (TAIL) {
+      const int full = (c - 1) / kTailTile * kTailTile;  // rows in the expert's full 256-row tiles
+      const bool thin = c > kTailTile && c - full <= kTailRows;
+      e_begin[e] = b + full;
+      e_rows[e] = thin ? c - full : 0;
+    } else {
+      e_begin[e] = b;
+      e_rows[e] = c;
+    }
+  }
   int n_units = 0;
 #pragma unroll
-  for (int e = 0; e < kExperts; ++e) n_units += per_expert * passes_of(o[e + 1] - o[e], kRowsPerPass);
+  for (int e = 0; e < kExperts; ++e) n_units += per_expert * passes_of(e_rows[e], kRowsPerPass);
   const int G = gridDim.x;
   if (static_cast<int>(blockIdx.x) >= n_units) return;
   const int total = (n_units - static_cast<int>(blockIdx.x) + G - 1) / G * KS;
@@ -144,8 +160,8 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
 #define SET_ISSUE_UNIT(U_)                                                                                   \
   {                                                                                                        \
     int e_, r_, p_;                                                                                        \
-    unit_of(o, per_expert, kRowsPerPass, (U_), &e_, &r_, &p_);                                             \
-    const int row_begin = o[e_], rows = o[e_ + 1] - o[e_];                                                 \
+    unit_of(e_rows, per_expert, kRowsPerPass, (U_), &e_, &r_, &p_);                                            \
+    const int row_begin = e_begin[e_], rows = e_rows[e_];                                                    \
     const bf16_t* a0;                                                                                      \
     const bf16_t* b0;                                                                                      \
     if constexpr (UP) {                                                                                    \
@@ -210,7 +226,7 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
   // Compute side.
   int cu = blockIdx.x, cks = 0, cslot = 0;
   int ce, cr, cp;
-  unit_of(o, per_expert, kRowsPerPass, cu, &ce, &cr, &cp);
+  unit_of(e_rows, per_expert, kRowsPerPass, cu, &ce, &cr, &cp);
   f32x4 acc[NB][MAXG];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -245,7 +261,7 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
     if (++cks == KS) {
       // acc[b][g][q]: expert row cp*16*MAXG + 16g + l16, feature 4*lg + q of
       // weight block b (up: blocks < NB/2 gate, the rest up, same features).
-      const int c_begin = o[ce], c_rows = o[ce + 1] - o[ce];
+      const int c_begin = e_begin[ce], c_rows = e_rows[ce];
 #pragma unroll
       for (int g = 0; g < MAXG; ++g) {
         const int m = cp * kRowsPerPass + 16 * g + l16;
@@ -273,7 +289,7 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
         for (int g = 0; g < MAXG; ++g) acc[b][g] = f32x4{0.f, 0.f, 0.f, 0.f};
       cks = 0;
       cu += G;
-      if (cu < n_units) unit_of(o, per_expert, kRowsPerPass, cu, &ce, &cr, &cp);
+      if (cu < n_units) unit_of(e_rows, per_expert, kRowsPerPass, cu, &ce, &cr, &cp);
     }
   }
 }
@@ -283,10 +299,10 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
 #undef LDS_PTR
 
 // GM workgroups (single waves) per CU.
-template <bool UP, int W, int NB, int MAXG, int S, int GM = 2>
+template <bool UP, int W, int NB, int MAXG, int S, int GM = 2, bool TAIL = false>
 hipError_t launch_stream(const bf16_t* act, const int32_t* sorted_slots, const int32_t* offs, const bf16_t* wa,
                          const bf16_t* wb, void* out, int d, int f, int act_rows, int n_cu, hipStream_t s) {
-  hipLaunchKernelGGL((decode_stream_kernel<UP, W, NB, MAXG, S>), dim3(GM * n_cu), dim3(kWave), 0, s, act,
+  hipLaunchKernelGGL((decode_stream_kernel<UP, TAIL, W, NB, MAXG, S>), dim3(GM * n_cu), dim3(kWave), 0, s, act,
                      sorted_slots, offs, wa, wb, out, d, f, act_rows);
   return hipGetLastError();
 }
@@ -318,6 +334,21 @@ hipError_t launch_down_decode_stream(const bf16_t* h, const int32_t* offs, const
   const int n_slots = static_cast<int>(T) * kTopK;
   if (T <= 32) return launch_stream<false, 256, 4, 1, 3>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s);
   return launch_stream<false, 256, 2, 2, 4>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s);
+}
+
+// Tails of the prefill layer (rows of an expert past its last full 256-row
+// tile when at most 32): one pass of two token groups.  x / h as in the
+// prefill launch; n_slots = T * 2.
+hipError_t launch_up_tail_stream(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
+                                 const bf16_t* w3, bf16_t* h, int64_t T, int d, int f, int n_cu, hipStream_t s) {
+  return launch_stream<true, 256, 2, 2, 4, 2, true>(x, sorted_slots, offs, w1, w3, h, d, f, static_cast<int>(T), n_cu,
+                                                     s);
+}
+
+hipError_t launch_down_tail_stream(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int64_t T,
+                                   int d, int f, int n_cu, hipStream_t s) {
+  const int n_slots = static_cast<int>(T) * kTopK;
+  return launch_stream<false, 256, 4, 2, 3, 2, true>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s);
 }
 
 }  // namespace moe

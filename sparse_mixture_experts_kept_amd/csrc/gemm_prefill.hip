@@ -272,7 +272,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
 grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ gather,
                             const int32_t* __restrict__ offs, const bf16_t* __restrict__ B0,
                             const bf16_t* __restrict__ B1, void* __restrict__ Cout, int N, int K,
-                            int64_t split_stride) {
+                            int64_t split_stride, int thin_elsewhere) {
   static_assert(!SWIGLU || SPLITK == 1, "the SwiGLU epilogue needs the full reduction");
   // One LDS object for all slots: A slots 0-1, B slots 2-4.
   __shared__ __align__(16) bf16_t ring[5][kSlotElems];
@@ -283,6 +283,7 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
 
   int n_full, n_thin;
   unit_counts<SPLITK>(offs, n_tiles_n, &n_full, &n_thin);
+  if (thin_elsewhere) n_thin = 0;  // the thin tiles' rows are computed by another kernel
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int slots = gridDim.x / kXcds;
@@ -568,25 +569,25 @@ bool prefill_fits(int64_t T, int d, int f) {
 }
 
 hipError_t launch_up_prefill(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
-                             const bf16_t* w3, bf16_t* h, int d, int f, int n_cu, hipStream_t s) {
+                             const bf16_t* w3, bf16_t* h, int d, int f, int n_cu, bool thin_elsewhere, hipStream_t s) {
   const int grid = (n_cu / kXcds) * kXcds;
   hipLaunchKernelGGL((grouped_gemm_prefill_kernel<true, 1>), dim3(grid), dim3(kThreads), 0, s, x, sorted_slots, offs,
-                     w1, w3, static_cast<void*>(h), f, d, int64_t{0});
+                     w1, w3, static_cast<void*>(h), f, d, int64_t{0}, thin_elsewhere ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_down_prefill(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,
-                               int n_cu, int split, int64_t split_stride, hipStream_t s) {
+                               int n_cu, int split, int64_t split_stride, bool thin_elsewhere, hipStream_t s) {
   const int grid = (n_cu / kXcds) * kXcds;
   // each work unit needs K/split to be a multiple of 64 and at least 2 stages
   if (split == 2 && f % 128 == 0 && f / 2 >= 2 * kBK)
     hipLaunchKernelGGL((grouped_gemm_prefill_kernel<false, 2>), dim3(grid), dim3(kThreads), 0, s, h,
                        static_cast<const int32_t*>(nullptr), offs, w2, static_cast<const bf16_t*>(nullptr),
-                       static_cast<void*>(y_rows), d, f, split_stride);
+                       static_cast<void*>(y_rows), d, f, split_stride, thin_elsewhere ? 1 : 0);
   else
     hipLaunchKernelGGL((grouped_gemm_prefill_kernel<false, 1>), dim3(grid), dim3(kThreads), 0, s, h,
                        static_cast<const int32_t*>(nullptr), offs, w2, static_cast<const bf16_t*>(nullptr),
-                       static_cast<void*>(y_rows), d, f, int64_t{0});
+                       static_cast<void*>(y_rows), d, f, int64_t{0}, thin_elsewhere ? 1 : 0);
   return hipGetLastError();
 }
 
