@@ -19,10 +19,12 @@
 //   so weight loads run up to two stages ahead and token loads one.  Slots
 //   are filled with direct global->LDS loads (global_load_lds_dwordx4, 1 KiB
 //   = 8 rows per instruction, no staging registers).
-// - Per stage and wave: 128 MFMAs in 16 rows of 8; after each row, two
-//   fragment reads (ds_read_b128) and one load, so the loads and reads are
-//   spread evenly under the MFMAs.  One barrier per stage, between its two
-//   k-halves.  All waits are explicit (s_waitcnt vmcnt(N) before the raw
+// - Per stage and wave: 128 MFMAs in 16 rows of 8; each row is cut into
+//   pairs of MFMAs with one load, then one fragment read (ds_read_b128), then
+//   another read between them (MFMA MFMA load MFMA MFMA read MFMA MFMA read
+//   MFMA MFMA), so the memory instructions issue while the MFMAs run (a
+//   load or read burst after each full row left the MFMA pipe idle: 4% on
+//   both projections).  One barrier per stage, between its two k-halves.  All waits are explicit (s_waitcnt vmcnt(N) before the raw
 //   barrier; the compiler adds the LDS-read waits before the MFMAs).
 // - LDS rows are 128 B with the 16-byte chunk index XOR-swizzled by bits 1..3
 //   of the row; the bank-conflict counter reads zero for the 16 rows x 4
@@ -219,20 +221,29 @@ __device__ __forceinline__ int first_thin_from(const int32_t* offs, int n_tiles_
     READ_A(FA, AS, H, (2 * (Q) - 7) & 7);    \
   }
 
-// MFMA row I: the wave's A block I times its 8 B blocks.
-#define MFMA_ROW(FA, FB, I)                                                                               \
-  _Pragma("unroll") for (int j = 0; j < 8; ++j) acc[I][j] =                                               \
+// Element K (0/1) of pair Q.
+#define READ_ONE(FA, FB, AS, BSL, H, Q, K)        \
+  if ((Q) < 4) {                                  \
+    READ_B(FB, BSL, H, (2 * (Q) + (K)) & 7);      \
+  } else {                                        \
+    READ_A(FA, AS, H, (2 * (Q) - 8 + (K)) & 7);   \
+  }
+
+// MFMA row I is the wave's A block I times its 8 B blocks; MFMA_QROW issues
+// pair Q (B blocks 2Q, 2Q+1) of it.
+#define MFMA_QROW(FA, FB, I, Q)                                                                           \
+  _Pragma("unroll") for (int j = 2 * (Q); j < 2 * (Q) + 2; ++j) acc[I][j] =                               \
       __builtin_amdgcn_mfma_f32_16x16x32_bf16(FB[j], FA[I], acc[I][j], 0, 0, 0);
 
 // Stage KT (A in slot KT&1, B in B slot BS = KT%3; BS1, BS2 = (KT+1)%3, (KT+2)%3):
-//   half 0: MFMA rows of set 0; after each row two reads of k-half 1 into
-//           set 1 and (LD) one B load of stage KT+2 into B slot BS2 (free
-//           since the barrier of stage KT-1)
+//   half 0: MFMA rows of set 0; within each row (LD) one B load of stage
+//           KT+2 into B slot BS2 (free since the barrier of stage KT-1) and
+//           two reads of k-half 1 into set 1
 //   wait until only stage KT+2's B loads are in flight; barrier.  All waves
 //           have read stage KT completely, and stage KT+1 has landed.
-//   half 1: MFMA rows of set 1; after each row (RD) two reads of k-half 0 of
-//           stage KT+1 into set 0 and (LD) one A load of stage KT+2 into A
-//           slot KT&1.
+//   half 1: MFMA rows of set 1; within each row (LD) one A load of stage
+//           KT+2 into A slot KT&1 and (RD) two reads of k-half 0 of stage
+//           KT+1 into set 0.
 // Reads are issued one row early at the end of each half so the first MFMAs
 // of the next half find them complete.
 #define STAGE(KT_, BS, BS1, BS2, LD, RD)                                                \
@@ -240,11 +251,22 @@ __device__ __forceinline__ int first_thin_from(const int32_t* offs, int n_tiles_
     const int as_ = (KT_) & 1;                                                          \
     _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                     \
       __builtin_amdgcn_sched_barrier(0);                                                \
-      MFMA_ROW(fa0, fb0, i);                                                            \
+      MFMA_QROW(fa0, fb0, i, 0);                                                        \
       __builtin_amdgcn_sched_barrier(0);                                                \
       if (LD) { LOAD_B((KT_) + 2, i, BS2); }                                            \
-      if (i < 7) { READ_PAIR(fa1, fb1, as_, BS, 1, i); }                                \
-      if (i == 6) { READ_PAIR(fa1, fb1, as_, BS, 1, 7); }                               \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      MFMA_QROW(fa0, fb0, i, 1);                                                        \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      if (i < 7) { READ_ONE(fa1, fb1, as_, BS, 1, i, 0); }                              \
+      if (i == 6) { READ_ONE(fa1, fb1, as_, BS, 1, 7, 0); }                             \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      MFMA_QROW(fa0, fb0, i, 2);                                                        \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      if (i < 7) { READ_ONE(fa1, fb1, as_, BS, 1, i, 1); }                              \
+      if (i == 6) { READ_ONE(fa1, fb1, as_, BS, 1, 7, 1); }                             \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      MFMA_QROW(fa0, fb0, i, 3);                                                        \
+      __builtin_amdgcn_sched_barrier(0);                                                \
     }                                                                                   \
     __builtin_amdgcn_sched_barrier(0);                                                  \
     if (LD)                                                                             \
@@ -254,11 +276,22 @@ __device__ __forceinline__ int first_thin_from(const int32_t* offs, int n_tiles_
     lds_barrier();                                                                      \
     _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                     \
       __builtin_amdgcn_sched_barrier(0);                                                \
-      MFMA_ROW(fa1, fb1, i);                                                            \
+      MFMA_QROW(fa1, fb1, i, 0);                                                        \
       __builtin_amdgcn_sched_barrier(0);                                                \
       if (LD) { LOAD_A((KT_) + 2, i); }                                                 \
-      if ((RD) && i < 7) { READ_PAIR(fa0, fb0, as_ ^ 1, BS1, 0, i); }                   \
-      if ((RD) && i == 6) { READ_PAIR(fa0, fb0, as_ ^ 1, BS1, 0, 7); }                  \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      MFMA_QROW(fa1, fb1, i, 1);                                                        \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      if ((RD) && i < 7) { READ_ONE(fa0, fb0, as_ ^ 1, BS1, 0, i, 0); }                 \
+      if ((RD) && i == 6) { READ_ONE(fa0, fb0, as_ ^ 1, BS1, 0, 7, 0); }                \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      MFMA_QROW(fa1, fb1, i, 2);                                                        \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      if ((RD) && i < 7) { READ_ONE(fa0, fb0, as_ ^ 1, BS1, 0, i, 1); }                 \
+      if ((RD) && i == 6) { READ_ONE(fa0, fb0, as_ ^ 1, BS1, 0, 7, 1); }                \
+      __builtin_amdgcn_sched_barrier(0);                                                \
+      MFMA_QROW(fa1, fb1, i, 3);                                                        \
+      __builtin_amdgcn_sched_barrier(0);                                                \
     }                                                                                   \
     __builtin_amdgcn_sched_barrier(0);                                                  \
   }
@@ -557,7 +590,8 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
 #undef READ_B
 #undef READ_A
 #undef READ_PAIR
-#undef MFMA_ROW
+#undef MFMA_QROW
+#undef READ_ONE
 #undef STAGE
 
 }  // namespace
