@@ -30,8 +30,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s at T=4096 + µs/layer at T=32; % of MFMA/HBM peak"
 # Kernels the roofline entries describe (names as the profiler reports them).
-UP_PREFILL_KERNEL = "moe::grouped_gemm_prefill_kernel<true, 1>"
-UP_DECODE_KERNEL = "moe::decode_stream_kernel<true, 512, 2, 1, 3>"
+# The prefill up projection is two launches: the GEMM over every full
+# 256-row tile and the streaming kernel over the experts' short tails.
+UP_PREFILL_KERNEL = ("moe::grouped_gemm_prefill_kernel<true, 1>", "moe::decode_stream_kernel<true, true, 256, 2, 2, 4>")
+UP_DECODE_KERNEL = "moe::decode_stream_kernel<true, false, 512, 2, 1, 3>"
 
 
 def _log(msg):
@@ -96,21 +98,26 @@ def staged_timing(L, steps, torch, moe, variant):
     return out
 
 
-def measured_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` from the rocprofv3 FETCH_SIZE and
-    WRITE_SIZE passes stored in data/traffic_<workload>.json, or None when
-    none were taken or the kernel's source changed since they were."""
+def measured_traffic(workload, kernels):
+    """HBM bytes per launch of `kernels` (a name or a tuple of names, summed)
+    from the rocprofv3 FETCH_SIZE and WRITE_SIZE passes stored in
+    data/traffic_<workload>.json, or None when none were taken or a kernel's
+    source changed since they were."""
     from sparse_mixture_experts_kept_amd import rocprof_summary
 
     path = os.path.join(ROOT, "sparse_mixture_experts_kept_amd", "data", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
-        rec = json.load(fh)["kernels"].get(kernel)
-    current = rocprof_summary.source_hash(kernel)
-    if rec is None or current is None or rec["source_sha256"] != current:
-        return None
-    return rec["read_bytes"] + rec["write_bytes"]
+        table = json.load(fh)["kernels"]
+    total = 0.0
+    for kernel in ((kernels,) if isinstance(kernels, str) else kernels):
+        rec = table.get(kernel)
+        current = rocprof_summary.source_hash(kernel)
+        if rec is None or current is None or rec["source_sha256"] != current:
+            return None
+        total += rec["read_bytes"] + rec["write_bytes"]
+    return total
 
 
 def cpu_baseline(L, sample_tokens, repeats):
@@ -193,7 +200,8 @@ def main():
                        "routing": "near-uniform (router std 0.02)", "counts": layer.counts.cpu().tolist()},
             "layer_frac_of_bf16_peak": flops / sec / A.PEAK_BF16_FLOPS,
             "stage_ms": stages,
-            "roofline": {"kernel": "grouped_gemm_prefill_kernel<SWIGLU=true> (up projection + SwiGLU)",
+            "roofline": {"kernel": "up projection + SwiGLU: grouped_gemm_prefill_kernel<true, 1> + tail "
+                                   "decode_stream_kernel<true, true, ...>",
                          "bound": "mfma", "achieved": up_flops / up_s / 1e12, "peak": A.PEAK_BF16_FLOPS / 1e12,
                          "unit": "TFLOP/s", "frac": up_flops / up_s / A.PEAK_BF16_FLOPS,
                          "traffic": measured_traffic("prefill", UP_PREFILL_KERNEL),
