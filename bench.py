@@ -49,7 +49,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=4096, help="tokens of the prefill workload the oracle runs")
     p.add_argument("--cpu-repeats", type=int, default=3)
-    p.add_argument("--only", choices=["prefill", "decode", "stack", "all"], default="all")
+    p.add_argument("--only", choices=["prefill", "skewed", "decode", "sweep", "stack", "all"], default="all")
+    p.add_argument("--sweep-steps", type=int, default=10)
     p.add_argument("--stack-steps", type=int, default=3)
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
@@ -214,6 +215,25 @@ def main():
         del layer, L
         torch.cuda.empty_cache()
 
+    if args.only in ("skewed", "all"):
+        _log("prefill_skewed: generating T=4096 layer with Zipf(1.2) slot shares")
+        L = inputs.make_workload("prefill_skewed", device=dev)
+        T = L["dims"]["T"]
+        layer = moe.FFN(L["x"], L["w_gate"], L["w1"], L["w3"], L["w2"], logit_bias=L["logit_bias"])
+        sec = time_layer(layer, args.steps, args.warmup, torch)
+        stages = staged_timing(L, args.steps, torch, moe, moe.VARIANT_AUTO)
+        counts = layer.counts.cpu().tolist()
+        needed, gemm_rows, tail_rows = A.prefill_rows_issued(counts)
+        _log(f"prefill_skewed: {sec * 1e3:.3f} ms/layer, counts {counts}")
+        result["prefill_skewed"] = {
+            "workload": "mixtral-moe-ffn-prefill-zipf", "T": T, "ms_per_layer": sec * 1e3, "tokens_per_s": T / sec,
+            "frac_of_bf16_peak": A.layer_flops(T, d, f, E, k) / sec / A.PEAK_BF16_FLOPS, "stage_ms": stages,
+            "counts": counts, "slot_shares": [c / (T * k) for c in counts],
+            "rows_needed": needed, "rows_issued_gemm": gemm_rows, "rows_issued_tails": tail_rows,
+            "tile_padding_waste": (gemm_rows + tail_rows) / needed - 1.0}
+        del layer, L
+        torch.cuda.empty_cache()
+
     if args.only in ("decode", "all"):
         _log("decode: generating two T=32 layers")
         Ls = [inputs.make_workload("decode", device=dev, seed=s) for s in (2, 1002)]
@@ -248,6 +268,28 @@ def main():
             result.update({"value": T / sec, "unit": "tokens/s", "ms_per_step": sec * 1e3,
                            "config": {"workload": "mixtral-moe-ffn-decode", "T": T, "d": d, "f": f, "E": E,
                                       "k": k}, "roofline": dec["roofline"]})
+
+    if args.only in ("sweep", "all"):
+        # T-sweep over both kernel families on one weight set (2.8 GB, far
+        # beyond the 256 MB Infinity Cache, so every call streams from HBM).
+        _log("sweep: generating a T=8192 layer")
+        L = inputs.make_custom(8192, d, f, dtype="bf16", seed=6, device=dev)
+        rows = []
+        for T in (1, 4, 16, 32, 64, 96, 128, 192, 256, 512, 1024, 2048, 4096, 8192):
+            x = L["x"][:T].contiguous()
+            row = {"T": T}
+            for name, v in (("auto", moe.VARIANT_AUTO), ("decode", moe.VARIANT_DECODE),
+                            ("prefill", moe.VARIANT_PREFILL)):
+                lay = moe.FFN(x, L["w_gate"], L["w1"], L["w3"], L["w2"], variant=v)
+                row[name + "_us"] = time_layer(lay, args.sweep_steps, 2, torch) * 1e6
+                del lay
+            row["tokens_per_s"] = T / (row["auto_us"] * 1e-6)
+            row["frac_of_bf16_peak"] = A.layer_flops(T, d, f, E, k) / (row["auto_us"] * 1e-6) / A.PEAK_BF16_FLOPS
+            _log(f"sweep: {json.dumps({k2: round(v2, 3) if isinstance(v2, float) else v2 for k2, v2 in row.items()})}")
+            rows.append(row)
+        result["t_sweep"] = rows
+        del L
+        torch.cuda.empty_cache()
 
     if args.only in ("stack", "all"):
         from sparse_mixture_experts_kept_amd.stack import MoEStack

@@ -84,3 +84,26 @@ def down_bytes(T: int, d: int, f: int, k: int, n_touched: int, elem_bytes: int =
     """Algorithmic HBM bytes of the down projection: h read once, the
     touched experts' down matrices read once, fp32 y_rows [T*k, d] written."""
     return (T * k * f + n_touched * d * f) * elem_bytes + T * k * d * out_bytes
+
+
+def prefill_rows_issued(counts, tile_rows: int = 256, tail_rows: int = 32, group_rows: int = 16):
+    """Rows the prefill path runs through the matrix cores for these
+    per-expert counts: each expert's rows in m-tiles of ``tile_rows``, except
+    a last tile of at most ``tail_rows`` rows after at least one full tile,
+    which goes to the streaming kernels in token groups of ``group_rows``.
+    Returns (rows needed, rows issued in GEMM tiles, rows issued in tails);
+    the padding waste is issued / needed - 1."""
+    needed = gemm = tails = 0
+    for c in counts:
+        c = int(c)
+        needed += c
+        if c == 0:
+            continue
+        tiles = -(-c // tile_rows)
+        last = c - (tiles - 1) * tile_rows
+        if tiles >= 2 and last <= tail_rows:
+            gemm += (tiles - 1) * tile_rows
+            tails += -(-last // group_rows) * group_rows
+        else:
+            gemm += tiles * tile_rows
+    return needed, gemm, tails

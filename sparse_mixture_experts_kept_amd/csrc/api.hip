@@ -75,20 +75,26 @@ bool tails_streamable(const moe_dims* dims) {
   return dims->T * dims->k * dims->f * 2 < limit && dims->T * dims->d * 2 < limit;
 }
 
+// partials (may be null): a scratch buffer of partial_bytes for the GEMMs'
+// remainder split (the work units past the last whole round of the grid are
+// cut along the reduction and their partial tiles summed by a fixup launch).
 moe_status up_prefill(const moe_dims* dims, const bf16_t* x, const int32_t* offs, const int32_t* sorted,
-                      const bf16_t* w1, const bf16_t* w3, bf16_t* h, int n_cu, hipStream_t s) {
+                      const bf16_t* w1, const bf16_t* w3, bf16_t* h, int n_cu, float* partials,
+                      int64_t partial_bytes, hipStream_t s) {
   const bool tails = kUpTailsStreamed && tails_streamable(dims);
-  moe_status st = hip_status(moe::launch_up_prefill(x, offs, sorted, w1, w3, h, dims->d, dims->f, n_cu, tails, s));
+  moe_status st = hip_status(moe::launch_up_prefill(x, offs, sorted, w1, w3, h, dims->d, dims->f, n_cu, tails,
+                                                    partials, partial_bytes, s));
   if (st != MOE_OK || !tails) return st;
   return hip_status(moe::launch_up_tail_stream(x, offs, sorted, w1, w3, h, dims->T, dims->d, dims->f, n_cu, s));
 }
 
 // split == 2 keeps the tails in the GEMM (their second partial sum must exist).
 moe_status down_prefill(const moe_dims* dims, const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows,
-                        int n_cu, int split, int64_t split_stride, hipStream_t s) {
+                        int n_cu, int split, int64_t split_stride, float* partials, int64_t partial_bytes,
+                        hipStream_t s) {
   const bool tails = split == 1 && tails_streamable(dims);
-  moe_status st = hip_status(
-      moe::launch_down_prefill(h, offs, w2, y_rows, dims->d, dims->f, n_cu, split, split_stride, tails, s));
+  moe_status st = hip_status(moe::launch_down_prefill(h, offs, w2, y_rows, dims->d, dims->f, n_cu, split,
+                                                      split_stride, tails, partials, partial_bytes, s));
   if (st != MOE_OK || !tails) return st;
   return hip_status(moe::launch_down_tail_stream(h, offs, w2, y_rows, dims->T, dims->d, dims->f, n_cu, s));
 }
@@ -141,7 +147,7 @@ moe_status run_up(const moe_dims* dims, const void* x, const int32_t* offs, cons
       return hip_status(moe::launch_up_decode_stream(xb, offs, sorted, w1b, w3b, hb, dims->T, dims->d, dims->f, n_cu, s));
     return hip_status(moe::launch_up_decode(xb, offs, sorted, w1b, w3b, hb, dims->T, dims->d, dims->f, s));
   }
-  return up_prefill(dims, xb, offs, sorted, w1b, w3b, hb, n_cu, s);
+  return up_prefill(dims, xb, offs, sorted, w1b, w3b, hb, n_cu, nullptr, 0, s);
 }
 
 moe_status run_down(const moe_dims* dims, const void* h, const int32_t* offs, const void* w2, float* y_rows,
@@ -159,7 +165,7 @@ moe_status run_down(const moe_dims* dims, const void* h, const int32_t* offs, co
       return hip_status(moe::launch_down_decode_stream(hb, offs, w2b, y_rows, dims->T, dims->d, dims->f, n_cu, s));
     return hip_status(moe::launch_down_decode(hb, offs, w2b, y_rows, dims->T, dims->d, dims->f, 1, 0, s));
   }
-  return down_prefill(dims, hb, offs, w2b, y_rows, n_cu, 1, 0, s);
+  return down_prefill(dims, hb, offs, w2b, y_rows, n_cu, 1, 0, nullptr, 0, s);
 }
 
 moe_status run_experts(const moe_dims* dims, const void* x, const int32_t* offs, const int32_t* sorted,
@@ -321,13 +327,18 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
     int n_cu = 0;
     st = cu_count(&n_cu);
     if (st != MOE_OK) return st;
-    st = run_up(dims, x, offs, sorted, w1, w3, h, s);
+    // The second partial's region is idle until the split down projection
+    // writes it: the remainder splits use it as their partial buffer.
+    float* second = reinterpret_cast<float*>(ws + plan.y_rows2);
+    const int64_t second_bytes = static_cast<int64_t>(plan.total - plan.y_rows2);
+    st = up_prefill(dims, static_cast<const bf16_t*>(x), offs, sorted, static_cast<const bf16_t*>(w1),
+                    static_cast<const bf16_t*>(w3), static_cast<bf16_t*>(h), n_cu, second, second_bytes, s);
     if (st != MOE_OK) return st;
     const int64_t full_units = (dims->T * dims->k / 256) * (dims->d / 256);
     const int split = full_units >= 2 * n_cu ? 1 : 2;
-    float* y_rows2 = split == 2 ? reinterpret_cast<float*>(ws + plan.y_rows2) : nullptr;
+    float* y_rows2 = split == 2 ? second : nullptr;
     st = down_prefill(dims, static_cast<const bf16_t*>(h), offs, static_cast<const bf16_t*>(w2), y_rows, n_cu, split,
-                      split == 2 ? y_rows2 - y_rows : 0, s);
+                      split == 2 ? y_rows2 - y_rows : 0, split == 2 ? nullptr : second, second_bytes, s);
     if (st != MOE_OK) return st;
     return hip_status(
         moe::launch_combine(dims->dtype, y_rows, y_rows2, rows, w, y, dims->T, dims->d, n_cu, s));

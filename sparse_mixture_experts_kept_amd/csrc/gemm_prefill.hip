@@ -176,6 +176,32 @@ __device__ __forceinline__ int thin_unit(const int32_t* offs, int n_tiles_n, int
   return fpre_sel + g * fm_sel * kGroupN * SPLITK + ((fm_sel - 1) * gw + j) * SPLITK + *ks;
 }
 
+// Remainder split.  When the full units do not fill whole rounds of the grid
+// (n_full = R*G + rem with 0 < rem), running the last rem units whole would
+// leave G - rem workgroups idle for a whole unit.  Instead the first R*G units
+// are dealt as usual (R per workgroup) and each of the last rem is cut along
+// the reduction into P = min(G / rem, KT / 2, planes / rem) parts of at least
+// two stages: piece c = p*rem + r (part p of remainder unit r) runs on
+// workgroup c and stores its fp32 partial tile in plane c of the partial
+// buffer; remainder_fixup_kernel then adds the P planes of each unit in part
+// order.  Used only without thin units in the GEMM and without SPLITK.
+struct RemSplit {
+  int n_main, rem, parts;
+};
+__device__ __forceinline__ RemSplit remainder_split(int n_full, int grid, int KT, int planes, bool enabled) {
+  RemSplit r{n_full, 0, 1};
+  if (!enabled || grid <= 0) return r;
+  const int R = n_full / grid, rem = n_full - R * grid;
+  if (rem == 0) return r;
+  const int P = min(min(grid / rem, KT / 2), planes / rem);
+  if (P < 2) return r;
+  r.n_main = R * grid;
+  r.rem = rem;
+  r.parts = P;
+  return r;
+}
+constexpr int kPlaneElems = kBM * kBN;  // one fp32 partial tile: [256 tile rows][256 B-tile rows]
+
 // First thin unit whose anchor is at or past full unit u (anchors rise with t).
 template <int SPLITK>
 __device__ __forceinline__ int first_thin_from(const int32_t* offs, int n_tiles_n, int n_thin, int u) {
@@ -305,7 +331,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
 grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ gather,
                             const int32_t* __restrict__ offs, const bf16_t* __restrict__ B0,
                             const bf16_t* __restrict__ B1, void* __restrict__ Cout, int N, int K,
-                            int64_t split_stride, int thin_elsewhere) {
+                            int64_t split_stride, int thin_elsewhere, float* __restrict__ partials,
+                            int planes) {
   static_assert(!SWIGLU || SPLITK == 1, "the SwiGLU epilogue needs the full reduction");
   // One LDS object for all slots: A slots 0-1, B slots 2-4.
   __shared__ __align__(16) bf16_t ring[5][kSlotElems];
@@ -317,12 +344,15 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
   int n_full, n_thin;
   unit_counts<SPLITK>(offs, n_tiles_n, &n_full, &n_thin);
   if (thin_elsewhere) n_thin = 0;  // the thin tiles' rows are computed by another kernel
+  const int k_part = K / SPLITK;
+  const int KT = k_part / kBK;  // >= 2 (the host guarantees it)
+  const RemSplit rs = remainder_split(n_full, gridDim.x, KT, planes, partials != nullptr && SPLITK == 1 && n_thin == 0);
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int slots = gridDim.x / kXcds;
-  const int per = (n_full + kXcds - 1) / kXcds;
-  const int fbeg = min(xcd * per, n_full);
-  const int fend = min(fbeg + per, n_full);
+  const int per = (rs.n_main + kXcds - 1) / kXcds;
+  const int fbeg = min(xcd * per, rs.n_main);
+  const int fend = min(fbeg + per, rs.n_main);
   const int tbeg = first_thin_from<SPLITK>(offs, n_tiles_n, n_thin, fbeg);
   const int tend = first_thin_from<SPLITK>(offs, n_tiles_n, n_thin, fend);
 
@@ -336,15 +366,17 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
   const int ld_row = lane / 8, pc = lane % 8;
   const int lc_even = (pc ^ (ld_row >> 1)) * 8;
   const int lc_odd = lc_even ^ 32;
-  const int k_part = K / SPLITK;
-  const int KT = k_part / kBK;  // >= 2 (the host guarantees it)
 
   // This workgroup's full units fbeg + slot + i*slots and thin units
   // tbeg + (slot + slots/2) % slots + i*slots, merged in anchor order.
   int u = fbeg + slot;
   int t = tbeg + (slot + slots / 2) % slots;
-  while (u < fend || t < tend) {
+  // ... then its piece of a remainder unit, if any.
+  bool piece = static_cast<int>(blockIdx.x) < rs.rem * rs.parts;
+  while (u < fend || t < tend || piece) {
     int e, mt, nt, ks;
+    int kbeg = 0, kt_n = KT;  // this unit's stages: [kbeg, kbeg + kt_n) of its part
+    float* plane = nullptr;   // partial-tile destination of a piece
     bool take_thin = false;
     if (t < tend) {
       int te, tmt, tnt, tks;
@@ -359,9 +391,17 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
     }
     if (take_thin) {
       t += slots;
-    } else {
+    } else if (u < fend) {
       full_unit<SPLITK>(offs, n_tiles_n, u, &e, &mt, &nt, &ks);
       u += slots;
+    } else {
+      const int c = blockIdx.x;
+      const int r = c % rs.rem, p = c / rs.rem;
+      full_unit<SPLITK>(offs, n_tiles_n, rs.n_main + r, &e, &mt, &nt, &ks);
+      kbeg = p * KT / rs.parts;
+      kt_n = (p + 1) * KT / rs.parts - kbeg;
+      plane = partials + static_cast<int64_t>(c) * kPlaneElems;
+      piece = false;
     }
     const int row_begin = offs[e];
     const int rows = offs[e + 1] - row_begin;
@@ -380,19 +420,19 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
       for (int j = 0; j < 8; ++j)  // x is below 4 GiB (the host checks)
         a_off[j] = ((static_cast<uint32_t>(slot_id[j]) / kTopK) * static_cast<uint32_t>(K) +
                     ((j & 1) ? lc_odd : lc_even)) * 2u;
-      a_base = A;
+      a_base = A + kbeg * kBK;
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
         a_off[j] = (static_cast<uint32_t>(min(wave * 64 + j * 8 + ld_row, rows - 1 - m0)) * static_cast<uint32_t>(K) +
                     ((j & 1) ? lc_odd : lc_even)) * 2u;
-      a_base = A + static_cast<int64_t>(row_begin + m0) * K + ks * k_part;
+      a_base = A + static_cast<int64_t>(row_begin + m0) * K + ks * k_part + kbeg * kBK;
     }
     // B: a wave's 64 weight rows are contiguous and all in range or all past
     // N (N is a multiple of 128), so clamping the block keeps them in range.
     const bf16_t* bsrc = SWIGLU ? ((wave & 1) ? B1 : B0) : B0;
     const int brow0 = min(SWIGLU ? n0 + (wave >> 1) * 64 : n0 + wave * 64, N - 64);
-    const bf16_t* b_base = bsrc + (static_cast<int64_t>(e) * N + brow0) * K + ks * k_part;
+    const bf16_t* b_base = bsrc + (static_cast<int64_t>(e) * N + brow0) * K + ks * k_part + kbeg * kBK;
     uint32_t b_off[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -447,10 +487,10 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) tacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int st = 0; st < 3 && st < KT; ++st) LOAD_THIN(st);
-      for (int kt = 0; kt < KT; ++kt) {
+      for (int st = 0; st < 3 && st < kt_n; ++st) LOAD_THIN(st);
+      for (int kt = 0; kt < kt_n; ++kt) {
         // stages kt+1 and kt+2 (if any) may stay in flight
-        const int after = min(2, KT - 1 - kt);
+        const int after = min(2, kt_n - 1 - kt);
         if (after == 2)
           __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kThinLoads));
         else if (after == 1)
@@ -458,7 +498,7 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
         else
           __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         lds_barrier();  // stage kt landed for all waves; stage kt-1 fully read
-        if (kt + 3 < KT) LOAD_THIN(kt + 3);  // into the slots of stage kt-1
+        if (kt + 3 < kt_n) LOAD_THIN(kt + 3);  // into the slots of stage kt-1
         bf16x8 ta[2][2], tb[2][4];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
@@ -484,16 +524,33 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
       lds_barrier();
       // Epilogue: tacc[i][j][q] is row m0 + i*16 + l16, B-tile row tb_row[j]'s
       // block at 4*lg + q.
+      // (the lane index re-read: address terms formed here, as in the main epilogue)
+      int elane = lane;
+      asm volatile("" : "+v"(elane));
+      const int el16 = elane % 16, elg = elane / 16;
+      if (plane) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int brow = SWIGLU ? (wave >> 1) * 128 + (j >= 2 ? 64 : 0) + (wave & 1) * 32 + (j & 1) * 16
+                                    : wave * 64 + j * 16;
+            const f32x4 v = tacc[i][j];
+            *reinterpret_cast<float4*>(plane + (i * 16 + el16) * kBN + brow + 4 * elg) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          }
+        continue;
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int m = m0 + i * 16 + l16;
+        const int m = m0 + i * 16 + el16;
         if (m >= rows) continue;
         const int64_t orow = row_begin + m;
         if constexpr (SWIGLU) {
           bf16_t* C = static_cast<bf16_t*>(Cout);
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
-            const int n = n0 + (wave >> 1) * 64 + (wave & 1) * 32 + j * 16 + 4 * lg;
+            const int n = n0 + (wave >> 1) * 64 + (wave & 1) * 32 + j * 16 + 4 * elg;
             const f32x4 g = tacc[i][j];
             const f32x4 u = tacc[i][j + 2];
             uint2 p;
@@ -505,7 +562,7 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
           float* C = static_cast<float*>(Cout) + ks * split_stride;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int n = n0 + wave * 64 + j * 16 + 4 * lg;
+            const int n = n0 + wave * 64 + j * 16 + 4 * elg;
             if (n >= N) continue;
             const f32x4 v = tacc[i][j];
             *reinterpret_cast<float4*>(C + orow * N + n) = make_float4(v[0], v[1], v[2], v[3]);
@@ -535,7 +592,7 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
 #pragma unroll
     for (int q = 0; q < 8; ++q) { READ_PAIR(fa0, fb0, 0, 0, 0, q); }
     int kt = 0, bs = 0;
-    for (; kt < KT - 2; ++kt) {
+    for (; kt < kt_n - 2; ++kt) {
       const int bs1 = bs == 2 ? 0 : bs + 1;
       const int bs2 = bs1 == 2 ? 0 : bs1 + 1;
       STAGE(kt, bs, bs1, bs2, true, true);
@@ -553,36 +610,118 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
 
     // Epilogue.  acc[i][j][q]: output row m0 + wm*128 + i*16 + l16, B-tile
     // row wn*128 + j*16 + 4*lg + q (the B rows were MFMA src0).
+    // A piece stores its raw partial tile instead (plane row = tile row,
+    // plane column = B-tile row).  The lane index is re-read here so that
+    // the epilogue's per-lane address terms are formed per tile, not kept
+    // live across the main loop.
+    int elane = lane;
+    asm volatile("" : "+v"(elane));
+    const int el16 = elane % 16, elg = elane / 16;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      const int m = m0 + wm * 128 + i * 16 + l16;
+      const int m = m0 + wm * 128 + i * 16 + el16;
       if (m >= rows) continue;
       const int64_t orow = row_begin + m;
+      float* prow = plane + (m - m0) * kBN + wn * 128 + 4 * elg;  // used only by a piece
       if constexpr (SWIGLU) {
         bf16_t* C = static_cast<bf16_t*>(Cout);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int n = n0 + wn * 64 + j * 16 + 4 * lg;
+          const int n = n0 + wn * 64 + j * 16 + 4 * elg;
           const f32x4 g = acc[i][j];
           const f32x4 u = acc[i][j + 4];
-          uint2 p;
-          p.x = pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
-          p.y = pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
-          *reinterpret_cast<uint2*>(C + orow * N + n) = p;
+          if (plane) {
+            *reinterpret_cast<float4*>(prow + j * 16) = make_float4(g[0], g[1], g[2], g[3]);
+            *reinterpret_cast<float4*>(prow + (j + 4) * 16) = make_float4(u[0], u[1], u[2], u[3]);
+          } else {
+            uint2 p;
+            p.x = pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
+            p.y = pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
+            *reinterpret_cast<uint2*>(C + orow * N + n) = p;
+          }
         }
       } else {
         float* C = static_cast<float*>(Cout) + ks * split_stride;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int n = n0 + wn * 128 + j * 16 + 4 * lg;
+          const int n = n0 + wn * 128 + j * 16 + 4 * elg;
           if (n >= N) continue;
           const f32x4 v = acc[i][j];
-          *reinterpret_cast<float4*>(C + orow * N + n) = make_float4(v[0], v[1], v[2], v[3]);
+          *reinterpret_cast<float4*>(plane ? prow + j * 16 : C + orow * N + n) = make_float4(v[0], v[1], v[2], v[3]);
         }
       }
     }
   }
+}
+
+// Adds the partial tiles of the remainder units (see remainder_split) in
+// part order and applies the epilogue the GEMM applies to a whole unit:
+// SiLU(gate) * up and one bf16 rounding (up projection) or an fp32 store
+// (down projection).  The split is recomputed from the offsets with the
+// GEMM's grid size, stage count and plane count.  One wave per output row.
+template <bool SWIGLU>
+__global__ void __launch_bounds__(kThreads) remainder_fixup_kernel(const int32_t* __restrict__ offs,
+                                                                   const float* __restrict__ partials,
+                                                                   void* __restrict__ Cout, int N, int K,
+                                                                   int gemm_grid, int planes, int thin_elsewhere) {
+  constexpr int TN = SWIGLU ? kBN / 2 : kBN;
+  constexpr int kWavesPerBlock = kThreads / kWave;
+  const int n_tiles_n = (N + TN - 1) / TN;
+  int n_full, n_thin;
+  unit_counts<1>(offs, n_tiles_n, &n_full, &n_thin);
+  if (thin_elsewhere) n_thin = 0;
+  const RemSplit rs = remainder_split(n_full, gemm_grid, K / kBK, planes, n_thin == 0);
+  if (rs.rem == 0) return;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int64_t part_stride = static_cast<int64_t>(rs.rem) * kPlaneElems;
+  for (int item = blockIdx.x * kWavesPerBlock + wave; item < rs.rem * kBM; item += gridDim.x * kWavesPerBlock) {
+    const int r = item / kBM, m = item % kBM;
+    int e, mt, nt, ks;
+    full_unit<1>(offs, n_tiles_n, rs.n_main + r, &e, &mt, &nt, &ks);
+    const int row_begin = offs[e];
+    const int rows = offs[e + 1] - row_begin;
+    const int m0 = mt * kBM;
+    if (m0 + m >= rows) continue;
+    const int n0 = nt * TN;
+    const int64_t orow = row_begin + m0 + m;
+    const float* src = partials + static_cast<int64_t>(r) * kPlaneElems + m * kBN;
+    if constexpr (SWIGLU) {
+      // output columns n0 + c, c + 1: gate sums at B-tile row (c/64)*128 + c%64, up sums 64 rows on
+      const int c = 2 * lane;
+      const int b = (c / 64) * 128 + c % 64;
+      float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
+      for (int p = 0; p < rs.parts; ++p) {
+        const float2 g = *reinterpret_cast<const float2*>(src + p * part_stride + b);
+        const float2 u = *reinterpret_cast<const float2*>(src + p * part_stride + b + 64);
+        g0 += g.x;
+        g1 += g.y;
+        u0 += u.x;
+        u1 += u.y;
+      }
+      bf16_t* C = static_cast<bf16_t*>(Cout);
+      *reinterpret_cast<uint32_t*>(C + orow * N + n0 + c) = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);
+    } else {
+      const int c = 4 * lane;
+      if (n0 + c >= N) continue;
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int p = 0; p < rs.parts; ++p) {
+        const float4 v = *reinterpret_cast<const float4*>(src + p * part_stride + c);
+        a.x += v.x;
+        a.y += v.y;
+        a.z += v.z;
+        a.w += v.w;
+      }
+      *reinterpret_cast<float4*>(static_cast<float*>(Cout) + orow * N + n0 + c) = a;
+    }
+  }
+}
+
+// Planes of the partial buffer (0 when there is none).
+int plane_count(const float* partials, int64_t partial_bytes) {
+  if (!partials) return 0;
+  const int64_t n = partial_bytes / (static_cast<int64_t>(kPlaneElems) * 4);
+  return n > (1 << 20) ? (1 << 20) : static_cast<int>(n);
 }
 
 #undef LOAD_A
@@ -603,25 +742,41 @@ bool prefill_fits(int64_t T, int d, int f) {
 }
 
 hipError_t launch_up_prefill(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
-                             const bf16_t* w3, bf16_t* h, int d, int f, int n_cu, bool thin_elsewhere, hipStream_t s) {
+                             const bf16_t* w3, bf16_t* h, int d, int f, int n_cu, bool thin_elsewhere,
+                             float* partials, int64_t partial_bytes, hipStream_t s) {
   const int grid = (n_cu / kXcds) * kXcds;
+  const int planes = plane_count(partials, partial_bytes);
+  float* part = planes >= 2 ? partials : nullptr;
   hipLaunchKernelGGL((grouped_gemm_prefill_kernel<true, 1>), dim3(grid), dim3(kThreads), 0, s, x, sorted_slots, offs,
-                     w1, w3, static_cast<void*>(h), f, d, int64_t{0}, thin_elsewhere ? 1 : 0);
+                     w1, w3, static_cast<void*>(h), f, d, int64_t{0}, thin_elsewhere ? 1 : 0, part, planes);
+  if (part)
+    hipLaunchKernelGGL((remainder_fixup_kernel<true>), dim3(2 * grid), dim3(kThreads), 0, s, offs,
+                       static_cast<const float*>(part), static_cast<void*>(h), f, d, grid, planes,
+                       thin_elsewhere ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_down_prefill(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,
-                               int n_cu, int split, int64_t split_stride, bool thin_elsewhere, hipStream_t s) {
+                               int n_cu, int split, int64_t split_stride, bool thin_elsewhere, float* partials,
+                               int64_t partial_bytes, hipStream_t s) {
   const int grid = (n_cu / kXcds) * kXcds;
   // each work unit needs K/split to be a multiple of 64 and at least 2 stages
-  if (split == 2 && f % 128 == 0 && f / 2 >= 2 * kBK)
+  if (split == 2 && f % 128 == 0 && f / 2 >= 2 * kBK) {
     hipLaunchKernelGGL((grouped_gemm_prefill_kernel<false, 2>), dim3(grid), dim3(kThreads), 0, s, h,
                        static_cast<const int32_t*>(nullptr), offs, w2, static_cast<const bf16_t*>(nullptr),
-                       static_cast<void*>(y_rows), d, f, split_stride, thin_elsewhere ? 1 : 0);
-  else
+                       static_cast<void*>(y_rows), d, f, split_stride, thin_elsewhere ? 1 : 0,
+                       static_cast<float*>(nullptr), 0);
+  } else {
+    const int planes = plane_count(partials, partial_bytes);
+    float* part = planes >= 2 ? partials : nullptr;
     hipLaunchKernelGGL((grouped_gemm_prefill_kernel<false, 1>), dim3(grid), dim3(kThreads), 0, s, h,
                        static_cast<const int32_t*>(nullptr), offs, w2, static_cast<const bf16_t*>(nullptr),
-                       static_cast<void*>(y_rows), d, f, int64_t{0}, thin_elsewhere ? 1 : 0);
+                       static_cast<void*>(y_rows), d, f, int64_t{0}, thin_elsewhere ? 1 : 0, part, planes);
+    if (part)
+      hipLaunchKernelGGL((remainder_fixup_kernel<false>), dim3(2 * grid), dim3(kThreads), 0, s, offs,
+                         static_cast<const float*>(part), static_cast<void*>(y_rows), d, f, grid, planes,
+                         thin_elsewhere ? 1 : 0);
+  }
   return hipGetLastError();
 }
 

@@ -30,12 +30,17 @@ bool prefill_fits(int64_t T, int d, int f);
 // thin_elsewhere: skip the rows of each expert's last 256-row tile when it
 // holds at most 32 of them and the expert has more than 256 rows (the tail
 // launchers below compute exactly those rows).
+// partials (may be null): an fp32 buffer of partial_bytes for the remainder
+// split of the work units (the up projection's, then the down projection's:
+// both launches are stream-ordered); it adds a fixup launch.
 hipError_t launch_up_prefill(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
-                             const bf16_t* w3, bf16_t* h, int d, int f, int n_cu, bool thin_elsewhere, hipStream_t s);
+                             const bf16_t* w3, bf16_t* h, int d, int f, int n_cu, bool thin_elsewhere,
+                             float* partials, int64_t partial_bytes, hipStream_t s);
 // split == 2: two partial sums over the two halves of f, the second at
 // y_rows + split_stride; otherwise one full sum in y_rows.
 hipError_t launch_down_prefill(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,
-                               int n_cu, int split, int64_t split_stride, bool thin_elsewhere, hipStream_t s);
+                               int n_cu, int split, int64_t split_stride, bool thin_elsewhere, float* partials,
+                               int64_t partial_bytes, hipStream_t s);
 // The rows the prefill launches skip with thin_elsewhere, on the streaming
 // kernels (full reduction: with split == 2 the tail rows' second partial
 // must be zero).  Need 2T * f * 2 and T * d * 2 below 2^31.

@@ -38,3 +38,18 @@ def test_layer_flops_and_bytes():
     # up + down per slot equals the per-token expert flops divided by k
     assert k * (A.up_flops_per_slot(d, f) + A.down_flops_per_slot(d, f)) == A.expert_flops_per_token(d, f, k)
     assert A.decode_layer_bytes(32, d, f, E, k, 8) == 2_818_572_288 + 8 * 4096 * 2 + 2 * 32 * 4096 * 2
+
+
+def test_prefill_rows_issued():
+    # one expert per case: a full tile, a ragged tile, a streamed tail, and a
+    # small expert that still takes a whole tile
+    assert A.prefill_rows_issued([256]) == (256, 256, 0)
+    assert A.prefill_rows_issued([300]) == (300, 512, 0)
+    assert A.prefill_rows_issued([1025]) == (1025, 1024, 16)
+    assert A.prefill_rows_issued([256 + 32]) == (288, 256, 32)
+    assert A.prefill_rows_issued([256 + 33]) == (289, 512, 0)
+    assert A.prefill_rows_issued([20]) == (20, 256, 0)
+    assert A.prefill_rows_issued([0, 0]) == (0, 0, 0)
+    counts = [1024, 300, 1025, 20]
+    n, g, t = A.prefill_rows_issued(counts)
+    assert n == sum(counts) and g == 1024 + 512 + 1024 + 256 and t == 16

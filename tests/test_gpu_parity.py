@@ -341,6 +341,62 @@ def test_errors_with_real_tensors():
     assert y0.shape == (0, 256)
 
 
+# --------------------------------------------------------------------------- remainder split of the prefill GEMMs
+
+
+def _unit_plan(counts, T, d, f, n_cu, k=2):
+    """The prefill GEMMs' work-unit rules restated (test helper, to assert
+    which cases a layer exercises): 256-row m-tiles per expert, a last tile of
+    at most 32 rows after a full one goes to the streaming kernels, n-tiles of
+    128 output columns (up) or 256 (down), 64-deep stages.  Units past the
+    last whole round of the grid are split in P parts when P >= 2."""
+    G = (n_cu // 8) * 8
+    planes = (T * k * d * 4) // (256 * 256 * 4)
+    down_unsplit = (T * k // 256) * (d // 256) >= 2 * n_cu
+    out = {}
+    for name, N, K, TN in (("up", f, d, 128), ("down", d, f, 256)):
+        ntn = -(-N // TN)
+        n_full = 0
+        for c in counts:
+            if c == 0:
+                continue
+            mts = -(-c // 256)
+            thin = mts >= 2 and c - (mts - 1) * 256 <= 32
+            n_full += (mts - (1 if thin else 0)) * ntn
+        R, rem = divmod(n_full, G)
+        P = min(G // rem, (K // 64) // 2, planes // rem) if rem else 1
+        if P < 2 or (name == "down" and not down_unsplit):
+            P, rem = 1, 0
+        out[name] = dict(n_full=n_full, rounds=R, rem=rem, parts=P)
+    return out
+
+
+@pytest.mark.parametrize("T,d,f,seed,bias7", [(4200, 4096, 256, 1, None), (4200, 4096, 1024, 2, None),
+                                             (4200, 4096, 256, 5, -3.0)])
+def test_prefill_remainder_split(T, d, f, seed, bias7):
+    # Layers whose work units leave a partial round of the grid: the units
+    # past the last whole round are cut along the reduction and summed by the
+    # fixup launch.  f=256: every up unit is split (no whole round); f=1024:
+    # one whole round plus a split remainder in both projections; bias7
+    # leaves expert 7 (the last in unit order) 14 rows, so its one m-tile
+    # takes the thin path inside the split.  Inputs are drawn on the CPU so
+    # the routing is fixed independently of the device.
+    layer = inputs.make_custom(T, d, f, seed=seed, device="cpu")
+    if bias7 is not None:
+        layer["logit_bias"] = torch.tensor([0.0] * 7 + [bias7], dtype=torch.float32)
+    layer = {k2: (v.cuda() if torch.is_tensor(v) else v) for k2, v in layer.items()}
+    out = run_and_check(layer, variant=moe.VARIANT_PREFILL)
+    counts = out["counts"].cpu().tolist()
+    plan = _unit_plan(counts, T, d, f, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert plan["up"]["parts"] >= 2 and plan["down"]["parts"] >= 2, (counts, plan)
+    if bias7 is not None:
+        assert 0 < counts[7] <= 32, counts
+    # deterministic: a second run gives the same bits
+    y2 = moe.ffn_forward(layer["x"], layer["w_gate"], layer["w1"], layer["w3"], layer["w2"],
+                         logit_bias=layer.get("logit_bias"), variant=moe.VARIANT_PREFILL)
+    assert torch.equal(out["y"], y2)
+
+
 # --------------------------------------------------------------------------- full Mixtral-sized layers (sampled)
 
 
