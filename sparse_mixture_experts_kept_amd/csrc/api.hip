@@ -2,6 +2,7 @@
 // carve-up, kernel-family choice and launch sequencing on the caller's
 // stream.  The declarations, with the passages of the pages each entry point
 // realises, are in include/moe.h.
+#include <algorithm>
 #include <mutex>
 
 #include "../../include/moe.h"
@@ -89,14 +90,28 @@ moe_status up_prefill(const moe_dims* dims, const bf16_t* x, const int32_t* offs
 }
 
 // split == 2 keeps the tails in the GEMM (their second partial sum must exist).
+// With partials (split == 1 only): the first n_cu planes of 256 x 256 fp32
+// serve the GEMM's remainder split, the rest the split tails; one fixup
+// launch after the tails completes both.
 moe_status down_prefill(const moe_dims* dims, const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows,
                         int n_cu, int split, int64_t split_stride, float* partials, int64_t partial_bytes,
                         hipStream_t s) {
   const bool tails = split == 1 && tails_streamable(dims);
+  const int64_t plane_bytes = std::min<int64_t>(partial_bytes, int64_t{n_cu} * 256 * 256 * 4);
+  float* tail_part = partials && partial_bytes > plane_bytes ? partials + plane_bytes / 4 : nullptr;
+  const int64_t tail_bytes = tail_part ? partial_bytes - plane_bytes : 0;
   moe_status st = hip_status(moe::launch_down_prefill(h, offs, w2, y_rows, dims->d, dims->f, n_cu, split,
-                                                      split_stride, tails, partials, partial_bytes, s));
-  if (st != MOE_OK || !tails) return st;
-  return hip_status(moe::launch_down_tail_stream(h, offs, w2, y_rows, dims->T, dims->d, dims->f, n_cu, s));
+                                                      split_stride, tails, partials, plane_bytes, s));
+  if (st != MOE_OK) return st;
+  if (tails) {
+    st = hip_status(moe::launch_down_tail_stream(h, offs, w2, y_rows, dims->T, dims->d, dims->f, n_cu, tail_part,
+                                                 tail_bytes, s));
+    if (st != MOE_OK) return st;
+  }
+  if (!partials || split != 1) return MOE_OK;
+  const bool split_tails = tails && moe::tail_part_capacity(tail_part, tail_bytes, dims->d) >= 2;
+  return hip_status(moe::launch_down_prefill_fixup(offs, partials, plane_bytes, split_tails ? tail_part : nullptr,
+                                                   y_rows, dims->d, dims->f, n_cu, tails, s));
 }
 
 size_t align256(size_t v) { return (v + 255) & ~size_t{255}; }

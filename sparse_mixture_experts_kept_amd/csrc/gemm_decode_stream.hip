@@ -40,6 +40,7 @@ constexpr int kBufferFlags = 0x00020000;       // word 3 of a raw buffer resourc
 constexpr int kNontemporal = 2;                // cache-policy bits of the weight loads
 constexpr int kTailTile = 256;                 // the prefill GEMM's row tile
 constexpr int kTailRows = 32;                  // tails up to this many rows are left to this kernel
+static_assert(kTailRows == kTailPartRows, "split tail partials hold every tail row");
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -88,13 +89,21 @@ __device__ __forceinline__ void unit_of(const int* rc, int per_expert, int rows_
 // offset past the end of the buffer, which the buffer hardware answers with
 // zeros and no memory traffic (the instruction count, and so the wait,
 // stays fixed).
+// Down-projection tails with few units for the grid (one or two experts
+// with tails leave most waves idle) also split the reduction: P parts
+// (doubling while the units still fit the grid, at most kMaxTailParts and
+// tail_pcap, dividing the stage count), unit u = part u / U of base unit
+// u % U.  With P > 1 each part stores fp32 partial sums to tail_part (layout
+// in launch.hpp) and a later launch adds them; workgroup 0 records P in the
+// buffer's header either way.
 template <bool UP, bool TAIL, int W, int NB, int MAXG, int S>
 __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __restrict__ act,
                                                               const int32_t* __restrict__ sorted_slots,
                                                               const int32_t* __restrict__ offs,
                                                               const bf16_t* __restrict__ wa,
                                                               const bf16_t* __restrict__ wb, void* __restrict__ out,
-                                                              int d, int f, int act_rows) {
+                                                              int d, int f, int act_rows, float* __restrict__ tail_part,
+                                                              int tail_pcap) {
   constexpr int kStageK = W / 2;                  // reduction elements per stage
   constexpr int kChunks = W / 16;                 // 16-byte chunks per LDS row
   constexpr int kBlockElems = 16 * kStageK;       // one 16-row block of a stage
@@ -134,8 +143,18 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
 #pragma unroll
   for (int e = 0; e < kExperts; ++e) n_units += per_expert * passes_of(e_rows[e], kRowsPerPass);
   const int G = gridDim.x;
-  if (static_cast<int>(blockIdx.x) >= n_units) return;
-  const int total = (n_units - static_cast<int>(blockIdx.x) + G - 1) / G * KS;
+  constexpr bool kSplit = TAIL && !UP;  // only these instantiations split the reduction
+  int P = 1;  // reduction parts
+  if constexpr (kSplit) {
+    if (tail_part) {
+      while (2 * P <= kMaxTailParts && 2 * P <= tail_pcap && n_units * 2 * P <= G && KS % (2 * P) == 0) P *= 2;
+      if (blockIdx.x == 0 && lane == 0) *reinterpret_cast<int*>(tail_part) = P;
+    }
+  }
+  const int n_total = n_units * P;
+  const int KSp = KS / P;  // stages per unit
+  if (static_cast<int>(blockIdx.x) >= n_total) return;
+  const int total = (n_total - static_cast<int>(blockIdx.x) + G - 1) / G * KSp;
 
   // Loads: instruction i of a 16-row block puts rows kRowsPerLoad*i .. +
   // kRowsPerLoad-1 into 1 KiB of LDS, this lane's 16 bytes at physical
@@ -150,7 +169,7 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
   }
 
   // Issue side: unit, stage within it, buffer resources and token offsets.
-  int iu = blockIdx.x, iks = 0;
+  int iu = blockIdx.x, iks = 0, ikbase = 0;
   __amdgpu_buffer_rsrc_t ra, rb;
   // (Fixed extents: an array sized by a template parameter and passed to
   // the buffer-load builtin keeps clang from emitting the launch stub.)
@@ -160,7 +179,9 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
 #define SET_ISSUE_UNIT(U_)                                                                                   \
   {                                                                                                        \
     int e_, r_, p_;                                                                                        \
-    unit_of(e_rows, per_expert, kRowsPerPass, (U_), &e_, &r_, &p_);                                            \
+    const int part_ = kSplit ? (U_) / n_units : 0;                                                         \
+    ikbase = part_ * KSp;                                                                                  \
+    unit_of(e_rows, per_expert, kRowsPerPass, (U_) - part_ * n_units, &e_, &r_, &p_);                      \
     const int row_begin = e_begin[e_], rows = e_rows[e_];                                                    \
     const bf16_t* a0;                                                                                      \
     const bf16_t* b0;                                                                                      \
@@ -198,7 +219,7 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
 #define ISSUE(SLOT_)                                                                                       \
   {                                                                                                        \
     bf16_t* st_ = ring[SLOT_];                                                                             \
-    const int so = iks * W;                                                                                \
+    const int so = (ikbase + iks) * W;                                                                     \
     _Pragma("unroll") for (int b = 0; b < NB; ++b) {                                                       \
       const int bo = (UP ? b % (NB / 2) : b) * 16 * K * 2; /* block's first row */                         \
       _Pragma("unroll") for (int i = 0; i < kLoadsPerBlock; ++i)                                           \
@@ -209,10 +230,10 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
     _Pragma("unroll") for (int g = 0; g < MAXG; ++g) _Pragma("unroll") for (int q = 0; q < kLoadsPerBlock; ++q) \
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rt, LDS_PTR(st_ + (NB + g) * kBlockElems + q * 512), 16,    \
                                                t_off[g][q], so, 0, 0);                                     \
-    if (++iks == KS) {                                                                                     \
+    if (++iks == KSp) {                                                                                    \
       iks = 0;                                                                                             \
       iu += G;                                                                                             \
-      if (iu < n_units) SET_ISSUE_UNIT(iu);                                                                \
+      if (iu < n_total) SET_ISSUE_UNIT(iu);                                                                \
     }                                                                                                      \
   }
 
@@ -225,8 +246,8 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
 
   // Compute side.
   int cu = blockIdx.x, cks = 0, cslot = 0;
-  int ce, cr, cp;
-  unit_of(e_rows, per_expert, kRowsPerPass, cu, &ce, &cr, &cp);
+  int ce, cr, cp, cpart = kSplit ? cu / n_units : 0;
+  unit_of(e_rows, per_expert, kRowsPerPass, cu - cpart * n_units, &ce, &cr, &cp);
   f32x4 acc[NB][MAXG];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -258,7 +279,7 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
       }
     }
     cslot = cslot == S - 1 ? 0 : cslot + 1;
-    if (++cks == KS) {
+    if (++cks == KSp) {
       // acc[b][g][q]: expert row cp*16*MAXG + 16g + l16, feature 4*lg + q of
       // weight block b (up: blocks < NB/2 gate, the rest up, same features).
       const int c_begin = e_begin[ce], c_rows = e_rows[ce];
@@ -267,6 +288,14 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
         const int m = cp * kRowsPerPass + 16 * g + l16;
         if (m >= c_rows) continue;
         const int64_t orow = c_begin + m;
+        if (kSplit && P > 1) {  // a part's partial sums (tail rows: m < kTailRows)
+          float* dst = tail_part + kTailPartHeader + ((cpart * kExperts + ce) * kTailRows + m) * static_cast<int64_t>(d);
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+            *reinterpret_cast<float4*>(dst + cr * unit_rows + b * 16 + 4 * lg) =
+                make_float4(acc[b][g][0], acc[b][g][1], acc[b][g][2], acc[b][g][3]);
+          continue;
+        }
         if constexpr (UP) {
 #pragma unroll
           for (int b = 0; b < NB / 2; ++b) {
@@ -289,7 +318,10 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
         for (int g = 0; g < MAXG; ++g) acc[b][g] = f32x4{0.f, 0.f, 0.f, 0.f};
       cks = 0;
       cu += G;
-      if (cu < n_units) unit_of(e_rows, per_expert, kRowsPerPass, cu, &ce, &cr, &cp);
+      if (cu < n_total) {
+        cpart = kSplit ? cu / n_units : 0;
+        unit_of(e_rows, per_expert, kRowsPerPass, cu - cpart * n_units, &ce, &cr, &cp);
+      }
     }
   }
 }
@@ -301,9 +333,10 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
 // GM workgroups (single waves) per CU.
 template <bool UP, int W, int NB, int MAXG, int S, int GM = 2, bool TAIL = false>
 hipError_t launch_stream(const bf16_t* act, const int32_t* sorted_slots, const int32_t* offs, const bf16_t* wa,
-                         const bf16_t* wb, void* out, int d, int f, int act_rows, int n_cu, hipStream_t s) {
+                         const bf16_t* wb, void* out, int d, int f, int act_rows, int n_cu, hipStream_t s,
+                         float* tail_part = nullptr, int tail_pcap = 0) {
   hipLaunchKernelGGL((decode_stream_kernel<UP, TAIL, W, NB, MAXG, S>), dim3(GM * n_cu), dim3(kWave), 0, s, act,
-                     sorted_slots, offs, wa, wb, out, d, f, act_rows);
+                     sorted_slots, offs, wa, wb, out, d, f, act_rows, tail_part, tail_pcap);
   return hipGetLastError();
 }
 
@@ -346,9 +379,11 @@ hipError_t launch_up_tail_stream(const bf16_t* x, const int32_t* offs, const int
 }
 
 hipError_t launch_down_tail_stream(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int64_t T,
-                                   int d, int f, int n_cu, hipStream_t s) {
+                                   int d, int f, int n_cu, float* tail_part, int64_t tail_part_bytes, hipStream_t s) {
   const int n_slots = static_cast<int>(T) * kTopK;
-  return launch_stream<false, 256, 4, 2, 3, 2, true>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s);
+  const int pcap = tail_part_capacity(tail_part, tail_part_bytes, d);
+  return launch_stream<false, 256, 4, 2, 3, 2, true>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s,
+                                                     pcap >= 2 ? tail_part : nullptr, pcap);
 }
 
 }  // namespace moe

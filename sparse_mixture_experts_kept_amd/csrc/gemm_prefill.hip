@@ -52,6 +52,7 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr int kXcds = 8;
 constexpr int kGroupN = 4;     // n-tiles per group in the tile order
 constexpr int kThinRows = 32;  // m-tiles with at most this many rows take the thin path
+static_assert(kThinRows == kTailPartRows, "the streamed tails are the thin tiles");
 constexpr int kSlotElems = kBM * kBK;  // one 32 KiB slot (kBM == kBN)
 // Word 3 of a raw buffer resource on gfx9 (no format conversion).
 constexpr int kBufferFlags = 0x00020000;
@@ -660,22 +661,53 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
 // SiLU(gate) * up and one bf16 rounding (up projection) or an fp32 store
 // (down projection).  The split is recomputed from the offsets with the
 // GEMM's grid size, stage count and plane count.  One wave per output row.
+// Down projection only: with tail_part, also the split tails' partial sums
+// (layout in launch.hpp): each tail row of y_rows = the sum of its P parts
+// in part order.
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kThreads) remainder_fixup_kernel(const int32_t* __restrict__ offs,
                                                                    const float* __restrict__ partials,
                                                                    void* __restrict__ Cout, int N, int K,
-                                                                   int gemm_grid, int planes, int thin_elsewhere) {
+                                                                   int gemm_grid, int planes, int thin_elsewhere,
+                                                                   const float* __restrict__ tail_part) {
   constexpr int TN = SWIGLU ? kBN / 2 : kBN;
   constexpr int kWavesPerBlock = kThreads / kWave;
   const int n_tiles_n = (N + TN - 1) / TN;
   int n_full, n_thin;
   unit_counts<1>(offs, n_tiles_n, &n_full, &n_thin);
   if (thin_elsewhere) n_thin = 0;
-  const RemSplit rs = remainder_split(n_full, gemm_grid, K / kBK, planes, n_thin == 0);
-  if (rs.rem == 0) return;
+  const RemSplit rs = remainder_split(n_full, gemm_grid, K / kBK, planes, partials != nullptr && n_thin == 0);
+  const int tail_parts = (!SWIGLU && tail_part) ? *reinterpret_cast<const int*>(tail_part) : 1;
+  const int tail_items = tail_parts > 1 ? kExperts * kTailPartRows : 0;
+  if (rs.rem == 0 && tail_items == 0) return;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int64_t part_stride = static_cast<int64_t>(rs.rem) * kPlaneElems;
-  for (int item = blockIdx.x * kWavesPerBlock + wave; item < rs.rem * kBM; item += gridDim.x * kWavesPerBlock) {
+  const int items = rs.rem * kBM + tail_items;
+  for (int item = blockIdx.x * kWavesPerBlock + wave; item < items; item += gridDim.x * kWavesPerBlock) {
+    if (item >= rs.rem * kBM) {  // row m of expert e's split tail
+      const int t = item - rs.rem * kBM;
+      const int e = t / kTailPartRows, m = t % kTailPartRows;
+      int fm;
+      bool thin;
+      expert_shape(offs, e, &fm, &thin);
+      const int row0 = offs[e] + fm * kBM;  // the tail's first row
+      if (!thin || row0 + m >= offs[e + 1]) continue;
+      const float* src = tail_part + kTailPartHeader + static_cast<int64_t>(e * kTailPartRows + m) * N;
+      const int64_t pstride = static_cast<int64_t>(kExperts) * kTailPartRows * N;
+      float* dst = static_cast<float*>(Cout) + static_cast<int64_t>(row0 + m) * N;
+      for (int c = 4 * lane; c < N; c += 4 * kWave) {
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int p = 0; p < tail_parts; ++p) {
+          const float4 v = *reinterpret_cast<const float4*>(src + p * pstride + c);
+          a.x += v.x;
+          a.y += v.y;
+          a.z += v.z;
+          a.w += v.w;
+        }
+        *reinterpret_cast<float4*>(dst + c) = a;
+      }
+      continue;
+    }
     const int r = item / kBM, m = item % kBM;
     int e, mt, nt, ks;
     full_unit<1>(offs, n_tiles_n, rs.n_main + r, &e, &mt, &nt, &ks);
@@ -752,7 +784,7 @@ hipError_t launch_up_prefill(const bf16_t* x, const int32_t* offs, const int32_t
   if (part)
     hipLaunchKernelGGL((remainder_fixup_kernel<true>), dim3(2 * grid), dim3(kThreads), 0, s, offs,
                        static_cast<const float*>(part), static_cast<void*>(h), f, d, grid, planes,
-                       thin_elsewhere ? 1 : 0);
+                       thin_elsewhere ? 1 : 0, static_cast<const float*>(nullptr));
   return hipGetLastError();
 }
 
@@ -772,11 +804,19 @@ hipError_t launch_down_prefill(const bf16_t* h, const int32_t* offs, const bf16_
     hipLaunchKernelGGL((grouped_gemm_prefill_kernel<false, 1>), dim3(grid), dim3(kThreads), 0, s, h,
                        static_cast<const int32_t*>(nullptr), offs, w2, static_cast<const bf16_t*>(nullptr),
                        static_cast<void*>(y_rows), d, f, int64_t{0}, thin_elsewhere ? 1 : 0, part, planes);
-    if (part)
-      hipLaunchKernelGGL((remainder_fixup_kernel<false>), dim3(2 * grid), dim3(kThreads), 0, s, offs,
-                         static_cast<const float*>(part), static_cast<void*>(y_rows), d, f, grid, planes,
-                         thin_elsewhere ? 1 : 0);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_down_prefill_fixup(const int32_t* offs, const float* partials, int64_t partial_bytes,
+                                     const float* tail_part, float* y_rows, int d, int f, int n_cu,
+                                     bool thin_elsewhere, hipStream_t s) {
+  const int grid = (n_cu / kXcds) * kXcds;
+  const int planes = plane_count(partials, partial_bytes);
+  const float* part = planes >= 2 ? partials : nullptr;
+  if (!part && !tail_part) return hipSuccess;
+  hipLaunchKernelGGL((remainder_fixup_kernel<false>), dim3(2 * grid), dim3(kThreads), 0, s, offs, part,
+                     static_cast<void*>(y_rows), d, f, grid, planes, thin_elsewhere ? 1 : 0, tail_part);
   return hipGetLastError();
 }
 

@@ -24,6 +24,20 @@ hipError_t launch_up_f32(const float* x, const int32_t* offs, const int32_t* sor
 hipError_t launch_down_f32(const float* h, const int32_t* offs, const float* w2, float* y_rows, int64_t n_slots,
                            int d, int f, hipStream_t s);
 
+// Split down-projection tails (launch_down_tail_stream with a buffer): the
+// first kTailPartHeader floats hold an int, the part count P the launch
+// chose (1: it wrote y_rows itself), then P x 8 experts x kTailPartRows rows
+// x d fp32 partial sums, row m of expert e's tail at ((p*8 + e)*32 + m)*d.
+constexpr int kTailPartHeader = 64;
+constexpr int kTailPartRows = 32;
+constexpr int kMaxTailParts = 8;
+// Parts that fit a buffer of `bytes` (0 without a buffer).
+inline int tail_part_capacity(const float* p, int64_t bytes, int d) {
+  if (!p || bytes <= kTailPartHeader * 4) return 0;
+  const int64_t n = (bytes - kTailPartHeader * 4) / (int64_t{8} * kTailPartRows * d * 4);
+  return n > kMaxTailParts ? kMaxTailParts : static_cast<int>(n);
+}
+
 // The prefill kernels handle the layer: d, f multiples of 128 and >= 256,
 // and x (T x d bf16) smaller than 4 GiB.
 bool prefill_fits(int64_t T, int d, int f);
@@ -37,17 +51,24 @@ hipError_t launch_up_prefill(const bf16_t* x, const int32_t* offs, const int32_t
                              const bf16_t* w3, bf16_t* h, int d, int f, int n_cu, bool thin_elsewhere,
                              float* partials, int64_t partial_bytes, hipStream_t s);
 // split == 2: two partial sums over the two halves of f, the second at
-// y_rows + split_stride; otherwise one full sum in y_rows.
+// y_rows + split_stride; otherwise one full sum in y_rows, and with
+// partials the remainder units' rows are completed by
+// launch_down_prefill_fixup (after the tail launch, whose split partial sums
+// it also adds when tail_part is given).
 hipError_t launch_down_prefill(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,
                                int n_cu, int split, int64_t split_stride, bool thin_elsewhere, float* partials,
                                int64_t partial_bytes, hipStream_t s);
+hipError_t launch_down_prefill_fixup(const int32_t* offs, const float* partials, int64_t partial_bytes,
+                                     const float* tail_part, float* y_rows, int d, int f, int n_cu,
+                                     bool thin_elsewhere, hipStream_t s);
 // The rows the prefill launches skip with thin_elsewhere, on the streaming
 // kernels (full reduction: with split == 2 the tail rows' second partial
 // must be zero).  Need 2T * f * 2 and T * d * 2 below 2^31.
 hipError_t launch_up_tail_stream(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
                                  const bf16_t* w3, bf16_t* h, int64_t T, int d, int f, int n_cu, hipStream_t s);
+// tail_part (may be null): buffer for split tails (layout above).
 hipError_t launch_down_tail_stream(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int64_t T,
-                                   int d, int f, int n_cu, hipStream_t s);
+                                   int d, int f, int n_cu, float* tail_part, int64_t tail_part_bytes, hipStream_t s);
 
 // Decode (few rows per expert).  T bounds the rows per expert of a top-2
 // routing (any routing stays correct, more rows only take more passes).

@@ -368,19 +368,32 @@ def _unit_plan(counts, T, d, f, n_cu, k=2):
         if P < 2 or (name == "down" and not down_unsplit):
             P, rem = 1, 0
         out[name] = dict(n_full=n_full, rounds=R, rem=rem, parts=P)
+    # down-projection tails (a last tile of at most 32 rows after a full one)
+    # on the streaming kernel: units of 64 w2 rows, 2 waves per CU, the
+    # reduction split in P parts (doubling up to 8 while the units fit and P
+    # divides the 128-deep stages)
+    n_tails = sum(1 for c in counts if c > 256 and c - (c - 1) // 256 * 256 <= 32)
+    units, stages, P = n_tails * (d // 64), f // 128, 1
+    if down_unsplit and n_tails:
+        while 2 * P <= 8 and units * 2 * P <= 2 * n_cu and stages % (2 * P) == 0:
+            P *= 2
+    out["tail_parts"] = P
     return out
 
 
-@pytest.mark.parametrize("T,d,f,seed,bias7", [(4200, 4096, 256, 1, None), (4200, 4096, 1024, 2, None),
-                                             (4200, 4096, 256, 5, -3.0)])
-def test_prefill_remainder_split(T, d, f, seed, bias7):
+@pytest.mark.parametrize("T,d,f,seed,bias7,tail_parts", [(4200, 4096, 256, 1, None, 2), (4200, 4096, 1024, 2, None, 2),
+                                                        (4200, 4096, 256, 5, -3.0, 1), (4160, 4096, 1024, 28, None, 8),
+                                                        (4160, 4096, 1024, 27, None, 4)])
+def test_prefill_remainder_split(T, d, f, seed, bias7, tail_parts):
     # Layers whose work units leave a partial round of the grid: the units
     # past the last whole round are cut along the reduction and summed by the
     # fixup launch.  f=256: every up unit is split (no whole round); f=1024:
     # one whole round plus a split remainder in both projections; bias7
     # leaves expert 7 (the last in unit order) 14 rows, so its one m-tile
-    # takes the thin path inside the split.  Inputs are drawn on the CPU so
-    # the routing is fixed independently of the device.
+    # takes the thin path inside the split.  The down-projection tails are
+    # split too when few experts have one: three (2 parts), two (4), one
+    # (8).  Inputs are drawn on the CPU so the routing is fixed independently
+    # of the device.
     layer = inputs.make_custom(T, d, f, seed=seed, device="cpu")
     if bias7 is not None:
         layer["logit_bias"] = torch.tensor([0.0] * 7 + [bias7], dtype=torch.float32)
@@ -389,6 +402,7 @@ def test_prefill_remainder_split(T, d, f, seed, bias7):
     counts = out["counts"].cpu().tolist()
     plan = _unit_plan(counts, T, d, f, torch.cuda.get_device_properties(0).multi_processor_count)
     assert plan["up"]["parts"] >= 2 and plan["down"]["parts"] >= 2, (counts, plan)
+    assert plan["tail_parts"] == tail_parts, (counts, plan)
     if bias7 is not None:
         assert 0 < counts[7] <= 32, counts
     # deterministic: a second run gives the same bits
