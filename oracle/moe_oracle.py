@@ -33,6 +33,8 @@ reason in the design notes of the repository):
 * top-2 first, then the softmax over the surviving pair (the router paragraph
   of the azimuth.plus page; the mbrenndoerfer "The Solution" page states the
   opposite order, which gives the same weights once its pair is renormalised);
+  that page's literal form, without the renormalisation, is available as the
+  "full" gating (softmax_top_k_gates);
 * ties in the selection go to the lower expert index, and slot 0 of a token is
   its larger score;
 * SwiGLU(x) = (SiLU(x W_gate^T) * (x W_up^T)) W_down^T with SiLU(z) = z/(1+e^-z);
@@ -117,6 +119,30 @@ def masked_softmax_gates(logits, idx) -> np.ndarray:
     return p[rows, idx]
 
 
+def softmax_top_k_gates(logits, idx) -> np.ndarray:
+    """Gates of the other reading of the router, shape [T, k]: a softmax over
+    all E scores first, then the probabilities of the selected experts as they
+    stand, not renormalised (they sum to less than 1 whenever the unselected
+    experts keep some probability).
+
+    "Mixtral & Sparse MoE (2024) > The Solution" (mbrenndoerfer.com), routing
+    paragraph: the scores are normalised by a softmax into a distribution over
+    the experts, the top two are selected, and their outputs are combined by
+    their routing scores.  The same two experts are selected as by the default
+    reading (the softmax keeps the order of the scores); only the weights
+    differ, by the common factor p_a + p_b.
+    """
+    l = _f64(logits)
+    idx = np.asarray(idx, dtype=np.int64)
+    rows = np.arange(l.shape[0])[:, None]
+    p = np.exp(l - l.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    return p[rows, idx]
+
+
+GATINGS = ("pair", "full")
+
+
 def silu(z) -> np.ndarray:
     """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z)) (Swish with beta = 1, the
     activation inside the SwiGLU expert of "Mixtral of Experts", azimuth.plus,
@@ -150,7 +176,7 @@ def swiglu_hidden(x_rows, w1_e, w3_e) -> np.ndarray:
 
 
 def moe_ffn(x, w_gate, w1, w3, w2, logit_bias=None, k: int = TOP_K, idx=None,
-            widen_expert=None) -> dict:
+            widen_expert=None, gating: str = "pair") -> dict:
     """The whole layer, vectorised over tokens (per expert, not per token).
 
     Returns a dict with ``y`` [T, d], ``idx`` [T, k], ``gates`` [T, k] and
@@ -164,8 +190,12 @@ def moe_ffn(x, w_gate, w1, w3, w2, logit_bias=None, k: int = TOP_K, idx=None,
     it; the gates are still the masked softmax of the scores over that
     assignment.  ``widen_expert`` (optional callable e -> (w1_e, w3_e, w2_e))
     lets the caller hand in one expert's weights at a time, so that a
-    full-size layer never holds all experts in float64 at once.
+    full-size layer never holds all experts in float64 at once.  ``gating``
+    "pair" (default) takes the softmax over the kept pair; "full" the
+    softmax over all scores without renormalising (softmax_top_k_gates).
     """
+    if gating not in GATINGS:
+        raise ValueError(f"unknown gating {gating!r}")
     x64 = _f64(x)
     logits = router_logits(x64, w_gate, logit_bias)
     T, E = logits.shape
@@ -173,7 +203,7 @@ def moe_ffn(x, w_gate, w1, w3, w2, logit_bias=None, k: int = TOP_K, idx=None,
         idx = select_top_k(logits, k)
     else:
         idx = np.asarray(idx, dtype=np.int64)
-    gates = masked_softmax_gates(logits, idx)
+    gates = masked_softmax_gates(logits, idx) if gating == "pair" else softmax_top_k_gates(logits, idx)
     y = None
     for e in range(E):
         tok, slot = np.nonzero(idx == e)
@@ -193,13 +223,16 @@ def moe_ffn(x, w_gate, w1, w3, w2, logit_bias=None, k: int = TOP_K, idx=None,
     return {"y": y, "idx": idx, "gates": gates, "logits": logits}
 
 
-def moe_ffn_scalar(x, w_gate, w1, w3, w2, logit_bias=None, k: int = TOP_K) -> np.ndarray:
+def moe_ffn_scalar(x, w_gate, w1, w3, w2, logit_bias=None, k: int = TOP_K, gating: str = "pair") -> np.ndarray:
     """The same layer written token by token with Python loops, for tiny inputs.
 
     For each token: score every expert, keep the k best (stable, lower index on
-    ties), softmax over the kept scores, run each kept expert, add the
-    weighted outputs.  Used to cross-check the vectorised form.
+    ties), softmax over the kept scores ("full": over all scores), run each
+    kept expert, add the weighted outputs.  Used to cross-check the vectorised
+    form.
     """
+    if gating not in GATINGS:
+        raise ValueError(f"unknown gating {gating!r}")
     x64 = _f64(x)
     wg = _f64(w_gate)
     b = None if logit_bias is None else _f64(logit_bias)
@@ -219,7 +252,7 @@ def moe_ffn_scalar(x, w_gate, w1, w3, w2, logit_bias=None, k: int = TOP_K) -> np
         kept = sorted(range(E), key=lambda e: (-scores[e], e))[:k]
         top = max(scores[e] for e in kept)
         num = [np.exp(scores[e] - top) for e in kept]
-        den = sum(num)
+        den = sum(num) if gating == "pair" else sum(np.exp(scores[e] - top) for e in range(E))
         for j, e in enumerate(kept):
             y[t] += (num[j] / den) * swiglu_expert(x64[t:t + 1], w1[e], w3[e], w2[e])[0]
     return y

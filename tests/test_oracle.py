@@ -123,6 +123,76 @@ def test_gates_shift_invariant():
         np.testing.assert_allclose(O.masked_softmax_gates(l + c, idx), O.masked_softmax_gates(l, idx), atol=1e-13)
 
 
+def test_full_gating_closed_form_and_bruteforce():
+    # Scores (2, 1, 0, ..., 0): softmax over all eight gives e^2 / (e^2 + e + 6)
+    # and e / (e^2 + e + 6) to the two kept experts.
+    l = np.array([[2.0, 1.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0], [0.0, 0.0, 0.0, -1.0, 0.0, 0.0, 3.0, 0.0]])
+    idx = O.select_top_k(l, 2)
+    np.testing.assert_array_equal(idx, [[0, 1], [6, 0]])
+    g = O.softmax_top_k_gates(l, idx)
+    den = math.e ** 2 + math.e + 6.0
+    np.testing.assert_allclose(g[0], [math.e ** 2 / den, math.e / den], rtol=1e-15)
+    den = math.e ** 3 + 6.0 + math.exp(-1.0)
+    np.testing.assert_allclose(g[1], [math.e ** 3 / den, 1.0 / den], rtol=1e-15)
+    # brute force with math.exp on random scores
+    rng = np.random.default_rng(21)
+    l = rng.standard_normal((40, 8)) * 2
+    idx = O.select_top_k(l, 2)
+    g = O.softmax_top_k_gates(l, idx)
+    for t in range(l.shape[0]):
+        z = sum(math.exp(v) for v in l[t])
+        for j in range(2):
+            assert abs(g[t, j] - math.exp(l[t, idx[t, j]]) / z) < 1e-14
+        assert g[t].sum() < 1.0 and g[t, 0] >= 1.0 / 8
+
+
+def test_full_gating_renormalises_to_the_pair_softmax():
+    # The two readings select the same pair and their weights differ by the
+    # common factor p_a + p_b; when the other six scores are far below, the
+    # full softmax leaves them no probability and both readings coincide.
+    rng = np.random.default_rng(22)
+    l = rng.standard_normal((300, 8)) * 1.5
+    idx = O.select_top_k(l, 2)
+    full = O.softmax_top_k_gates(l, idx)
+    pair = O.masked_softmax_gates(l, idx)
+    np.testing.assert_allclose(full / full.sum(axis=1, keepdims=True), pair, rtol=1e-14)
+    np.testing.assert_allclose(full[:, 0] / full[:, 1], pair[:, 0] / pair[:, 1], rtol=1e-13)
+    far = l.copy()
+    rows = np.arange(l.shape[0])[:, None]
+    keep = np.zeros_like(l, dtype=bool)
+    keep[rows, idx] = True
+    far[~keep] = -1e4
+    np.testing.assert_array_equal(O.softmax_top_k_gates(far, idx), O.masked_softmax_gates(far, idx))
+    for c in (-3.0, 11.0):
+        np.testing.assert_allclose(O.softmax_top_k_gates(l + c, idx), full, rtol=1e-13)
+
+
+def test_full_gating_layer_scales_the_dense_output():
+    # Shared expert weights: y = (p_a + p_b) * SwiGLU(x) for every token.
+    rng = np.random.default_rng(23)
+    T, d, f = 30, 16, 24
+    x = rng.standard_normal((T, d))
+    wg = rng.standard_normal((8, d)) * 0.5
+    a1, a3, a2 = (rng.standard_normal((f, d)), rng.standard_normal((f, d)), rng.standard_normal((d, f)))
+    out = O.moe_ffn(x, wg, np.stack([a1] * 8), np.stack([a3] * 8), np.stack([a2] * 8), gating="full")
+    dense = O.swiglu_expert(x, a1, a3, a2)
+    l = x @ wg.T
+    p = np.exp(l - l.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    top2 = np.sort(p, axis=1)[:, -2:].sum(axis=1)
+    np.testing.assert_allclose(out["y"], top2[:, None] * dense, rtol=1e-12, atol=1e-12)
+    assert np.all(out["gates"].sum(axis=1) < 1.0)
+
+
+def test_full_gating_scalar_and_vectorised_forms_agree():
+    x, wg, w1, w3, w2 = _rand_layer(24, T=12, d=16, f=32)
+    yv = O.moe_ffn(x, wg, w1, w3, w2, gating="full")["y"]
+    ys = O.moe_ffn_scalar(x, wg, w1, w3, w2, gating="full")
+    np.testing.assert_allclose(yv, ys, rtol=1e-12, atol=1e-12)
+    with pytest.raises(ValueError):
+        O.moe_ffn(x, wg, w1, w3, w2, gating="softmax")
+
+
 # --------------------------------------------------------------------------- experts
 
 
