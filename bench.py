@@ -209,6 +209,13 @@ def main():
                          "algorithmic_per_launch": up_flops,
                          "algorithmic_bytes_per_launch": A.up_bytes(T, d, f, k, sum(1 for c in layer.counts.tolist() if c > 0))},
         })
+        # the same layer with the softmax over all experts (pair not renormalised)
+        layer_full = moe.FFN(L["x"], L["w_gate"], L["w1"], L["w3"], L["w2"], gating=moe.GATING_FULL)
+        sec_full = time_layer(layer_full, args.steps, args.warmup, torch)
+        result["prefill_full_gating"] = {"workload": "mixtral-moe-ffn-prefill, softmax over all experts",
+                                         "T": T, "ms_per_layer": sec_full * 1e3, "tokens_per_s": T / sec_full}
+        _log(f"prefill (full gating): {sec_full * 1e3:.3f} ms/layer")
+        del layer_full
         if not args.no_cpu_baseline:
             _log("cpu baseline: running the fp64 oracle on a token sample")
             result["cpu_baseline"] = cpu_baseline(L, args.cpu_sample, args.cpu_repeats)

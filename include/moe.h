@@ -34,7 +34,7 @@
  * - Errors: every argument is checked on the host before anything is
  *   enqueued; on error nothing is enqueued and outputs are untouched.
  *   NULL required pointer, T < 0, misaligned pointer -> MOE_ERR_INVALID_ARGUMENT;
- *   E != 8, k != 2, d or f not a multiple of 128, unknown dtype/variant,
+ *   E != 8, k != 2, d or f not a multiple of 128, unknown dtype/variant/gating,
  *   or a size above a stated limit -> MOE_ERR_UNSUPPORTED;
  *   T == 0 -> MOE_OK with nothing enqueued.  A failed launch -> MOE_ERR_HIP
  *   (outputs unspecified).  Device faults surface at the caller's next sync.
@@ -69,6 +69,16 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * kernels. */
 typedef enum { MOE_VARIANT_AUTO = 0, MOE_VARIANT_DECODE = 1, MOE_VARIANT_PREFILL = 2 } moe_variant;
 
+/* Gates of the two kept experts.  PAIR (Mixtral, the default): softmax over
+ * the kept pair with every other score at -inf, g_a = 1/(1+exp(l_b-l_a)),
+ * g_b = 1 - g_a ("Mixtral of Experts", azimuth.plus, router paragraph).
+ * FULL: softmax over all E scores first, then the two largest
+ * probabilities as they stand, g_e = exp(l_e) / sum_j exp(l_j), which sum to
+ * less than 1 ("Mixtral & Sparse MoE (2024) > The Solution",
+ * mbrenndoerfer.com, routing paragraph, read literally).  Both select the
+ * same experts; the outputs differ by the factor g_a + g_b. */
+typedef enum { MOE_GATING_PAIR = 0, MOE_GATING_FULL = 1 } moe_gating;
+
 typedef struct {
   int64_t T;        /* tokens, >= 0; T * k must fit in int32 */
   int32_t d;        /* hidden size, multiple of 128 */
@@ -77,6 +87,7 @@ typedef struct {
   int32_t k;        /* experts per token, must be 2 */
   int32_t dtype;    /* moe_dtype */
   int32_t variant;  /* moe_variant */
+  int32_t gating;   /* moe_gating (0 = PAIR) */
 } moe_dims;
 
 /* Human-readable name of a status code (static string). */
@@ -91,7 +102,8 @@ const char* moe_version(void);
  *   x [T, d] (dtype), w_gate [E, d] (dtype), logit_bias [E] fp32 or NULL
  *   (added to every token's scores; a workload device, not part of Mixtral).
  *   Outputs: topk_idx [T, 2] int32 (slot 0 = larger score, ties to the lower
- *   index), topk_w [T, 2] fp32 (>= 0, sum 1), logits [T, E] fp32 or NULL.
+ *   index), topk_w [T, 2] fp32 (>= 0; sum 1 with MOE_GATING_PAIR, below 1
+ *   with MOE_GATING_FULL), logits [T, E] fp32 or NULL.
  *   Scores are accumulated in fp32.  Limit: E * d * elem_size <= 128 KiB
  *   (the router matrix is staged in LDS), i.e. d <= 8192 for bf16.
  */

@@ -46,6 +46,7 @@ moe_status check_dims(const moe_dims* dims) {
   if (dims->d <= 0 || dims->f <= 0 || dims->d % 128 != 0 || dims->f % 128 != 0) return MOE_ERR_UNSUPPORTED;
   if (dims->dtype != MOE_F32 && dims->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (dims->variant < MOE_VARIANT_AUTO || dims->variant > MOE_VARIANT_PREFILL) return MOE_ERR_UNSUPPORTED;
+  if (dims->gating != MOE_GATING_PAIR && dims->gating != MOE_GATING_FULL) return MOE_ERR_UNSUPPORTED;
   if (dims->T > (int64_t{1} << 30) / dims->k) return MOE_ERR_UNSUPPORTED;  // slot ids are int32
   // Largest row offset of h / y_rows must fit comfortably in int64 (always true) and
   // element offsets r*f, r*d are formed in int64 on the device.
@@ -141,7 +142,8 @@ moe_status run_router(const moe_dims* dims, const void* x, const void* w_gate, c
   int n_cu = 0;
   moe_status st = cu_count(&n_cu);
   if (st != MOE_OK) return st;
-  return hip_status(moe::launch_router(dims->dtype, x, w_gate, bias, idx, w, logits, dims->T, dims->d, n_cu, s));
+  return hip_status(
+      moe::launch_router(dims->dtype, x, w_gate, bias, idx, w, logits, dims->T, dims->d, dims->gating, n_cu, s));
 }
 
 moe_status run_up(const moe_dims* dims, const void* x, const int32_t* offs, const int32_t* sorted, const void* w1,
@@ -322,8 +324,8 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
   if (dims->T <= kDecodeMaxTokens) {
     // Small batch: routing and permutation in one workgroup.
     st = hip_status(moe::launch_route_permute(dims->dtype, x, w_gate, logit_bias, idx, w,
-                                              static_cast<int32_t>(dims->T), dims->d, offs, sorted, rows,
-                                              expert_counts_out, s));
+                                              static_cast<int32_t>(dims->T), dims->d, dims->gating, offs, sorted,
+                                              rows, expert_counts_out, s));
     if (st != MOE_OK) return st;
     // (bf16 decode then runs the streaming up and down projections through
     // run_experts below.)

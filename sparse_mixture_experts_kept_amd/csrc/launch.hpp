@@ -11,8 +11,12 @@ typedef uint16_t bf16_t;
 constexpr int kDtypeF32 = 0;
 constexpr int kDtypeBF16 = 1;
 
+// Gating of the kept pair (values of moe_dims.gating).
+constexpr int kGatingPair = 0;  // softmax over the kept pair (weights sum to 1)
+constexpr int kGatingFull = 1;  // softmax over all scores, pair not renormalised
+
 hipError_t launch_router(int dtype, const void* x, const void* wg, const float* bias, int32_t* idx, float* w,
-                         float* logits, int64_t T, int d, int n_cu, hipStream_t s);
+                         float* logits, int64_t T, int d, int gating, int n_cu, hipStream_t s);
 
 hipError_t launch_permute(const int32_t* idx, int32_t n_slots, int32_t* offsets, int32_t* sorted_slots,
                           int32_t* slot_rows, int32_t* counts_out, hipStream_t s);
@@ -90,8 +94,8 @@ hipError_t launch_down_decode_stream(const bf16_t* h, const int32_t* offs, const
 
 // Small batches (T <= 64): routing + permutation in one workgroup.
 hipError_t launch_route_permute(int dtype, const void* x, const void* wg, const float* bias, int32_t* idx, float* w,
-                                int32_t T, int d, int32_t* offsets, int32_t* sorted_slots, int32_t* slot_rows,
-                                int32_t* counts_out, hipStream_t s);
+                                int32_t T, int d, int gating, int32_t* offsets, int32_t* sorted_slots,
+                                int32_t* slot_rows, int32_t* counts_out, hipStream_t s);
 
 // y_rows2 (optional): a second partial-sum buffer added to y_rows first.
 hipError_t launch_combine(int dtype, const float* y_rows, const float* y_rows2, const int32_t* slot_rows,

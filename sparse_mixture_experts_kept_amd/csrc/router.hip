@@ -1,6 +1,8 @@
 // Router: scores x W_g^T, top-2 selection and the softmax over the kept pair.
 // "Mixtral of Experts" (azimuth.plus), router paragraph: one linear map to 8
 // scores, keep the two largest, all others -inf, softmax over the survivors.
+// (Or, with the full gating, the softmax over all 8 scores of "Mixtral &
+// Sparse MoE (2024) > The Solution": see select_top2.)
 //
 // bf16: the scores are a [T, d] x [d, 8] contraction and run on MFMA (the 8
 // router rows padded to 16), the reduction over d split across waves and
@@ -16,13 +18,43 @@
 
 namespace moe {
 
+// Top-2 from the 8 scores (larger first; strict '>' keeps the lower index
+// on ties) and the two gates.  kGatingPair: softmax over the kept pair with
+// the other six at -inf, g_a = 1/(1+r), g_b = r/(1+r), r = exp(l_b - l_a)
+// ("Mixtral of Experts", azimuth.plus, router paragraph).  kGatingFull:
+// softmax over all eight scores, the pair's probabilities kept as they are
+// (no renormalisation), g = (1, r) / sum_e exp(l_e - l_a), summed in expert
+// order ("Mixtral & Sparse MoE (2024) > The Solution", routing paragraph).
+__device__ __forceinline__ void select_top2(const float* sc, int gating, int32_t* idx_out, float* w_out) {
+  int ia = 0;
+  float la = sc[0];
+#pragma unroll
+  for (int e = 1; e < kExperts; ++e)
+    if (sc[e] > la) { la = sc[e]; ia = e; }
+  int ib = -1;
+  float lb = 0.0f;
+#pragma unroll
+  for (int e = 0; e < kExperts; ++e)
+    if (e != ia && (ib < 0 || sc[e] > lb)) { lb = sc[e]; ib = e; }
+  const float r = expf(lb - la);
+  float den = 1.0f + r;
+  if (gating == kGatingFull) {
+    den = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kExperts; ++e) den += expf(sc[e] - la);
+  }
+  idx_out[0] = ia;
+  idx_out[1] = ib;
+  w_out[0] = 1.0f / den;
+  w_out[1] = r / den;
+}
+
 // Route one token with one wavefront: 8 fp32 dot products over d (the
 // router matrix is in LDS), butterfly sums so every lane holds all 8 scores,
-// then lane 0 keeps the two largest (larger first, lower index on ties) and
-// the softmax over that pair.
+// then lane 0 keeps the two largest and their gates (select_top2).
 template <typename T>
 __device__ __forceinline__ void route_token(const T* __restrict__ xr, const T* wg_s, const float* b, int d, int lane,
-                                            int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                                            int gating, int32_t* __restrict__ idx_out, float* __restrict__ w_out,
                                             float* __restrict__ logits_out) {
   constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte load
   // A lane's x chunks are loaded kChunks at a time before any arithmetic, so
@@ -57,25 +89,7 @@ __device__ __forceinline__ void route_token(const T* __restrict__ xr, const T* w
 #pragma unroll
   for (int e = 0; e < kExperts; ++e) acc[e] = wave_sum(acc[e]) + b[e];
 
-  if (lane == 0) {
-    // Two largest, larger first; strict '>' keeps the lower index on ties.
-    int ia = 0;
-    float la = acc[0];
-#pragma unroll
-    for (int e = 1; e < kExperts; ++e)
-      if (acc[e] > la) { la = acc[e]; ia = e; }
-    int ib = -1;
-    float lb = 0.0f;
-#pragma unroll
-    for (int e = 0; e < kExperts; ++e)
-      if (e != ia && (ib < 0 || acc[e] > lb)) { lb = acc[e]; ib = e; }
-    // softmax over {la, lb} with the others at -inf
-    const float r = expf(lb - la);
-    idx_out[0] = ia;
-    idx_out[1] = ib;
-    w_out[0] = 1.0f / (1.0f + r);
-    w_out[1] = r / (1.0f + r);
-  }
+  if (lane == 0) select_top2(acc, gating, idx_out, w_out);
   if (logits_out && lane < kExperts) {
     float v = acc[0];
 #pragma unroll
@@ -112,7 +126,7 @@ template <typename T>
 __global__ void __launch_bounds__(256) router_top2_kernel(const T* __restrict__ x, const T* __restrict__ wg,
                                                           const float* __restrict__ bias, int32_t* __restrict__ idx_out,
                                                           float* __restrict__ w_out, float* __restrict__ logits_out,
-                                                          int64_t T_tokens, int d) {
+                                                          int64_t T_tokens, int d, int gating) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* wg_s = reinterpret_cast<T*>(smem_raw);
   float b[kExperts];
@@ -122,7 +136,7 @@ __global__ void __launch_bounds__(256) router_top2_kernel(const T* __restrict__ 
   const int64_t wave_id = static_cast<int64_t>(blockIdx.x) * waves_per_block + threadIdx.x / kWave;
   const int64_t n_waves = static_cast<int64_t>(gridDim.x) * waves_per_block;
   for (int64_t t = wave_id; t < T_tokens; t += n_waves)
-    route_token(x + t * d, wg_s, b, d, lane, idx_out + 2 * t, w_out + 2 * t,
+    route_token(x + t * d, wg_s, b, d, lane, gating, idx_out + 2 * t, w_out + 2 * t,
                 logits_out ? logits_out + t * kExperts : nullptr);
 }
 
@@ -161,29 +175,10 @@ __host__ __device__ inline int router_slices(int d, int cap) {
   return sl;
 }
 
-// Top-2 and pair softmax from the 8 scores (lower index wins ties).
-__device__ __forceinline__ void select_top2(const float* sc, int32_t* idx_out, float* w_out) {
-  int ia = 0;
-  float la = sc[0];
-#pragma unroll
-  for (int e = 1; e < kExperts; ++e)
-    if (sc[e] > la) { la = sc[e]; ia = e; }
-  int ib = -1;
-  float lb = 0.0f;
-#pragma unroll
-  for (int e = 0; e < kExperts; ++e)
-    if (e != ia && (ib < 0 || sc[e] > lb)) { lb = sc[e]; ib = e; }
-  const float r = expf(lb - la);
-  idx_out[0] = ia;
-  idx_out[1] = ib;
-  w_out[0] = 1.0f / (1.0f + r);
-  w_out[1] = r / (1.0f + r);
-}
-
 // Reduce the slice partials of one 16-token group (parked in LDS as
 // part[slice][lane] = f32x4) and route its tokens; run by one wave.
 __device__ __forceinline__ void router_finish_group(const f32x4 (*part)[kWave], int slices, int group, int T,
-                                                    const float* __restrict__ bias, int lane,
+                                                    const float* __restrict__ bias, int lane, int gating,
                                                     int32_t* __restrict__ idx_out, float* __restrict__ w_out,
                                                     float* __restrict__ logits_out) {
   f32x4 sum = part[0][lane];
@@ -202,7 +197,7 @@ __device__ __forceinline__ void router_finish_group(const f32x4 (*part)[kWave], 
   if (lane < 16 && t < T) {
 #pragma unroll
     for (int e = 0; e < kExperts; ++e) sc[e] += bias ? bias[e] : 0.0f;
-    select_top2(sc, idx_out + kTopK * t, w_out + kTopK * t);
+    select_top2(sc, gating, idx_out + kTopK * t, w_out + kTopK * t);
     if (logits_out) {
 #pragma unroll
       for (int e = 0; e < kExperts; ++e) logits_out[static_cast<int64_t>(t) * kExperts + e] = sc[e];
@@ -215,13 +210,14 @@ __device__ __forceinline__ void router_finish_group(const f32x4 (*part)[kWave], 
 __global__ void __launch_bounds__(1024) router_mfma_kernel(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg,
                                                            const float* __restrict__ bias,
                                                            int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-                                                           float* __restrict__ logits_out, int T, int d) {
+                                                           float* __restrict__ logits_out, int T, int d,
+                                                           int gating) {
   __shared__ f32x4 part[16][kWave];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int slices = router_slices(d, 16);
   if (wave < slices) part[wave][lane] = router_scores_partial(x, wg, T, d, blockIdx.x, wave, slices, lane);
   __syncthreads();
-  if (wave == 0) router_finish_group(part, slices, blockIdx.x, T, bias, lane, idx_out, w_out, logits_out);
+  if (wave == 0) router_finish_group(part, slices, blockIdx.x, T, bias, lane, gating, idx_out, w_out, logits_out);
 }
 
 // Small batches: routing and the expert-major permutation in one workgroup
@@ -231,24 +227,25 @@ template <typename T>
 __global__ void __launch_bounds__(kPermThreads) route_permute_kernel(
     const T* __restrict__ x, const T* __restrict__ wg, const float* __restrict__ bias, int32_t* __restrict__ idx_out,
     float* __restrict__ w_out, int32_t T_tokens, int d, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_rows, int32_t* __restrict__ counts_out) {
+    int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_rows, int32_t* __restrict__ counts_out,
+    int gating) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* wg_s = reinterpret_cast<T*>(smem_raw);
   float b[kExperts];
   stage_router(wg, bias, wg_s, d, b);
   const int lane = threadIdx.x % kWave;
   for (int t = threadIdx.x / kWave; t < T_tokens; t += kPermWaves)
-    route_token(x + static_cast<int64_t>(t) * d, wg_s, b, d, lane, idx_out + 2 * t, w_out + 2 * t, nullptr);
+    route_token(x + static_cast<int64_t>(t) * d, wg_s, b, d, lane, gating, idx_out + 2 * t, w_out + 2 * t, nullptr);
   __syncthreads();  // the ids written above are read back by permute_block
   permute_block(idx_out, T_tokens * kTopK, offsets, sorted_slots, slot_rows, counts_out);
 }
 
 hipError_t launch_router(int dtype, const void* x, const void* wg, const float* bias, int32_t* idx, float* w,
-                         float* logits, int64_t T, int d, int n_cu, hipStream_t s) {
+                         float* logits, int64_t T, int d, int gating, int n_cu, hipStream_t s) {
   if (dtype == kDtypeBF16) {
     const int64_t groups = (T + 15) / 16;
     hipLaunchKernelGGL(router_mfma_kernel, dim3(groups), dim3(1024), 0, s, static_cast<const bf16_t*>(x),
-                       static_cast<const bf16_t*>(wg), bias, idx, w, logits, static_cast<int>(T), d);
+                       static_cast<const bf16_t*>(wg), bias, idx, w, logits, static_cast<int>(T), d, gating);
     return hipGetLastError();
   }
   const int threads = 256;
@@ -266,10 +263,12 @@ hipError_t launch_router(int dtype, const void* x, const void* wg, const float* 
   }
   if (dtype == kDtypeBF16) {
     hipLaunchKernelGGL(router_top2_kernel<bf16_t>, dim3(blocks), dim3(threads), lds, s,
-                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(wg), bias, idx, w, logits, T, d);
+                       static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(wg), bias, idx, w, logits, T, d,
+                       gating);
   } else {
     hipLaunchKernelGGL(router_top2_kernel<float>, dim3(blocks), dim3(threads), lds, s,
-                       static_cast<const float*>(x), static_cast<const float*>(wg), bias, idx, w, logits, T, d);
+                       static_cast<const float*>(x), static_cast<const float*>(wg), bias, idx, w, logits, T, d,
+                       gating);
   }
   return hipGetLastError();
 }
@@ -287,7 +286,8 @@ namespace moe {
 __global__ void __launch_bounds__(kPermThreads) route_permute_mfma_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const float* __restrict__ bias,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t T_tokens, int d, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_rows, int32_t* __restrict__ counts_out) {
+    int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_rows, int32_t* __restrict__ counts_out,
+    int gating) {
   constexpr int kGroups = 4;  // T <= 64
   __shared__ f32x4 part[kPermWaves][kGroups][kWave];
   __shared__ int32_t idx_s[kGroups * 16 * kTopK];
@@ -343,7 +343,7 @@ __global__ void __launch_bounds__(kPermThreads) route_permute_mfma_kernel(
       for (int e = 0; e < kExperts; ++e) sc[e] += bias ? bias[e] : 0.0f;
       int32_t pair[kTopK];
       float gate[kTopK];
-      select_top2(sc, pair, gate);
+      select_top2(sc, gating, pair, gate);
       idx_out[kTopK * t] = pair[0];
       idx_out[kTopK * t + 1] = pair[1];
       w_out[kTopK * t] = gate[0];
@@ -361,12 +361,12 @@ __global__ void __launch_bounds__(kPermThreads) route_permute_mfma_kernel(
 namespace moe {
 
 hipError_t launch_route_permute(int dtype, const void* x, const void* wg, const float* bias, int32_t* idx, float* w,
-                                int32_t T, int d, int32_t* offsets, int32_t* sorted_slots, int32_t* slot_rows,
-                                int32_t* counts_out, hipStream_t s) {
+                                int32_t T, int d, int gating, int32_t* offsets, int32_t* sorted_slots,
+                                int32_t* slot_rows, int32_t* counts_out, hipStream_t s) {
   if (dtype == kDtypeBF16) {
     hipLaunchKernelGGL(route_permute_mfma_kernel, dim3(1), dim3(kPermThreads), 0, s, static_cast<const bf16_t*>(x),
                        static_cast<const bf16_t*>(wg), bias, idx, w, T, d, offsets, sorted_slots, slot_rows,
-                       counts_out);
+                       counts_out, gating);
     return hipGetLastError();
   }
   const size_t lds = kExperts * static_cast<size_t>(d) * (dtype == kDtypeBF16 ? 2 : 4);
@@ -379,11 +379,11 @@ hipError_t launch_route_permute(int dtype, const void* x, const void* wg, const 
   if (dtype == kDtypeBF16)
     hipLaunchKernelGGL(route_permute_kernel<bf16_t>, dim3(1), dim3(kPermThreads), lds, s,
                        static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(wg), bias, idx, w, T, d, offsets,
-                       sorted_slots, slot_rows, counts_out);
+                       sorted_slots, slot_rows, counts_out, gating);
   else
     hipLaunchKernelGGL(route_permute_kernel<float>, dim3(1), dim3(kPermThreads), lds, s,
                        static_cast<const float*>(x), static_cast<const float*>(wg), bias, idx, w, T, d, offsets,
-                       sorted_slots, slot_rows, counts_out);
+                       sorted_slots, slot_rows, counts_out, gating);
   return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16 = 0, 1
 VARIANT_AUTO, VARIANT_DECODE, VARIANT_PREFILL = 0, 1, 2
+GATING_PAIR, GATING_FULL = 0, 1  # softmax over the kept pair / over all experts (not renormalised)
 E_EXPERTS, TOP_K = 8, 2
 
 EXPORTED = ("moe_status_string", "moe_version", "moe_router_topk", "moe_permute", "moe_grouped_swiglu",
@@ -33,7 +34,8 @@ class MoeError(RuntimeError):
 
 class MoeDims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("f", ctypes.c_int32), ("E", ctypes.c_int32),
-                ("k", ctypes.c_int32), ("dtype", ctypes.c_int32), ("variant", ctypes.c_int32)]
+                ("k", ctypes.c_int32), ("dtype", ctypes.c_int32), ("variant", ctypes.c_int32),
+                ("gating", ctypes.c_int32)]
 
 
 _lib = None
@@ -91,10 +93,10 @@ def torch_dtype(code: int) -> torch.dtype:
     return torch.bfloat16 if code == MOE_BF16 else torch.float32
 
 
-def make_dims(T, d, f, dtype, variant=VARIANT_AUTO, E=E_EXPERTS, k=TOP_K) -> MoeDims:
+def make_dims(T, d, f, dtype, variant=VARIANT_AUTO, E=E_EXPERTS, k=TOP_K, gating=GATING_PAIR) -> MoeDims:
     if isinstance(dtype, torch.dtype):
         dtype = dtype_code(dtype)
-    return MoeDims(int(T), int(d), int(f), int(E), int(k), int(dtype), int(variant))
+    return MoeDims(int(T), int(d), int(f), int(E), int(k), int(dtype), int(variant), int(gating))
 
 
 def ptr(t):
@@ -112,20 +114,20 @@ def stream_handle():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _layer_dims(x, w1, variant):
+def _layer_dims(x, w1, variant, gating=GATING_PAIR):
     T, d = x.shape
     f = w1.shape[1]
-    return make_dims(T, d, f, x.dtype, variant)
+    return make_dims(T, d, f, x.dtype, variant, gating=gating)
 
 
 # --------------------------------------------------------------------------- staged calls
 
 
-def router_topk(x, w_gate, logit_bias=None, return_logits=False):
+def router_topk(x, w_gate, logit_bias=None, return_logits=False, gating=GATING_PAIR):
     """topk_idx [T,2] int32, topk_w [T,2] fp32 (and logits [T,8] fp32)."""
     lib = load_library()
     T, d = x.shape
-    dims = make_dims(T, d, 128, x.dtype)
+    dims = make_dims(T, d, 128, x.dtype, gating=gating)
     idx = torch.empty((T, TOP_K), dtype=torch.int32, device=x.device)
     w = torch.empty((T, TOP_K), dtype=torch.float32, device=x.device)
     logits = torch.empty((T, E_EXPERTS), dtype=torch.float32, device=x.device) if return_logits else None
@@ -220,9 +222,9 @@ class FFN:
     and ``counts`` may be supplied to share buffers between layers."""
 
     def __init__(self, x, w_gate, w1, w3, w2, logit_bias=None, variant=VARIANT_AUTO, routing=True, y=None,
-                 workspace=None, counts=None):
+                 workspace=None, counts=None, gating=GATING_PAIR):
         self.lib = load_library()
-        self.dims = _layer_dims(x, w1, variant)
+        self.dims = _layer_dims(x, w1, variant, gating)
         T, d = x.shape
         self.args = (x, w_gate, logit_bias, w1, w3, w2)
         self.y = y if y is not None else torch.empty((T, d), dtype=x.dtype, device=x.device)
@@ -245,9 +247,10 @@ class FFN:
         return self.y
 
 
-def ffn_forward(x, w_gate, w1, w3, w2, logit_bias=None, variant=VARIANT_AUTO, return_routing=False):
+def ffn_forward(x, w_gate, w1, w3, w2, logit_bias=None, variant=VARIANT_AUTO, return_routing=False,
+                gating=GATING_PAIR):
     """y [T, d] (x's dtype); with return_routing also (topk_idx, topk_w, counts)."""
-    layer = FFN(x, w_gate, w1, w3, w2, logit_bias, variant, routing=True)
+    layer = FFN(x, w_gate, w1, w3, w2, logit_bias, variant, routing=True, gating=gating)
     y = layer()
     if return_routing:
         return y, layer.idx, layer.w, layer.counts

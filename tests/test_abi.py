@@ -68,6 +68,8 @@ def _dims(**kw):
     (dict(d=0), moe.MOE_ERR_UNSUPPORTED),
     (dict(dtype=7), moe.MOE_ERR_UNSUPPORTED),
     (dict(variant=3), moe.MOE_ERR_UNSUPPORTED),
+    (dict(gating=2), moe.MOE_ERR_UNSUPPORTED),
+    (dict(gating=-1), moe.MOE_ERR_UNSUPPORTED),
     (dict(T=1 << 31), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_bad_dims_are_rejected(kw, status):

@@ -36,7 +36,7 @@ def _widen_experts(layer):
     return lambda e: (O._f64(w1[e]), O._f64(w3[e]), O._f64(w2[e]))
 
 
-def _check_routing(idx_gpu, w_gpu, ref, tokens=None):
+def _check_routing(idx_gpu, w_gpu, ref, tokens=None, gating="pair"):
     logits = ref["logits"]
     gap = O.second_third_gap(logits)
     clear = gap > GAP
@@ -45,17 +45,24 @@ def _check_routing(idx_gpu, w_gpu, ref, tokens=None):
     np.testing.assert_array_equal(gi[clear], ref["idx"][clear])
     assert O.is_valid_top2(logits, gi, GAP).all()
     np.testing.assert_allclose(gw[clear], ref["gates"][clear], atol=1e-5, rtol=0)
-    np.testing.assert_allclose(gw.sum(axis=1), 1.0, atol=1e-6)
+    if gating == "pair":
+        np.testing.assert_allclose(gw.sum(axis=1), 1.0, atol=1e-6)
+    else:
+        assert (gw.sum(axis=1) <= 1.0 + 1e-6).all()
     assert (gw >= 0).all()
     return clear
 
 
-def run_and_check(layer, variant=moe.VARIANT_AUTO, sample=None):
+_GATING = {"pair": moe.GATING_PAIR, "full": moe.GATING_FULL}
+
+
+def run_and_check(layer, variant=moe.VARIANT_AUTO, sample=None, gating="pair"):
     """Whole layer on the GPU vs the oracle on all tokens (or a sample)."""
     dims = layer["dims"]
     x = layer["x"]
     y, idx, w, counts = moe.ffn_forward(x, layer["w_gate"], layer["w1"], layer["w3"], layer["w2"],
-                                        logit_bias=layer.get("logit_bias"), variant=variant, return_routing=True)
+                                        logit_bias=layer.get("logit_bias"), variant=variant, return_routing=True,
+                                        gating=_GATING[gating])
     torch.cuda.synchronize()
     idx_g = idx.cpu().numpy().astype(np.int64)
     w_g = w.cpu().numpy().astype(np.float64)
@@ -65,8 +72,8 @@ def run_and_check(layer, variant=moe.VARIANT_AUTO, sample=None):
     xs = _cpu(x)[tok]
     bias = _cpu(layer.get("logit_bias"))
     widen = _widen_experts(layer)
-    ref = O.moe_ffn(xs, _cpu(layer["w_gate"]), None, None, None, logit_bias=bias, widen_expert=widen)
-    clear = _check_routing(idx_g[tok], w_g[tok], ref)
+    ref = O.moe_ffn(xs, _cpu(layer["w_gate"]), None, None, None, logit_bias=bias, widen_expert=widen, gating=gating)
+    clear = _check_routing(idx_g[tok], w_g[tok], ref, gating=gating)
     if sample is None:
         # per-expert counts over the tokens whose routing is decided beyond the tie margin
         np.testing.assert_array_equal(np.bincount(idx_g[clear].reshape(-1), minlength=8),
@@ -74,7 +81,7 @@ def run_and_check(layer, variant=moe.VARIANT_AUTO, sample=None):
     # outputs, under the assignment the GPU made (identical to the oracle's on clear tokens)
     if not np.array_equal(idx_g[tok], ref["idx"]):
         ref = O.moe_ffn(xs, _cpu(layer["w_gate"]), None, None, None, logit_bias=bias, idx=idx_g[tok],
-                        widen_expert=widen)
+                        widen_expert=widen, gating=gating)
     yg = y.float().cpu().numpy().astype(np.float64)[tok]
     err = np.abs(yg - ref["y"]).max() if yg.size else 0.0
     tol = _tol(dims["dtype"], ref["y"])
@@ -339,6 +346,37 @@ def test_errors_with_real_tensors():
                         layer["w3"], layer["w2"])
     y0 = moe.ffn_forward(layer["x"][:0], layer["w_gate"], layer["w1"], layer["w3"], layer["w2"])
     assert y0.shape == (0, 256)
+
+
+# --------------------------------------------------------------------------- softmax over all experts (full gating)
+
+
+@pytest.mark.parametrize("T,d,f,dtype,variant", [(300, 256, 512, "bf16", moe.VARIANT_PREFILL),
+                                                 (48, 256, 512, "bf16", moe.VARIANT_DECODE),
+                                                 (200, 256, 384, "bf16", moe.VARIANT_DECODE),
+                                                 (100, 128, 256, "f32", moe.VARIANT_AUTO),
+                                                 (40, 128, 256, "f32", moe.VARIANT_AUTO)])
+def test_full_gating_layer(T, d, f, dtype, variant):
+    # Every router kernel with the full gating: bf16 MFMA router (T > 64),
+    # bf16 routing fused with the permutation (T <= 64), fp32 wave router,
+    # fp32 fused form; the gates sum to less than 1 and scale the outputs.
+    layer = _layer(T, d, f, dtype=dtype, seed=400 + T)
+    out = run_and_check(layer, variant=variant, gating="full")
+    sums = out["w"].sum(dim=1).cpu().numpy()
+    assert (sums < 1.0).all() and (sums > 0.25).all()
+    # same experts as the pair gating; weights differ by the factor g_a + g_b
+    y2, idx2, w2, _ = moe.ffn_forward(layer["x"], layer["w_gate"], layer["w1"], layer["w3"], layer["w2"],
+                                      variant=variant, return_routing=True)
+    torch.testing.assert_close(idx2, out["idx"], rtol=0, atol=0)
+    torch.testing.assert_close(w2, out["w"] / out["w"].sum(dim=1, keepdim=True), rtol=0, atol=2e-6)
+
+
+def test_full_gating_router_entry_point():
+    layer = _layer(77, 256, 256, seed=41)
+    idx, w, logits = moe.router_topk(layer["x"], layer["w_gate"], return_logits=True, gating=moe.GATING_FULL)
+    l64 = O._f64(logits.cpu())
+    ref = O.softmax_top_k_gates(l64, idx.cpu().numpy().astype(np.int64))
+    np.testing.assert_allclose(w.cpu().numpy(), ref, atol=1e-6, rtol=0)
 
 
 # --------------------------------------------------------------------------- remainder split of the prefill GEMMs
