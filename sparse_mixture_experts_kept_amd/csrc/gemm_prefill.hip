@@ -656,6 +656,47 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
   }
 }
 
+// Sum over parts p = 0..P-1 of src[p * stride .. +3] (or +1), added in part
+// order; the loads of up to kPartBatch parts are issued before any add, so
+// a row costs one memory latency per batch rather than one per part.
+constexpr int kPartBatch = 8;
+__device__ __forceinline__ float4 sum_parts4(const float* src, int64_t stride, int P) {
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p0 = 0; p0 < P; p0 += kPartBatch) {
+    float4 v[kPartBatch];
+#pragma unroll
+    for (int j = 0; j < kPartBatch; ++j)
+      v[j] = p0 + j < P ? *reinterpret_cast<const float4*>(src + (p0 + j) * stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < kPartBatch; ++j) {
+      if (p0 + j < P) {
+        a.x += v[j].x;
+        a.y += v[j].y;
+        a.z += v[j].z;
+        a.w += v[j].w;
+      }
+    }
+  }
+  return a;
+}
+__device__ __forceinline__ float2 sum_parts2(const float* src, int64_t stride, int P) {
+  float2 a = make_float2(0.f, 0.f);
+  for (int p0 = 0; p0 < P; p0 += kPartBatch) {
+    float2 v[kPartBatch];
+#pragma unroll
+    for (int j = 0; j < kPartBatch; ++j)
+      v[j] = p0 + j < P ? *reinterpret_cast<const float2*>(src + (p0 + j) * stride) : make_float2(0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < kPartBatch; ++j) {
+      if (p0 + j < P) {
+        a.x += v[j].x;
+        a.y += v[j].y;
+      }
+    }
+  }
+  return a;
+}
+
 // Adds the partial tiles of the remainder units (see remainder_split) in
 // part order and applies the epilogue the GEMM applies to a whole unit:
 // SiLU(gate) * up and one bf16 rounding (up projection) or an fp32 store
@@ -678,14 +719,17 @@ __global__ void __launch_bounds__(kThreads) remainder_fixup_kernel(const int32_t
   if (thin_elsewhere) n_thin = 0;
   const RemSplit rs = remainder_split(n_full, gemm_grid, K / kBK, planes, partials != nullptr && n_thin == 0);
   const int tail_parts = (!SWIGLU && tail_part) ? *reinterpret_cast<const int*>(tail_part) : 1;
-  const int tail_items = tail_parts > 1 ? kExperts * kTailPartRows : 0;
+  constexpr int kTailChunk = 4 * 4 * kWave;  // columns per tail item (4 float4 per lane)
+  const int tail_chunks = (N + kTailChunk - 1) / kTailChunk;
+  const int tail_items = tail_parts > 1 ? kExperts * kTailPartRows * tail_chunks : 0;
   if (rs.rem == 0 && tail_items == 0) return;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int64_t part_stride = static_cast<int64_t>(rs.rem) * kPlaneElems;
   const int items = rs.rem * kBM + tail_items;
   for (int item = blockIdx.x * kWavesPerBlock + wave; item < items; item += gridDim.x * kWavesPerBlock) {
-    if (item >= rs.rem * kBM) {  // row m of expert e's split tail
-      const int t = item - rs.rem * kBM;
+    if (item >= rs.rem * kBM) {  // columns [ch*kTailChunk, +kTailChunk) of row m of expert e's split tail
+      const int t0 = item - rs.rem * kBM;
+      const int ch = t0 % tail_chunks, t = t0 / tail_chunks;
       const int e = t / kTailPartRows, m = t % kTailPartRows;
       int fm;
       bool thin;
@@ -695,17 +739,10 @@ __global__ void __launch_bounds__(kThreads) remainder_fixup_kernel(const int32_t
       const float* src = tail_part + kTailPartHeader + static_cast<int64_t>(e * kTailPartRows + m) * N;
       const int64_t pstride = static_cast<int64_t>(kExperts) * kTailPartRows * N;
       float* dst = static_cast<float*>(Cout) + static_cast<int64_t>(row0 + m) * N;
-      for (int c = 4 * lane; c < N; c += 4 * kWave) {
-        float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int p = 0; p < tail_parts; ++p) {
-          const float4 v = *reinterpret_cast<const float4*>(src + p * pstride + c);
-          a.x += v.x;
-          a.y += v.y;
-          a.z += v.z;
-          a.w += v.w;
-        }
-        *reinterpret_cast<float4*>(dst + c) = a;
-      }
+      const int c_end = min(N, (ch + 1) * kTailChunk);
+#pragma unroll 4
+      for (int c = ch * kTailChunk + 4 * lane; c < c_end; c += 4 * kWave)
+        *reinterpret_cast<float4*>(dst + c) = sum_parts4(src + c, pstride, tail_parts);
       continue;
     }
     const int r = item / kBM, m = item % kBM;
@@ -722,29 +759,15 @@ __global__ void __launch_bounds__(kThreads) remainder_fixup_kernel(const int32_t
       // output columns n0 + c, c + 1: gate sums at B-tile row (c/64)*128 + c%64, up sums 64 rows on
       const int c = 2 * lane;
       const int b = (c / 64) * 128 + c % 64;
-      float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
-      for (int p = 0; p < rs.parts; ++p) {
-        const float2 g = *reinterpret_cast<const float2*>(src + p * part_stride + b);
-        const float2 u = *reinterpret_cast<const float2*>(src + p * part_stride + b + 64);
-        g0 += g.x;
-        g1 += g.y;
-        u0 += u.x;
-        u1 += u.y;
-      }
+      const float2 g = sum_parts2(src + b, part_stride, rs.parts);
+      const float2 u = sum_parts2(src + b + 64, part_stride, rs.parts);
       bf16_t* C = static_cast<bf16_t*>(Cout);
-      *reinterpret_cast<uint32_t*>(C + orow * N + n0 + c) = pack_bf16x2(silu(g0) * u0, silu(g1) * u1);
+      *reinterpret_cast<uint32_t*>(C + orow * N + n0 + c) = pack_bf16x2(silu(g.x) * u.x, silu(g.y) * u.y);
     } else {
       const int c = 4 * lane;
       if (n0 + c >= N) continue;
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int p = 0; p < rs.parts; ++p) {
-        const float4 v = *reinterpret_cast<const float4*>(src + p * part_stride + c);
-        a.x += v.x;
-        a.y += v.y;
-        a.z += v.z;
-        a.w += v.w;
-      }
-      *reinterpret_cast<float4*>(static_cast<float*>(Cout) + orow * N + n0 + c) = a;
+      *reinterpret_cast<float4*>(static_cast<float*>(Cout) + orow * N + n0 + c) =
+          sum_parts4(src + c, part_stride, rs.parts);
     }
   }
 }
