@@ -176,7 +176,7 @@ def swiglu_hidden(x_rows, w1_e, w3_e) -> np.ndarray:
 
 
 def moe_ffn(x, w_gate, w1, w3, w2, logit_bias=None, k: int = TOP_K, idx=None,
-            widen_expert=None, gating: str = "pair") -> dict:
+            widen_expert=None, gating: str = "pair", capacity: int = 0) -> dict:
     """The whole layer, vectorised over tokens (per expert, not per token).
 
     Returns a dict with ``y`` [T, d], ``idx`` [T, k], ``gates`` [T, k] and
@@ -193,6 +193,9 @@ def moe_ffn(x, w_gate, w1, w3, w2, logit_bias=None, k: int = TOP_K, idx=None,
     full-size layer never holds all experts in float64 at once.  ``gating``
     "pair" (default) takes the softmax over the kept pair; "full" the
     softmax over all scores without renormalising (softmax_top_k_gates).
+    ``capacity`` > 0 drops the slots past each expert's capacity
+    (capacity_keep); a dropped slot adds nothing and the token's other gate
+    is left as it is.  The result then also holds ``keep`` [T, k].
     """
     if gating not in GATINGS:
         raise ValueError(f"unknown gating {gating!r}")
@@ -204,9 +207,10 @@ def moe_ffn(x, w_gate, w1, w3, w2, logit_bias=None, k: int = TOP_K, idx=None,
     else:
         idx = np.asarray(idx, dtype=np.int64)
     gates = masked_softmax_gates(logits, idx) if gating == "pair" else softmax_top_k_gates(logits, idx)
+    keep = capacity_keep(idx, capacity, E)
     y = None
     for e in range(E):
-        tok, slot = np.nonzero(idx == e)
+        tok, slot = np.nonzero((idx == e) & keep)
         if tok.size == 0:
             continue
         if widen_expert is not None:
@@ -220,7 +224,7 @@ def moe_ffn(x, w_gate, w1, w3, w2, logit_bias=None, k: int = TOP_K, idx=None,
     if y is None:  # T == 0
         d = _f64(w2[0]).shape[0] if widen_expert is None else 0
         y = np.zeros((T, d))
-    return {"y": y, "idx": idx, "gates": gates, "logits": logits}
+    return {"y": y, "idx": idx, "gates": gates, "logits": logits, "keep": keep}
 
 
 def moe_ffn_scalar(x, w_gate, w1, w3, w2, logit_bias=None, k: int = TOP_K, gating: str = "pair") -> np.ndarray:
@@ -276,6 +280,50 @@ def expert_permutation(idx, n_experts: int = N_EXPERTS):
     slot_rows = np.empty_like(sorted_slots)
     slot_rows[sorted_slots] = np.arange(flat.size)
     return offsets, sorted_slots, slot_rows
+
+
+def capacity_keep(idx, capacity: int, n_experts: int = N_EXPERTS) -> np.ndarray:
+    """Which slots an expert capacity admits, shape [T, k] bool.
+
+    "Mixtral & Sparse MoE (2024) > The Solution" (mbrenndoerfer.com),
+    load-balancing paragraph: a capacity constraint limits how many tokens
+    each expert receives.  The page gives no rule for which ones; the reading
+    here: each expert admits its first ``capacity`` slots in slot order (slot
+    s = t*k + j, so earlier tokens first and, within a token, its larger score
+    first) and drops the rest.  ``capacity`` 0 means no limit (dropless).
+    Written as a walk over the slots with one counter per expert.
+    """
+    flat = np.asarray(idx, dtype=np.int64).reshape(-1)
+    keep = np.ones(flat.size, dtype=bool)
+    if capacity > 0:
+        taken = np.zeros(n_experts, dtype=np.int64)
+        for s, e in enumerate(flat):
+            keep[s] = taken[e] < capacity
+            taken[e] += 1
+    return keep.reshape(np.asarray(idx).shape)
+
+
+def load_balance_loss(logits, idx, n_experts: int = N_EXPERTS) -> float:
+    """Auxiliary load-balancing loss E * sum_e f_e * P_e.
+
+    "Mixtral & Sparse MoE (2024) > The Solution", load-balancing paragraph:
+    auxiliary losses pushed the router towards an even spread of work over
+    the experts; the page gives no formula.  The reading here is the usual
+    product form: f_e = the fraction of the T*k routed slots that chose expert
+    e (before any capacity limit), P_e = the mean over tokens of the softmax
+    over all E scores at e.  It is 1 for a perfectly even router and grows
+    towards E as the work collapses onto fewer experts.
+    """
+    l = _f64(logits)
+    T, E = l.shape
+    if T == 0:
+        return 0.0
+    flat = np.asarray(idx, dtype=np.int64).reshape(-1)
+    f = np.bincount(flat, minlength=n_experts) / flat.size
+    p = np.exp(l - l.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    P = p.mean(axis=0)
+    return float(n_experts * np.sum(f * P))
 
 
 def second_third_gap(logits) -> np.ndarray:

@@ -193,6 +193,75 @@ def test_full_gating_scalar_and_vectorised_forms_agree():
         O.moe_ffn(x, wg, w1, w3, w2, gating="softmax")
 
 
+# --------------------------------------------------------------------------- capacity limit, load-balance loss
+
+
+def test_capacity_keep_matches_ranks_in_the_stable_permutation():
+    # A slot is admitted iff its position among its expert's slots (the stable
+    # expert-major order of expert_permutation) is below the capacity.
+    rng = np.random.default_rng(31)
+    l = rng.standard_normal((200, 8)) + np.array([1.5, 0.8, 0, 0, 0, 0, 0, -1.0])
+    idx = O.select_top_k(l, 2)
+    offsets, sorted_slots, slot_rows = O.expert_permutation(idx)
+    flat = idx.reshape(-1)
+    rank = slot_rows - offsets[flat]
+    for cap in (1, 7, 40, 100, 400):
+        keep = O.capacity_keep(idx, cap).reshape(-1)
+        np.testing.assert_array_equal(keep, rank < cap)
+        counts = np.bincount(flat, minlength=8)
+        assert keep.sum() == np.minimum(counts, cap).sum()
+    assert O.capacity_keep(idx, 0).all()
+
+
+def test_capacity_handworked_and_no_renormalisation():
+    # Four tokens routed (0, 1), (1, 0), (0, 2), (1, 2); capacity 2 admits
+    # slots 0, 1, 2, 3 and 5 (expert 2 keeps both its slots) and drops slot 4
+    # (expert 0's third) and slot 6 (expert 1's third).
+    idx = np.array([[0, 1], [1, 0], [0, 2], [1, 2]])
+    keep = O.capacity_keep(idx, 2)
+    np.testing.assert_array_equal(keep, [[True, True], [True, True], [False, True], [False, True]])
+    x, wg, w1, w3, w2 = _rand_layer(32, T=4)
+    full = O.moe_ffn(x, wg, w1, w3, w2, idx=idx)
+    capped = O.moe_ffn(x, wg, w1, w3, w2, idx=idx, capacity=2)
+    np.testing.assert_allclose(capped["y"][:2], full["y"][:2], rtol=1e-15, atol=0)
+    for t in (2, 3):  # only the second expert, weighted by its own (unrenormalised) gate
+        o2 = O.swiglu_expert(x[t:t + 1], w1[2], w3[2], w2[2])[0]
+        np.testing.assert_allclose(capped["y"][t], full["gates"][t, 1] * o2, rtol=1e-13, atol=1e-15)
+    # a token with both slots dropped outputs zero
+    idx2 = np.array([[3, 4], [3, 4]])
+    y2 = O.moe_ffn(x[:2], wg, w1, w3, w2, idx=idx2, capacity=1)["y"]
+    assert np.array_equal(y2[1], np.zeros(x.shape[1])) and np.abs(y2[0]).max() > 0
+
+
+def test_capacity_at_least_the_largest_count_changes_nothing():
+    x, wg, w1, w3, w2 = _rand_layer(33, T=40)
+    ref = O.moe_ffn(x, wg, w1, w3, w2)
+    big = int(np.bincount(ref["idx"].reshape(-1), minlength=8).max())
+    out = O.moe_ffn(x, wg, w1, w3, w2, capacity=big)
+    np.testing.assert_array_equal(out["y"], ref["y"])
+    assert out["keep"].all()
+    out = O.moe_ffn(x, wg, w1, w3, w2, capacity=big - 1)
+    assert not out["keep"].all() and not np.array_equal(out["y"], ref["y"])
+
+
+def test_load_balance_loss_closed_forms():
+    # Even router, even routing: f_e = P_e = 1/8, loss 1.
+    l = np.zeros((8, 8))
+    idx = np.array([[e, (e + 1) % 8] for e in range(8)])
+    assert abs(O.load_balance_loss(l, idx) - 1.0) < 1e-15
+    # One token, scores (a, b, 0, ..., 0), routed to (0, 1): f = (1/2, 1/2, 0...)
+    # and the loss is 8 * (p_0 + p_1) / 2.
+    a, b = 2.0, 0.5
+    z = math.exp(a) + math.exp(b) + 6.0
+    loss = O.load_balance_loss(np.array([[a, b, 0, 0, 0, 0, 0, 0]]), np.array([[0, 1]]))
+    assert abs(loss - 4.0 * (math.exp(a) + math.exp(b)) / z) < 1e-14
+    # Collapse onto two experts with scores far above the rest: loss -> 4.
+    l = np.full((50, 8), -40.0)
+    l[:, :2] = 10.0
+    assert abs(O.load_balance_loss(l, np.tile([0, 1], (50, 1))) - 4.0) < 1e-12
+    assert O.load_balance_loss(np.zeros((0, 8)), np.zeros((0, 2), dtype=np.int64)) == 0.0
+
+
 # --------------------------------------------------------------------------- experts
 
 
