@@ -238,7 +238,29 @@ def main():
             "counts": counts, "slot_shares": [c / (T * k) for c in counts],
             "rows_needed": needed, "rows_issued_gemm": gemm_rows, "rows_issued_tails": tail_rows,
             "tile_padding_waste": (gemm_rows + tail_rows) / needed - 1.0}
-        del layer, L
+        # capacity factor 1.0: each expert keeps at most T*k/E slots
+        cap = T * k // E
+        layer_cap = moe.FFN(L["x"], L["w_gate"], L["w1"], L["w3"], L["w2"], logit_bias=L["logit_bias"],
+                            capacity=cap)
+        sec_cap = time_layer(layer_cap, args.steps, args.warmup, torch)
+        kept = sum(min(c, cap) for c in counts)
+        # the load-balancing loss on this layer's scores (one small launch)
+        idx_l, _, logits_l = moe.router_topk(L["x"], L["w_gate"], L["logit_bias"], return_logits=True)
+        loss = moe.load_balance_loss(logits_l, idx_l)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(20):
+            moe.load_balance_loss(logits_l, idx_l)
+        ev1.record()
+        torch.cuda.synchronize()
+        result["prefill_skewed"]["capacity_factor_1"] = {
+            "capacity": cap, "ms_per_layer": sec_cap * 1e3, "tokens_per_s": T / sec_cap,
+            "slots_kept": kept, "slots_dropped": T * k - kept, "dropped_fraction": 1.0 - kept / (T * k)}
+        result["prefill_skewed"]["load_balance_loss"] = {"value": float(loss.cpu()[0]),
+                                                          "us_per_call": ev0.elapsed_time(ev1) * 1e3 / 20}
+        _log(f"prefill_skewed with capacity {cap}: {sec_cap * 1e3:.3f} ms/layer, "
+             f"{T * k - kept} of {T * k} slots dropped; load-balance loss {float(loss.cpu()[0]):.4f}")
+        del layer, layer_cap, L
         torch.cuda.empty_cache()
 
     if args.only in ("decode", "all"):

@@ -69,6 +69,15 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  * kernels. */
 typedef enum { MOE_VARIANT_AUTO = 0, MOE_VARIANT_DECODE = 1, MOE_VARIANT_PREFILL = 2 } moe_variant;
 
+/* Expert capacity (moe_dims.capacity = C > 0): each expert keeps its first C
+ * slots in slot order (slot s = t*k + j: earlier tokens first, a token's
+ * larger score before its smaller) and drops the rest; a dropped slot adds
+ * nothing to its token's output and the token's other gate is not
+ * renormalised (a token with both slots dropped outputs zero).  Reading of
+ * "Mixtral & Sparse MoE (2024) > The Solution" (mbrenndoerfer.com),
+ * load-balancing paragraph: capacity constraints limit the tokens routed to
+ * each expert (the page gives no rule for which; this is the plainest). */
+
 /* Gates of the two kept experts.  PAIR (Mixtral, the default): softmax over
  * the kept pair with every other score at -inf, g_a = 1/(1+exp(l_b-l_a)),
  * g_b = 1 - g_a ("Mixtral of Experts", azimuth.plus, router paragraph).
@@ -88,6 +97,7 @@ typedef struct {
   int32_t dtype;    /* moe_dtype */
   int32_t variant;  /* moe_variant */
   int32_t gating;   /* moe_gating (0 = PAIR) */
+  int32_t capacity; /* slots each expert keeps, >= 0; 0 = no limit (dropless, Mixtral) */
 } moe_dims;
 
 /* Human-readable name of a status code (static string). */
@@ -119,9 +129,11 @@ moe_status moe_router_topk(const moe_dims* dims, const void* x, const void* w_ga
  *   topk_idx [T, k] int32 (values must lie in [0, E); other values are
  *   undefined behaviour).
  *   Outputs: expert_offsets [E + 1] int32 (exclusive prefix sum of the per-
- *   expert counts; offsets[E] = T * k), sorted_slots [T * k] int32 (slots of
- *   expert 0 in increasing slot id, then expert 1, ...: a stable order),
- *   slot_rows [T * k] int32 (inverse: position of slot s in sorted_slots).
+ *   expert rows; offsets[E] = T * k without a capacity), sorted_slots
+ *   [T * k] int32 (slots of expert 0 in increasing slot id, then expert 1,
+ *   ...: a stable order; entries past offsets[E] are left as they were),
+ *   slot_rows [T * k] int32 (inverse: position of slot s in sorted_slots, or
+ *   -1 for a slot dropped by dims->capacity).
  *   Deterministic.  Runs as one workgroup.
  */
 moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* expert_offsets,
@@ -185,6 +197,21 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
                            void* y, int32_t* topk_idx_out, float* topk_w_out,
                            int32_t* expert_counts_out, void* workspace, size_t* workspace_bytes,
                            void* stream);
+
+/*
+ * Auxiliary load-balancing loss, loss[0] = E * sum_e f_e * P_e, with f_e the
+ * fraction of the T * k slots whose router choice is expert e (before any
+ * capacity) and P_e the mean over tokens of the softmax over all E scores at
+ * e: 1 for an even router, up to E when the work collapses onto one expert.
+ * "Mixtral & Sparse MoE (2024) > The Solution", load-balancing paragraph
+ * (auxiliary losses push towards an even spread of work; the page gives no
+ * formula, this is the usual product form).
+ *   logits [T, E] fp32 (moe_router_topk's optional output), topk_idx [T, k]
+ *   int32, loss: one fp32 in device memory.  One workgroup, deterministic
+ *   (fixed reduction order).  T == 0: nothing is enqueued (loss untouched).
+ */
+moe_status moe_load_balance_loss(const moe_dims* dims, const float* logits, const int32_t* topk_idx,
+                                 float* loss, void* stream);
 
 /*
  * Glue between stacked layers (not part of the MoE layer itself; the

@@ -47,6 +47,7 @@ moe_status check_dims(const moe_dims* dims) {
   if (dims->dtype != MOE_F32 && dims->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (dims->variant < MOE_VARIANT_AUTO || dims->variant > MOE_VARIANT_PREFILL) return MOE_ERR_UNSUPPORTED;
   if (dims->gating != MOE_GATING_PAIR && dims->gating != MOE_GATING_FULL) return MOE_ERR_UNSUPPORTED;
+  if (dims->capacity < 0) return MOE_ERR_INVALID_ARGUMENT;
   if (dims->T > (int64_t{1} << 30) / dims->k) return MOE_ERR_UNSUPPORTED;  // slot ids are int32
   // Largest row offset of h / y_rows must fit comfortably in int64 (always true) and
   // element offsets r*f, r*d are formed in int64 on the device.
@@ -239,7 +240,8 @@ moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* e
   if (!aligned(topk_idx, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_slots, 4) || !aligned(slot_rows, 4))
     return MOE_ERR_INVALID_ARGUMENT;
   return hip_status(moe::launch_permute(topk_idx, static_cast<int32_t>(dims->T * dims->k), expert_offsets,
-                                        sorted_slots, slot_rows, nullptr, static_cast<hipStream_t>(stream)));
+                                        sorted_slots, slot_rows, nullptr, dims->capacity,
+                                        static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_grouped_swiglu(const moe_dims* dims, const void* x, const int32_t* expert_offsets,
@@ -324,8 +326,8 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
   if (dims->T <= kDecodeMaxTokens) {
     // Small batch: routing and permutation in one workgroup.
     st = hip_status(moe::launch_route_permute(dims->dtype, x, w_gate, logit_bias, idx, w,
-                                              static_cast<int32_t>(dims->T), dims->d, dims->gating, offs, sorted,
-                                              rows, expert_counts_out, s));
+                                              static_cast<int32_t>(dims->T), dims->d, dims->gating,
+                                              dims->capacity, offs, sorted, rows, expert_counts_out, s));
     if (st != MOE_OK) return st;
     // (bf16 decode then runs the streaming up and down projections through
     // run_experts below.)
@@ -333,7 +335,7 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
     st = run_router(dims, x, w_gate, logit_bias, idx, w, nullptr, s);
     if (st != MOE_OK) return st;
     st = hip_status(moe::launch_permute(idx, static_cast<int32_t>(dims->T * dims->k), offs, sorted, rows,
-                                        expert_counts_out, s));
+                                        expert_counts_out, dims->capacity, s));
     if (st != MOE_OK) return st;
   }
   if (dims->dtype == MOE_BF16 && !use_decode(dims)) {
@@ -363,6 +365,16 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
   st = run_experts(dims, x, offs, sorted, w1, w3, w2, h, y_rows, s);
   if (st != MOE_OK) return st;
   return run_combine(dims, y_rows, rows, w, y, s);
+}
+
+moe_status moe_load_balance_loss(const moe_dims* dims, const float* logits, const int32_t* topk_idx, float* loss,
+                                 void* stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (dims->T == 0) return MOE_OK;
+  if (!logits || !topk_idx || !loss) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(loss, 4)) return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(moe::launch_load_balance_loss(logits, topk_idx, dims->T, loss, static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_rmsnorm_residual(int64_t T, int32_t d, float* resid, const void* y_add, void* u_out, float eps,

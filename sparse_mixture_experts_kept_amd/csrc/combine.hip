@@ -6,8 +6,9 @@
 // "Mixtral of Experts" (azimuth.plus), router paragraph: the gates set how
 // much each expert contributes.  Gather form of the scatter-add: each token
 // reads its two rows of y_rows (found through slot_rows) and adds them in
-// slot order, so the result is deterministic.  HBM-bound: 2*d*4 bytes read
-// and d*elem bytes written per token.
+// slot order, so the result is deterministic.  A slot dropped by an expert
+// capacity (slot_rows = -1) adds nothing.  HBM-bound: 2*d*4 bytes read and
+// d*elem bytes written per token.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -29,11 +30,12 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     const int64_t r1 = slot_rows[2 * t + 1];
     const float g0 = topk_w[2 * t];
     const float g1 = topk_w[2 * t + 1];
-    float4 a = *reinterpret_cast<const float4*>(y_rows + r0 * d + c);
-    float4 b = *reinterpret_cast<const float4*>(y_rows + r1 * d + c);
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 a = r0 >= 0 ? *reinterpret_cast<const float4*>(y_rows + r0 * d + c) : zero;
+    float4 b = r1 >= 0 ? *reinterpret_cast<const float4*>(y_rows + r1 * d + c) : zero;
     if (y_rows2) {  // second partial sum of a split reduction, added first
-      const float4 a2 = *reinterpret_cast<const float4*>(y_rows2 + r0 * d + c);
-      const float4 b2 = *reinterpret_cast<const float4*>(y_rows2 + r1 * d + c);
+      const float4 a2 = r0 >= 0 ? *reinterpret_cast<const float4*>(y_rows2 + r0 * d + c) : zero;
+      const float4 b2 = r1 >= 0 ? *reinterpret_cast<const float4*>(y_rows2 + r1 * d + c) : zero;
       a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
       b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
     }

@@ -18,8 +18,12 @@ constexpr int kGatingFull = 1;  // softmax over all scores, pair not renormalise
 hipError_t launch_router(int dtype, const void* x, const void* wg, const float* bias, int32_t* idx, float* w,
                          float* logits, int64_t T, int d, int gating, int n_cu, hipStream_t s);
 
+// capacity > 0: each expert keeps its first `capacity` slots (slot order);
+// dropped slots get slot_rows = -1.
 hipError_t launch_permute(const int32_t* idx, int32_t n_slots, int32_t* offsets, int32_t* sorted_slots,
-                          int32_t* slot_rows, int32_t* counts_out, hipStream_t s);
+                          int32_t* slot_rows, int32_t* counts_out, int capacity, hipStream_t s);
+// loss[0] = E * sum_e f_e * P_e from the scores [T, E] and the pairs [T, k].
+hipError_t launch_load_balance_loss(const float* logits, const int32_t* idx, int64_t T, float* loss, hipStream_t s);
 
 // Expert projections.  up: h = SiLU(x w1^T) * (x w3^T) over the gathered
 // rows; down: y_rows = h w2^T.  n_slots = T * k.
@@ -94,7 +98,7 @@ hipError_t launch_down_decode_stream(const bf16_t* h, const int32_t* offs, const
 
 // Small batches (T <= 64): routing + permutation in one workgroup.
 hipError_t launch_route_permute(int dtype, const void* x, const void* wg, const float* bias, int32_t* idx, float* w,
-                                int32_t T, int d, int gating, int32_t* offsets, int32_t* sorted_slots,
+                                int32_t T, int d, int gating, int capacity, int32_t* offsets, int32_t* sorted_slots,
                                 int32_t* slot_rows, int32_t* counts_out, hipStream_t s);
 
 // y_rows2 (optional): a second partial-sum buffer added to y_rows first.

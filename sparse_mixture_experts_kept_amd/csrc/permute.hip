@@ -14,7 +14,10 @@
 // of each wave (shuffles) and over the 16 waves (LDS) gives every thread the
 // number of earlier slots of each expert, and the thread places its 8 slots
 // in order.  Stable (slot order within an expert) and free of atomics, so the
-// result is deterministic.
+// result is deterministic.  With an expert capacity C > 0 a slot whose rank
+// among its expert's slots is C or more is dropped: it gets no row and
+// slot_rows = -1 (reading of the load-balancing paragraph of "Mixtral &
+// Sparse MoE (2024) > The Solution": a capacity limits the tokens per expert).
 #include "common.hpp"
 #include "launch.hpp"
 #include "permute_dev.hpp"
@@ -44,10 +47,11 @@ __global__ void __launch_bounds__(kPermThreads) permute_kernel(const int32_t* __
                                                                int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ sorted_slots,
                                                                int32_t* __restrict__ slot_rows,
-                                                               int32_t* __restrict__ counts_out) {
+                                                               int32_t* __restrict__ counts_out, int capacity) {
   __shared__ int32_t wave_sum[kPermWaves][kExperts];
   __shared__ uint32_t wave_pk[kPermWaves][kExperts / 2];
-  __shared__ int32_t base_s[kExperts];
+  __shared__ int32_t base_s[kExperts];  // the expert's slots in earlier chunks (its rank so far)
+  __shared__ int32_t off_s[kExperts];   // the expert's first row
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
 
   // Pass 1: counts per expert.
@@ -76,9 +80,10 @@ __global__ void __launch_bounds__(kPermThreads) permute_kernel(const int32_t* __
       int tot = 0;
       for (int w = 0; w < kPermWaves; ++w) tot += wave_sum[w][e];
       offsets[e] = run;
-      base_s[e] = run;
+      off_s[e] = run;
+      base_s[e] = 0;
       if (counts_out) counts_out[e] = tot;
-      run += tot;
+      run += kept_rows(tot, capacity);
     }
     offsets[kExperts] = run;
   }
@@ -130,7 +135,7 @@ __global__ void __launch_bounds__(kPermThreads) permute_kernel(const int32_t* __
         total[k] += v;
       }
     }
-    int next[kExperts];  // position of this thread's next slot of each expert
+    int next[kExperts];  // rank of this thread's next slot of each expert
 #pragma unroll
     for (int k = 0; k < kExperts / 2; ++k) {
       const uint32_t ex = before[k] + inc[k] - pk[k];  // exclusive prefix
@@ -141,12 +146,19 @@ __global__ void __launch_bounds__(kPermThreads) permute_kernel(const int32_t* __
     for (int i = 0; i < kSlotsPerThread; ++i) {
       const int e = ids[i];
       if (e < 0) continue;
-      int pos = 0;
+      int r = 0, off = 0;
 #pragma unroll
       for (int ee = 0; ee < kExperts; ++ee)
-        if (e == ee) pos = next[ee]++;
-      sorted_slots[pos] = s0 + i;
-      slot_rows[s0 + i] = pos;
+        if (e == ee) {
+          r = next[ee]++;
+          off = off_s[ee];
+        }
+      if (capacity > 0 && r >= capacity) {
+        slot_rows[s0 + i] = -1;  // dropped
+      } else {
+        sorted_slots[off + r] = s0 + i;
+        slot_rows[s0 + i] = off + r;
+      }
     }
     __syncthreads();  // every thread has read base_s and wave_pk of this chunk
     if (tid < kExperts) {
@@ -162,20 +174,21 @@ __global__ void __launch_bounds__(kPermThreads) permute_small_kernel(const int32
                                                                      int32_t* __restrict__ offsets,
                                                                      int32_t* __restrict__ sorted_slots,
                                                                      int32_t* __restrict__ slot_rows,
-                                                                     int32_t* __restrict__ counts_out) {
-  permute_block(idx, n_slots, offsets, sorted_slots, slot_rows, counts_out);
+                                                                     int32_t* __restrict__ counts_out,
+                                                                     int capacity) {
+  permute_block(idx, n_slots, offsets, sorted_slots, slot_rows, counts_out, capacity);
 }
 
 }  // namespace
 
 hipError_t launch_permute(const int32_t* idx, int32_t n_slots, int32_t* offsets, int32_t* sorted_slots,
-                          int32_t* slot_rows, int32_t* counts_out, hipStream_t s) {
+                          int32_t* slot_rows, int32_t* counts_out, int capacity, hipStream_t s) {
   if (n_slots <= kPermThreads)
     hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kPermThreads), 0, s, idx, n_slots, offsets, sorted_slots,
-                       slot_rows, counts_out);
+                       slot_rows, counts_out, capacity);
   else
     hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, idx, n_slots, offsets, sorted_slots,
-                       slot_rows, counts_out);
+                       slot_rows, counts_out, capacity);
   return hipGetLastError();
 }
 

@@ -13,14 +13,22 @@ constexpr int kPermWaves = kPermThreads / kWave;
 // Ids outside [0, E) are skipped (never used as an index).
 __device__ __forceinline__ int valid_expert(int e) { return (e >= 0 && e < kExperts) ? e : -1; }
 
+// Rows an expert with `count` routed slots keeps under `capacity` (0: all).
+__device__ __forceinline__ int kept_rows(int count, int capacity) {
+  return (capacity > 0 && count > capacity) ? capacity : count;
+}
+
 // The whole permutation by one workgroup of kPermThreads threads.  idx is
 // read from global memory (it may have been written by this workgroup before
-// a __syncthreads()).
+// a __syncthreads()).  capacity > 0: each expert keeps its first `capacity`
+// slots in slot order; the others get slot_rows = -1 and no row (offsets
+// count kept rows; counts_out the routed slots).
 __device__ inline void permute_block(const int32_t* __restrict__ idx, int32_t n_slots, int32_t* __restrict__ offsets,
                               int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_rows,
-                              int32_t* __restrict__ counts_out) {
+                              int32_t* __restrict__ counts_out, int capacity) {
   __shared__ int32_t hist[kExperts];
-  __shared__ int32_t base[kExperts];
+  __shared__ int32_t base[kExperts];   // slots of the expert in earlier chunks (its rank so far)
+  __shared__ int32_t off_s[kExperts];  // the expert's first row
   __shared__ int32_t wave_cnt[kPermWaves][kExperts];
 
   const int tid = threadIdx.x;
@@ -46,9 +54,10 @@ __device__ inline void permute_block(const int32_t* __restrict__ idx, int32_t n_
     int run = 0;
     for (int e = 0; e < kExperts; ++e) {
       offsets[e] = run;
-      base[e] = run;
+      off_s[e] = run;
+      base[e] = 0;
       if (counts_out) counts_out[e] = hist[e];
-      run += hist[e];
+      run += kept_rows(hist[e], capacity);
     }
     offsets[kExperts] = run;
   }
@@ -68,10 +77,14 @@ __device__ inline void permute_block(const int32_t* __restrict__ idx, int32_t n_
     }
     __syncthreads();
     if (e >= 0) {
-      int pos = base[e] + rank;
-      for (int w = 0; w < wave; ++w) pos += wave_cnt[w][e];
-      sorted_slots[pos] = s;
-      slot_rows[s] = pos;
+      int r = base[e] + rank;  // the slot's rank among its expert's slots
+      for (int w = 0; w < wave; ++w) r += wave_cnt[w][e];
+      if (capacity > 0 && r >= capacity) {
+        slot_rows[s] = -1;  // dropped
+      } else {
+        sorted_slots[off_s[e] + r] = s;
+        slot_rows[s] = off_s[e] + r;
+      }
     }
     __syncthreads();
     if (tid < kExperts) {

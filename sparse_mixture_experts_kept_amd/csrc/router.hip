@@ -228,7 +228,7 @@ __global__ void __launch_bounds__(kPermThreads) route_permute_kernel(
     const T* __restrict__ x, const T* __restrict__ wg, const float* __restrict__ bias, int32_t* __restrict__ idx_out,
     float* __restrict__ w_out, int32_t T_tokens, int d, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_rows, int32_t* __restrict__ counts_out,
-    int gating) {
+    int gating, int capacity) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* wg_s = reinterpret_cast<T*>(smem_raw);
   float b[kExperts];
@@ -237,7 +237,7 @@ __global__ void __launch_bounds__(kPermThreads) route_permute_kernel(
   for (int t = threadIdx.x / kWave; t < T_tokens; t += kPermWaves)
     route_token(x + static_cast<int64_t>(t) * d, wg_s, b, d, lane, gating, idx_out + 2 * t, w_out + 2 * t, nullptr);
   __syncthreads();  // the ids written above are read back by permute_block
-  permute_block(idx_out, T_tokens * kTopK, offsets, sorted_slots, slot_rows, counts_out);
+  permute_block(idx_out, T_tokens * kTopK, offsets, sorted_slots, slot_rows, counts_out, capacity);
 }
 
 hipError_t launch_router(int dtype, const void* x, const void* wg, const float* bias, int32_t* idx, float* w,
@@ -287,7 +287,7 @@ __global__ void __launch_bounds__(kPermThreads) route_permute_mfma_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const float* __restrict__ bias,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t T_tokens, int d, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_rows, int32_t* __restrict__ counts_out,
-    int gating) {
+    int gating, int capacity) {
   constexpr int kGroups = 4;  // T <= 64
   __shared__ f32x4 part[kPermWaves][kGroups][kWave];
   __shared__ int32_t idx_s[kGroups * 16 * kTopK];
@@ -353,7 +353,7 @@ __global__ void __launch_bounds__(kPermThreads) route_permute_mfma_kernel(
     }
   }
   __syncthreads();
-  permute_block(idx_s, T_tokens * kTopK, offsets, sorted_slots, slot_rows, counts_out);
+  permute_block(idx_s, T_tokens * kTopK, offsets, sorted_slots, slot_rows, counts_out, capacity);
 }
 
 }  // namespace moe
@@ -361,12 +361,12 @@ __global__ void __launch_bounds__(kPermThreads) route_permute_mfma_kernel(
 namespace moe {
 
 hipError_t launch_route_permute(int dtype, const void* x, const void* wg, const float* bias, int32_t* idx, float* w,
-                                int32_t T, int d, int gating, int32_t* offsets, int32_t* sorted_slots,
+                                int32_t T, int d, int gating, int capacity, int32_t* offsets, int32_t* sorted_slots,
                                 int32_t* slot_rows, int32_t* counts_out, hipStream_t s) {
   if (dtype == kDtypeBF16) {
     hipLaunchKernelGGL(route_permute_mfma_kernel, dim3(1), dim3(kPermThreads), 0, s, static_cast<const bf16_t*>(x),
                        static_cast<const bf16_t*>(wg), bias, idx, w, T, d, offsets, sorted_slots, slot_rows,
-                       counts_out, gating);
+                       counts_out, gating, capacity);
     return hipGetLastError();
   }
   const size_t lds = kExperts * static_cast<size_t>(d) * (dtype == kDtypeBF16 ? 2 : 4);
@@ -379,11 +379,86 @@ hipError_t launch_route_permute(int dtype, const void* x, const void* wg, const 
   if (dtype == kDtypeBF16)
     hipLaunchKernelGGL(route_permute_kernel<bf16_t>, dim3(1), dim3(kPermThreads), lds, s,
                        static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(wg), bias, idx, w, T, d, offsets,
-                       sorted_slots, slot_rows, counts_out, gating);
+                       sorted_slots, slot_rows, counts_out, gating, capacity);
   else
     hipLaunchKernelGGL(route_permute_kernel<float>, dim3(1), dim3(kPermThreads), lds, s,
                        static_cast<const float*>(x), static_cast<const float*>(wg), bias, idx, w, T, d, offsets,
-                       sorted_slots, slot_rows, counts_out, gating);
+                       sorted_slots, slot_rows, counts_out, gating, capacity);
+  return hipGetLastError();
+}
+
+}  // namespace moe
+
+namespace moe {
+
+// Load-balancing loss E * sum_e f_e * P_e (f_e: fraction of the T*k slots
+// routed to e; P_e: mean over tokens of the softmax over all E scores at e),
+// the reading of the auxiliary losses of "Mixtral & Sparse MoE (2024) > The
+// Solution" (load-balancing paragraph).  One workgroup: thread i takes tokens
+// i, i + 1024, ...; the per-thread sums are added over the lanes of a wave
+// (butterfly) and then over the waves in wave order, so the result is
+// deterministic.
+__global__ void __launch_bounds__(kPermThreads) load_balance_loss_kernel(const float* __restrict__ logits,
+                                                                          const int32_t* __restrict__ idx,
+                                                                          int64_t T, float* __restrict__ loss) {
+  __shared__ float wsum[kPermWaves][2 * kExperts];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  float p[kExperts], n[kExperts];
+#pragma unroll
+  for (int e = 0; e < kExperts; ++e) p[e] = n[e] = 0.0f;
+  for (int64_t t = tid; t < T; t += kPermThreads) {
+    float l[kExperts];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < kExperts; ++e) {
+      l[e] = logits[t * kExperts + e];
+      mx = fmaxf(mx, l[e]);
+    }
+    float z = 0.0f;
+#pragma unroll
+    for (int e = 0; e < kExperts; ++e) {
+      l[e] = expf(l[e] - mx);
+      z += l[e];
+    }
+    const float rz = 1.0f / z;
+#pragma unroll
+    for (int e = 0; e < kExperts; ++e) p[e] += l[e] * rz;
+#pragma unroll
+    for (int j = 0; j < kTopK; ++j) {
+      const int e = idx[t * kTopK + j];
+#pragma unroll
+      for (int ee = 0; ee < kExperts; ++ee) n[ee] += e == ee ? 1.0f : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < kExperts; ++e) {
+    p[e] = wave_sum(p[e]);
+    n[e] = wave_sum(n[e]);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int e = 0; e < kExperts; ++e) {
+      wsum[wave][e] = p[e];
+      wsum[wave][kExperts + e] = n[e];
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float acc = 0.0f;
+    for (int e = 0; e < kExperts; ++e) {
+      float pe = 0.0f, ne = 0.0f;
+      for (int w = 0; w < kPermWaves; ++w) {
+        pe += wsum[w][e];
+        ne += wsum[w][kExperts + e];
+      }
+      acc += (ne / static_cast<float>(T * kTopK)) * (pe / static_cast<float>(T));
+    }
+    loss[0] = T > 0 ? static_cast<float>(kExperts) * acc : 0.0f;
+  }
+}
+
+hipError_t launch_load_balance_loss(const float* logits, const int32_t* idx, int64_t T, float* loss, hipStream_t s) {
+  hipLaunchKernelGGL(load_balance_loss_kernel, dim3(1), dim3(kPermThreads), 0, s, logits, idx, T, loss);
   return hipGetLastError();
 }
 

@@ -23,7 +23,8 @@ GATING_PAIR, GATING_FULL = 0, 1  # softmax over the kept pair / over all experts
 E_EXPERTS, TOP_K = 8, 2
 
 EXPORTED = ("moe_status_string", "moe_version", "moe_router_topk", "moe_permute", "moe_grouped_swiglu",
-            "moe_expert_up", "moe_expert_down", "moe_combine", "moe_ffn_forward", "moe_rmsnorm_residual")
+            "moe_expert_up", "moe_expert_down", "moe_combine", "moe_ffn_forward", "moe_rmsnorm_residual",
+            "moe_load_balance_loss")
 
 
 class MoeError(RuntimeError):
@@ -35,7 +36,7 @@ class MoeError(RuntimeError):
 class MoeDims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("f", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("dtype", ctypes.c_int32), ("variant", ctypes.c_int32),
-                ("gating", ctypes.c_int32)]
+                ("gating", ctypes.c_int32), ("capacity", ctypes.c_int32)]
 
 
 _lib = None
@@ -63,6 +64,7 @@ def load_library(path: str = LIB_PATH):
         "moe_combine": (I32, [D, P, P, P, P, P]),
         "moe_ffn_forward": (I32, [D, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "moe_rmsnorm_residual": (I32, [I64, I32, P, P, P, F32, I32, P]),
+        "moe_load_balance_loss": (I32, [D, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -93,10 +95,11 @@ def torch_dtype(code: int) -> torch.dtype:
     return torch.bfloat16 if code == MOE_BF16 else torch.float32
 
 
-def make_dims(T, d, f, dtype, variant=VARIANT_AUTO, E=E_EXPERTS, k=TOP_K, gating=GATING_PAIR) -> MoeDims:
+def make_dims(T, d, f, dtype, variant=VARIANT_AUTO, E=E_EXPERTS, k=TOP_K, gating=GATING_PAIR,
+              capacity=0) -> MoeDims:
     if isinstance(dtype, torch.dtype):
         dtype = dtype_code(dtype)
-    return MoeDims(int(T), int(d), int(f), int(E), int(k), int(dtype), int(variant), int(gating))
+    return MoeDims(int(T), int(d), int(f), int(E), int(k), int(dtype), int(variant), int(gating), int(capacity))
 
 
 def ptr(t):
@@ -114,10 +117,10 @@ def stream_handle():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _layer_dims(x, w1, variant, gating=GATING_PAIR):
+def _layer_dims(x, w1, variant, gating=GATING_PAIR, capacity=0):
     T, d = x.shape
     f = w1.shape[1]
-    return make_dims(T, d, f, x.dtype, variant, gating=gating)
+    return make_dims(T, d, f, x.dtype, variant, gating=gating, capacity=capacity)
 
 
 # --------------------------------------------------------------------------- staged calls
@@ -136,11 +139,12 @@ def router_topk(x, w_gate, logit_bias=None, return_logits=False, gating=GATING_P
     return (idx, w, logits) if return_logits else (idx, w)
 
 
-def permute(topk_idx, d=128, f=128):
-    """expert_offsets [9], sorted_slots [T*2], slot_rows [T*2] (int32)."""
+def permute(topk_idx, d=128, f=128, capacity=0):
+    """expert_offsets [9], sorted_slots [T*2], slot_rows [T*2] (int32; -1 for
+    a slot dropped by the expert capacity)."""
     lib = load_library()
     T = topk_idx.shape[0]
-    dims = make_dims(T, d, f, MOE_BF16)
+    dims = make_dims(T, d, f, MOE_BF16, capacity=capacity)
     offs = torch.zeros((E_EXPERTS + 1,), dtype=torch.int32, device=topk_idx.device)
     sorted_slots = torch.empty((T * TOP_K,), dtype=torch.int32, device=topk_idx.device)
     slot_rows = torch.empty((T * TOP_K,), dtype=torch.int32, device=topk_idx.device)
@@ -222,9 +226,9 @@ class FFN:
     and ``counts`` may be supplied to share buffers between layers."""
 
     def __init__(self, x, w_gate, w1, w3, w2, logit_bias=None, variant=VARIANT_AUTO, routing=True, y=None,
-                 workspace=None, counts=None, gating=GATING_PAIR):
+                 workspace=None, counts=None, gating=GATING_PAIR, capacity=0):
         self.lib = load_library()
-        self.dims = _layer_dims(x, w1, variant, gating)
+        self.dims = _layer_dims(x, w1, variant, gating, capacity)
         T, d = x.shape
         self.args = (x, w_gate, logit_bias, w1, w3, w2)
         self.y = y if y is not None else torch.empty((T, d), dtype=x.dtype, device=x.device)
@@ -248,13 +252,25 @@ class FFN:
 
 
 def ffn_forward(x, w_gate, w1, w3, w2, logit_bias=None, variant=VARIANT_AUTO, return_routing=False,
-                gating=GATING_PAIR):
-    """y [T, d] (x's dtype); with return_routing also (topk_idx, topk_w, counts)."""
-    layer = FFN(x, w_gate, w1, w3, w2, logit_bias, variant, routing=True, gating=gating)
+                gating=GATING_PAIR, capacity=0):
+    """y [T, d] (x's dtype); with return_routing also (topk_idx, topk_w, counts).
+    counts are the routed slots per expert (before any capacity)."""
+    layer = FFN(x, w_gate, w1, w3, w2, logit_bias, variant, routing=True, gating=gating, capacity=capacity)
     y = layer()
     if return_routing:
         return y, layer.idx, layer.w, layer.counts
     return y
+
+
+def load_balance_loss(logits, topk_idx):
+    """E * sum_e f_e * P_e as a one-element fp32 tensor (see moe.h)."""
+    lib = load_library()
+    T = logits.shape[0]
+    dims = make_dims(T, 128, 128, MOE_F32)
+    loss = torch.zeros((1,), dtype=torch.float32, device=logits.device)
+    _check("moe_load_balance_loss", lib.moe_load_balance_loss(ctypes.byref(dims), ptr(logits), ptr(topk_idx),
+                                                              ptr(loss), stream_handle()))
+    return loss
 
 
 def rmsnorm_residual(resid, y_add, out_dtype, eps=1e-5):

@@ -70,6 +70,7 @@ def _dims(**kw):
     (dict(variant=3), moe.MOE_ERR_UNSUPPORTED),
     (dict(gating=2), moe.MOE_ERR_UNSUPPORTED),
     (dict(gating=-1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(capacity=-1), moe.MOE_ERR_INVALID_ARGUMENT),
     (dict(T=1 << 31), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_bad_dims_are_rejected(kw, status):
@@ -82,6 +83,7 @@ def test_bad_dims_are_rejected(kw, status):
     assert lib.moe_combine(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, None) == status
     assert lib.moe_ffn_forward(ctypes.byref(dims), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, None,
                                None, ctypes.byref(n), None) == status
+    assert lib.moe_load_balance_loss(ctypes.byref(dims), FAKE, FAKE, FAKE, None) == status
 
 
 @needs_no_gpu
@@ -108,6 +110,9 @@ def test_null_and_misaligned_pointers():
                                   None) == INV
     assert lib.moe_combine(ctypes.byref(dims), FAKE, FAKE, FAKE, None, None) == INV
     assert lib.moe_combine(ctypes.byref(dims), MISALIGNED, FAKE, FAKE, FAKE, None) == INV
+    assert lib.moe_load_balance_loss(ctypes.byref(dims), None, FAKE, FAKE, None) == INV
+    assert lib.moe_load_balance_loss(ctypes.byref(dims), FAKE, FAKE, None, None) == INV
+    assert lib.moe_load_balance_loss(ctypes.byref(dims), MISALIGNED, FAKE, FAKE, None) == INV
     assert lib.moe_rmsnorm_residual(4, 256, None, None, FAKE, 1e-5, 1, None) == INV
     assert lib.moe_rmsnorm_residual(-1, 256, FAKE, None, FAKE, 1e-5, 1, None) == INV
     assert lib.moe_rmsnorm_residual(4, 250, FAKE, None, FAKE, 1e-5, 1, None) == moe.MOE_ERR_UNSUPPORTED
@@ -161,6 +166,7 @@ def test_zero_tokens_is_a_no_op():
     assert lib.moe_ffn_forward(ctypes.byref(dims), None, None, None, None, None, None, None, None, None, None,
                                None, ctypes.byref(n), None) == moe.MOE_OK
     assert lib.moe_rmsnorm_residual(0, 256, None, None, None, 1e-5, 1, None) == moe.MOE_OK
+    assert lib.moe_load_balance_loss(ctypes.byref(dims), None, None, None, None) == moe.MOE_OK
 
 
 def test_binding_refuses_cpu_tensors():

@@ -56,13 +56,14 @@ def _check_routing(idx_gpu, w_gpu, ref, tokens=None, gating="pair"):
 _GATING = {"pair": moe.GATING_PAIR, "full": moe.GATING_FULL}
 
 
-def run_and_check(layer, variant=moe.VARIANT_AUTO, sample=None, gating="pair"):
+def run_and_check(layer, variant=moe.VARIANT_AUTO, sample=None, gating="pair", capacity=0):
     """Whole layer on the GPU vs the oracle on all tokens (or a sample)."""
     dims = layer["dims"]
     x = layer["x"]
     y, idx, w, counts = moe.ffn_forward(x, layer["w_gate"], layer["w1"], layer["w3"], layer["w2"],
                                         logit_bias=layer.get("logit_bias"), variant=variant, return_routing=True,
-                                        gating=_GATING[gating])
+                                        gating=_GATING[gating], capacity=capacity)
+    assert capacity == 0 or sample is None  # the capacity depends on every earlier token
     torch.cuda.synchronize()
     idx_g = idx.cpu().numpy().astype(np.int64)
     w_g = w.cpu().numpy().astype(np.float64)
@@ -72,7 +73,8 @@ def run_and_check(layer, variant=moe.VARIANT_AUTO, sample=None, gating="pair"):
     xs = _cpu(x)[tok]
     bias = _cpu(layer.get("logit_bias"))
     widen = _widen_experts(layer)
-    ref = O.moe_ffn(xs, _cpu(layer["w_gate"]), None, None, None, logit_bias=bias, widen_expert=widen, gating=gating)
+    ref = O.moe_ffn(xs, _cpu(layer["w_gate"]), None, None, None, logit_bias=bias, widen_expert=widen, gating=gating,
+                    capacity=capacity)
     clear = _check_routing(idx_g[tok], w_g[tok], ref, gating=gating)
     if sample is None:
         # per-expert counts over the tokens whose routing is decided beyond the tie margin
@@ -81,7 +83,7 @@ def run_and_check(layer, variant=moe.VARIANT_AUTO, sample=None, gating="pair"):
     # outputs, under the assignment the GPU made (identical to the oracle's on clear tokens)
     if not np.array_equal(idx_g[tok], ref["idx"]):
         ref = O.moe_ffn(xs, _cpu(layer["w_gate"]), None, None, None, logit_bias=bias, idx=idx_g[tok],
-                        widen_expert=widen, gating=gating)
+                        widen_expert=widen, gating=gating, capacity=capacity)
     yg = y.float().cpu().numpy().astype(np.float64)[tok]
     err = np.abs(yg - ref["y"]).max() if yg.size else 0.0
     tol = _tol(dims["dtype"], ref["y"])
@@ -377,6 +379,67 @@ def test_full_gating_router_entry_point():
     l64 = O._f64(logits.cpu())
     ref = O.softmax_top_k_gates(l64, idx.cpu().numpy().astype(np.int64))
     np.testing.assert_allclose(w.cpu().numpy(), ref, atol=1e-6, rtol=0)
+
+
+# --------------------------------------------------------------------------- expert capacity, load-balance loss
+
+
+@pytest.mark.parametrize("T,d,f,dtype,variant,capacity", [(300, 256, 512, "bf16", moe.VARIANT_PREFILL, 40),
+                                                          (2100, 256, 512, "bf16", moe.VARIANT_PREFILL, 450),
+                                                          (48, 256, 512, "bf16", moe.VARIANT_DECODE, 6),
+                                                          (200, 256, 384, "bf16", moe.VARIANT_DECODE, 30),
+                                                          (100, 128, 256, "f32", moe.VARIANT_AUTO, 20),
+                                                          (40, 128, 256, "f32", moe.VARIANT_AUTO, 5)])
+def test_capacity_layer(T, d, f, dtype, variant, capacity):
+    # Slots past an expert's capacity are dropped (slot order); every router
+    # and permutation path: chunked permutation (T > 512), ballot form, the
+    # fused small-batch routers, fp32.  The skew makes some experts overflow.
+    layer = _layer(T, d, f, dtype=dtype, seed=500 + T)
+    layer["logit_bias"] = torch.tensor([1.0, 0.5, 0, 0, 0, 0, -0.5, -1.0], device="cuda")
+    out = run_and_check(layer, variant=variant, capacity=capacity)
+    counts = out["counts"].cpu().numpy()
+    assert counts.max() > capacity, counts  # something was dropped
+
+
+def test_capacity_large_enough_changes_nothing():
+    layer = _layer(700, 256, 512, seed=71)
+    y0, idx, w, counts = moe.ffn_forward(layer["x"], layer["w_gate"], layer["w1"], layer["w3"], layer["w2"],
+                                         return_routing=True)
+    y1 = moe.ffn_forward(layer["x"], layer["w_gate"], layer["w1"], layer["w3"], layer["w2"],
+                         capacity=int(counts.max()))
+    assert torch.equal(y0, y1)
+
+
+@pytest.mark.parametrize("T,capacity", [(200, 30), (3000, 500), (3000, 1)])
+def test_capacity_permutation_exact(T, capacity):
+    rng = np.random.default_rng(T + capacity)
+    l = rng.standard_normal((T, 8)) + np.array([1.2, 0.6, 0, 0, 0, 0, -0.6, -1.2])
+    idx = O.select_top_k(l, 2)
+    offs, sorted_slots, slot_rows = moe.permute(torch.from_numpy(idx.astype(np.int32)).cuda(), capacity=capacity)
+    o_offs, o_sorted, o_rows = O.expert_permutation(idx)
+    keep = O.capacity_keep(idx, capacity).reshape(-1)
+    flat = idx.reshape(-1)
+    counts = np.bincount(flat, minlength=8)
+    kept = np.minimum(counts, capacity)
+    exp_offs = np.concatenate([[0], np.cumsum(kept)])
+    rank = o_rows - o_offs[flat]
+    exp_rows = np.where(keep, exp_offs[flat] + rank, -1)
+    np.testing.assert_array_equal(offs.cpu().numpy(), exp_offs)
+    np.testing.assert_array_equal(slot_rows.cpu().numpy(), exp_rows)
+    n = int(exp_offs[-1])
+    got_sorted = sorted_slots.cpu().numpy()[:n]
+    np.testing.assert_array_equal(got_sorted, o_sorted[keep[o_sorted]])
+
+
+@pytest.mark.parametrize("T", [37, 5000])
+def test_load_balance_loss(T):
+    layer = _layer(T, 256, 256, seed=81)
+    layer_bias = torch.tensor([0.8, 0.3, 0, 0, 0, 0, 0, -0.4], device="cuda")
+    idx, w, logits = moe.router_topk(layer["x"], layer["w_gate"], layer_bias, return_logits=True)
+    loss = float(moe.load_balance_loss(logits, idx).cpu()[0])
+    ref = O.load_balance_loss(O._f64(logits.cpu()), idx.cpu().numpy().astype(np.int64))
+    assert abs(loss - ref) <= 1e-5 * ref, (loss, ref)
+    assert loss > 1.0
 
 
 # --------------------------------------------------------------------------- remainder split of the prefill GEMMs
