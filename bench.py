@@ -335,11 +335,15 @@ def main():
 
         sec = time_layer(stack_step, args.stack_steps, 1, torch)
         hist = stack.hist.cpu().tolist()
+        stack.fused = False  # every layer routes its own input: the router as its own launch
+        sec_unfused = time_layer(stack_step, args.stack_steps, 1, torch)
+        stack.fused = True
         flops = w["layers"] * A.layer_flops(w["T"], d, f, E, k)
         _log(f"stack: {sec * 1e3:.1f} ms per {w['layers']}-layer pass")
         result["stack"] = {"workload": "mixtral-moe-ffn-stack", "T": w["T"], "layers": w["layers"],
                            "ms_per_pass": sec * 1e3, "tokens_per_s": w["T"] / sec,
                            "ms_per_layer": sec * 1e3 / w["layers"], "frac_of_bf16_peak": flops / sec / A.PEAK_BF16_FLOPS,
+                           "ms_per_pass_router_unfused": sec_unfused * 1e3,
                            "expert_weight_bytes_resident": w["layers"] * A.expert_weight_bytes(d, f, E),
                            "routing_histograms": hist}
         del stack

@@ -199,6 +199,19 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
                            void* stream);
 
 /*
+ * The whole layer from a routing computed elsewhere (by
+ * moe_rmsnorm_residual_route, or any top-2 pairs and gates): permutation,
+ * both expert projections and the combine, as moe_ffn_forward without its
+ * router.  topk_idx [T, 2] int32 (values in [0, E)), topk_w [T, 2] fp32, as
+ * moe_router_topk writes them; dims->capacity applies; dims->gating is not
+ * used.  Workspace as moe_ffn_forward (same size query).
+ */
+moe_status moe_ffn_forward_routed(const moe_dims* dims, const void* x, const int32_t* topk_idx,
+                                  const float* topk_w, const void* w1, const void* w3, const void* w2,
+                                  void* y, int32_t* expert_counts_out, void* workspace,
+                                  size_t* workspace_bytes, void* stream);
+
+/*
  * Auxiliary load-balancing loss, loss[0] = E * sum_e f_e * P_e, with f_e the
  * fraction of the T * k slots whose router choice is expert e (before any
  * capacity) and P_e the mean over tokens of the softmax over all E scores at
@@ -224,6 +237,20 @@ moe_status moe_load_balance_loss(const moe_dims* dims, const float* logits, cons
  */
 moe_status moe_rmsnorm_residual(int64_t T, int32_t d, float* resid, const void* y_add, void* u_out,
                                 float eps, int32_t dtype, void* stream);
+
+/*
+ * moe_rmsnorm_residual fused with the router of the layer that follows:
+ * resid += y_add (if given), u = resid / sqrt(mean(resid^2) + eps) in
+ * dims->dtype, then that layer's top-2 pair and gates from the rounded u
+ * exactly as moe_router_topk computes them (dims->gating; w_gate [E, d],
+ * logit_bias [E] or NULL), written to topk_idx [T, 2] and topk_w [T, 2].
+ * One read of the residual row serves both steps (the stacked-layer glue
+ * and "Mixtral of Experts", azimuth.plus, router paragraph).  Limits: d <=
+ * 8192 and E * d * elem_size <= 128 KiB.
+ */
+moe_status moe_rmsnorm_residual_route(const moe_dims* dims, float* resid, const void* y_add, void* u_out,
+                                      float eps, const void* w_gate, const float* logit_bias,
+                                      int32_t* topk_idx, float* topk_w, void* stream);
 
 #ifdef __cplusplus
 }

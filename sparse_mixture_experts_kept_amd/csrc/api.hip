@@ -291,14 +291,22 @@ moe_status moe_combine(const moe_dims* dims, const float* y_rows, const int32_t*
   return run_combine(dims, y_rows, slot_rows, topk_w, y, static_cast<hipStream_t>(stream));
 }
 
-moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_gate, const float* logit_bias,
-                           const void* w1, const void* w3, const void* w2, void* y, int32_t* topk_idx_out,
-                           float* topk_w_out, int32_t* expert_counts_out, void* workspace, size_t* workspace_bytes,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The whole layer.  routed_idx / routed_w given: the routing was computed by
+// the caller (e.g. by moe_rmsnorm_residual_route) and the router is skipped.
+moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_gate, const float* logit_bias,
+                            const int32_t* routed_idx, const float* routed_w, const void* w1, const void* w3,
+                            const void* w2, void* y, int32_t* topk_idx_out, float* topk_w_out,
+                            int32_t* expert_counts_out, void* workspace, size_t* workspace_bytes, void* stream) {
+  const bool routed = routed_idx != nullptr;
   moe_status st = check_dims(dims);
   if (st != MOE_OK) return st;
   if (!workspace_bytes) return MOE_ERR_INVALID_ARGUMENT;
-  if (static_cast<size_t>(dims->E) * dims->d * elem_size(dims->dtype) > kRouterLdsLimit) return MOE_ERR_UNSUPPORTED;
+  if (!routed && static_cast<size_t>(dims->E) * dims->d * elem_size(dims->dtype) > kRouterLdsLimit)
+    return MOE_ERR_UNSUPPORTED;
   const Workspace plan = plan_workspace(dims);
   if (!workspace) {
     *workspace_bytes = plan.total;
@@ -306,10 +314,11 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
   }
   if (dims->T == 0) return MOE_OK;
   if (*workspace_bytes < plan.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  if (!x || !w_gate || !w1 || !w3 || !w2 || !y) return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned(workspace, 256) || !aligned(x, 16) || !aligned(w_gate, 16) || !aligned(w1, 16) || !aligned(w3, 16) ||
-      !aligned(w2, 16) || !aligned(y, 16) || (logit_bias && !aligned(logit_bias, 16)) ||
+  if (!x || (!routed && !w_gate) || (routed && !routed_w) || !w1 || !w3 || !w2 || !y) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(workspace, 256) || !aligned(x, 16) || (w_gate && !aligned(w_gate, 16)) || !aligned(w1, 16) ||
+      !aligned(w3, 16) || !aligned(w2, 16) || !aligned(y, 16) || (logit_bias && !aligned(logit_bias, 16)) ||
       (topk_idx_out && !aligned(topk_idx_out, 8)) || (topk_w_out && !aligned(topk_w_out, 8)) ||
+      (routed_idx && !aligned(routed_idx, 8)) || (routed_w && !aligned(routed_w, 8)) ||
       (expert_counts_out && !aligned(expert_counts_out, 4)))
     return MOE_ERR_INVALID_ARGUMENT;
 
@@ -317,13 +326,19 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
   char* ws = static_cast<char*>(workspace);
   int32_t* idx = topk_idx_out ? topk_idx_out : reinterpret_cast<int32_t*>(ws + plan.idx);
   float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + plan.w);
+  const int32_t* pair = routed ? routed_idx : idx;
+  const float* gate = routed ? routed_w : w;
   int32_t* offs = reinterpret_cast<int32_t*>(ws + plan.offsets);
   int32_t* sorted = reinterpret_cast<int32_t*>(ws + plan.sorted);
   int32_t* rows = reinterpret_cast<int32_t*>(ws + plan.rows);
   void* h = ws + plan.h;
   float* y_rows = reinterpret_cast<float*>(ws + plan.y_rows);
 
-  if (dims->T <= kDecodeMaxTokens) {
+  if (routed) {
+    st = hip_status(moe::launch_permute(pair, static_cast<int32_t>(dims->T * dims->k), offs, sorted, rows,
+                                        expert_counts_out, dims->capacity, s));
+    if (st != MOE_OK) return st;
+  } else if (dims->T <= kDecodeMaxTokens) {
     // Small batch: routing and permutation in one workgroup.
     st = hip_status(moe::launch_route_permute(dims->dtype, x, w_gate, logit_bias, idx, w,
                                               static_cast<int32_t>(dims->T), dims->d, dims->gating,
@@ -360,11 +375,52 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
                       split == 2 ? y_rows2 - y_rows : 0, split == 2 ? nullptr : second, second_bytes, s);
     if (st != MOE_OK) return st;
     return hip_status(
-        moe::launch_combine(dims->dtype, y_rows, y_rows2, rows, w, y, dims->T, dims->d, n_cu, s));
+        moe::launch_combine(dims->dtype, y_rows, y_rows2, rows, gate, y, dims->T, dims->d, n_cu, s));
   }
   st = run_experts(dims, x, offs, sorted, w1, w3, w2, h, y_rows, s);
   if (st != MOE_OK) return st;
-  return run_combine(dims, y_rows, rows, w, y, s);
+  return run_combine(dims, y_rows, rows, gate, y, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_gate, const float* logit_bias,
+                           const void* w1, const void* w3, const void* w2, void* y, int32_t* topk_idx_out,
+                           float* topk_w_out, int32_t* expert_counts_out, void* workspace, size_t* workspace_bytes,
+                           void* stream) {
+  return ffn_forward_impl(dims, x, w_gate, logit_bias, nullptr, nullptr, w1, w3, w2, y, topk_idx_out, topk_w_out,
+                          expert_counts_out, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_ffn_forward_routed(const moe_dims* dims, const void* x, const int32_t* topk_idx, const float* topk_w,
+                                  const void* w1, const void* w3, const void* w2, void* y,
+                                  int32_t* expert_counts_out, void* workspace, size_t* workspace_bytes,
+                                  void* stream) {
+  // (a NULL topk_idx leaves no router and no routing: INVALID_ARGUMENT, except for the size query)
+  return ffn_forward_impl(dims, x, nullptr, nullptr, topk_idx, topk_w, w1, w3, w2, y, nullptr, nullptr,
+                          expert_counts_out, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_rmsnorm_residual_route(const moe_dims* dims, float* resid, const void* y_add, void* u_out, float eps,
+                                      const void* w_gate, const float* logit_bias, int32_t* topk_idx, float* topk_w,
+                                      void* stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (dims->d > moe::kMaxNormRouteD) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<size_t>(dims->E) * dims->d * elem_size(dims->dtype) > kRouterLdsLimit) return MOE_ERR_UNSUPPORTED;
+  if (dims->T == 0) return MOE_OK;
+  if (!resid || !u_out || !w_gate || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(resid, 16) || !aligned(u_out, 16) || (y_add && !aligned(y_add, 16)) || !aligned(w_gate, 16) ||
+      (logit_bias && !aligned(logit_bias, 16)) || !aligned(topk_idx, 8) || !aligned(topk_w, 8))
+    return MOE_ERR_INVALID_ARGUMENT;
+  int n_cu = 0;
+  st = cu_count(&n_cu);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_rmsnorm_route(dims->dtype, resid, y_add, u_out, w_gate, logit_bias, topk_idx, topk_w,
+                                              dims->T, dims->d, eps, dims->gating, n_cu,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_load_balance_loss(const moe_dims* dims, const float* logits, const int32_t* topk_idx, float* loss,

@@ -107,5 +107,11 @@ hipError_t launch_combine(int dtype, const float* y_rows, const float* y_rows2, 
 
 hipError_t launch_rmsnorm_residual(int dtype, float* resid, const void* y_add, void* u, int64_t T, int d, float eps,
                                    hipStream_t s);
+// The same glue with the next layer's router fused in (idx [T, 2], w [T, 2]);
+// d <= kMaxNormRouteD and W_g within the router's LDS limit.
+constexpr int kMaxNormRouteD = 8192;
+hipError_t launch_rmsnorm_route(int dtype, float* resid, const void* y_add, void* u, const void* wg,
+                                const float* bias, int32_t* idx, float* w, int64_t T, int d, float eps, int gating,
+                                int n_cu, hipStream_t s);
 
 }  // namespace moe

@@ -140,6 +140,142 @@ __global__ void __launch_bounds__(256) router_top2_kernel(const T* __restrict__ 
                 logits_out ? logits_out + t * kExperts : nullptr);
 }
 
+// The residual add and RMSNorm of the glue between stacked layers with the
+// next layer's router fused in: resid += y_add (optional); u = resid /
+// sqrt(mean(resid^2) + eps) rounded to T; then that layer's scores from the
+// rounded u (what the router would read back), top-2 and gates
+// (select_top2).  One wavefront per token row, W_g staged in LDS once per
+// workgroup; a lane keeps its d/64 elements of the row in registers (8
+// consecutive ones per 16-byte step), so the row is read once.  ("Mixtral
+// of Experts", azimuth.plus, router paragraph, for the routing; the norm is
+// the stacked workload's glue.)
+// 8 consecutive elements of T as floats (16 or 32 bytes, aligned), and back.
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float* out) {
+  if constexpr (sizeof(T) == 4) {
+    const float4 a = *reinterpret_cast<const float4*>(p);
+    const float4 c = *reinterpret_cast<const float4*>(p + 4);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = c.x; out[5] = c.y; out[6] = c.z; out[7] = c.w;
+  } else {
+    const uint4 a = *reinterpret_cast<const uint4*>(p);
+    const T* e = reinterpret_cast<const T*>(&a);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) out[q] = to_f32<T>(e[q]);
+  }
+}
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const T* in) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(in[0], in[1], in[2], in[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(in[4], in[5], in[6], in[7]);
+  } else {
+    uint4 a;
+    T* e = reinterpret_cast<T*>(&a);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) e[q] = in[q];
+    *reinterpret_cast<uint4*>(p) = a;
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) rmsnorm_route_kernel(float* __restrict__ resid, const T* __restrict__ y_add,
+                                                            T* __restrict__ u, const T* __restrict__ wg,
+                                                            const float* __restrict__ bias,
+                                                            int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                                                            int64_t T_tokens, int d, float eps, int gating) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* wg_s = reinterpret_cast<T*>(smem_raw);
+  float b[kExperts];
+  stage_router(wg, bias, wg_s, d, b);
+  constexpr int kVec = 8;                       // elements per lane and step
+  constexpr int kSteps = kMaxNormRouteD / (kWave * kVec);
+  const int lane = threadIdx.x % kWave;
+  const int waves_per_block = blockDim.x / kWave;
+  const int64_t n_waves = static_cast<int64_t>(gridDim.x) * waves_per_block;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * waves_per_block + threadIdx.x / kWave; t < T_tokens;
+       t += n_waves) {
+    float* r = resid + t * d;
+    float v[kSteps][kVec];
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      const int i = (j * kWave + lane) * kVec;
+#pragma unroll
+      for (int q = 0; q < kVec; ++q) v[j][q] = 0.0f;
+      if (i < d) {
+        const float4 r0 = *reinterpret_cast<const float4*>(r + i);
+        const float4 r1 = *reinterpret_cast<const float4*>(r + i + 4);
+        v[j][0] = r0.x; v[j][1] = r0.y; v[j][2] = r0.z; v[j][3] = r0.w;
+        v[j][4] = r1.x; v[j][5] = r1.y; v[j][6] = r1.z; v[j][7] = r1.w;
+        if (y_add) {
+          float ya[kVec];
+          load8(y_add + t * d + i, ya);
+#pragma unroll
+          for (int q = 0; q < kVec; ++q) v[j][q] += ya[q];
+          *reinterpret_cast<float4*>(r + i) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
+          *reinterpret_cast<float4*>(r + i + 4) = make_float4(v[j][4], v[j][5], v[j][6], v[j][7]);
+        }
+#pragma unroll
+        for (int q = 0; q < kVec; ++q) ss += v[j][q] * v[j][q];
+      }
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(d) + eps);
+    float acc[kExperts];
+#pragma unroll
+    for (int e = 0; e < kExperts; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      const int i = (j * kWave + lane) * kVec;
+      if (i < d) {
+        T uq[kVec];
+        float uf[kVec];
+#pragma unroll
+        for (int q = 0; q < kVec; ++q) {
+          uq[q] = from_f32<T>(v[j][q] * inv);
+          uf[q] = to_f32<T>(uq[q]);
+        }
+        store8(u + t * d + i, uq);
+#pragma unroll
+        for (int e = 0; e < kExperts; ++e) {
+          float wf[kVec];
+          load8(wg_s + e * d + i, wf);
+#pragma unroll
+          for (int q = 0; q < kVec; ++q) acc[e] = fmaf(uf[q], wf[q], acc[e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < kExperts; ++e) acc[e] = wave_sum(acc[e]) + b[e];
+    if (lane == 0) select_top2(acc, gating, idx_out + kTopK * t, w_out + kTopK * t);
+  }
+}
+
+hipError_t launch_rmsnorm_route(int dtype, float* resid, const void* y_add, void* u, const void* wg,
+                                const float* bias, int32_t* idx, float* w, int64_t T, int d, float eps, int gating,
+                                int n_cu, hipStream_t s) {
+  const size_t lds = kExperts * static_cast<size_t>(d) * (dtype == kDtypeBF16 ? 2 : 4);
+  const void* fn = dtype == kDtypeBF16 ? reinterpret_cast<const void*>(&rmsnorm_route_kernel<bf16_t>)
+                                       : reinterpret_cast<const void*>(&rmsnorm_route_kernel<float>);
+  if (lds > 64 * 1024) {
+    const hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (err != hipSuccess) return err;
+  }
+  int64_t blocks = (T + 3) / 4;  // 4 waves, a row each
+  const int64_t cap = static_cast<int64_t>(n_cu) * 2;
+  if (blocks > cap) blocks = cap;
+  if (dtype == kDtypeBF16)
+    hipLaunchKernelGGL(rmsnorm_route_kernel<bf16_t>, dim3(blocks), dim3(256), lds, s, resid,
+                       static_cast<const bf16_t*>(y_add), static_cast<bf16_t*>(u), static_cast<const bf16_t*>(wg),
+                       bias, idx, w, T, d, eps, gating);
+  else
+    hipLaunchKernelGGL(rmsnorm_route_kernel<float>, dim3(blocks), dim3(256), lds, s, resid,
+                       static_cast<const float*>(y_add), static_cast<float*>(u), static_cast<const float*>(wg), bias,
+                       idx, w, T, d, eps, gating);
+  return hipGetLastError();
+}
+
 // bf16 scores on MFMA: one 16-token group times the 8 router rows (padded to
 // 16 with zeros) per v_mfma_f32_16x16x32_bf16, with fp32 accumulation (the
 // bf16 products are exact in fp32, as in the VALU form).  `slices` waves

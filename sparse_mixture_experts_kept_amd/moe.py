@@ -24,7 +24,7 @@ E_EXPERTS, TOP_K = 8, 2
 
 EXPORTED = ("moe_status_string", "moe_version", "moe_router_topk", "moe_permute", "moe_grouped_swiglu",
             "moe_expert_up", "moe_expert_down", "moe_combine", "moe_ffn_forward", "moe_rmsnorm_residual",
-            "moe_load_balance_loss")
+            "moe_load_balance_loss", "moe_ffn_forward_routed", "moe_rmsnorm_residual_route")
 
 
 class MoeError(RuntimeError):
@@ -65,6 +65,8 @@ def load_library(path: str = LIB_PATH):
         "moe_ffn_forward": (I32, [D, P, P, P, P, P, P, P, P, P, P, P, SZ, P]),
         "moe_rmsnorm_residual": (I32, [I64, I32, P, P, P, F32, I32, P]),
         "moe_load_balance_loss": (I32, [D, P, P, P, P]),
+        "moe_ffn_forward_routed": (I32, [D, P, P, P, P, P, P, P, P, P, SZ, P]),
+        "moe_rmsnorm_residual_route": (I32, [D, P, P, P, F32, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -260,6 +262,44 @@ def ffn_forward(x, w_gate, w1, w3, w2, logit_bias=None, variant=VARIANT_AUTO, re
     if return_routing:
         return y, layer.idx, layer.w, layer.counts
     return y
+
+
+def rmsnorm_residual_route(resid, y_add, u, w_gate, logit_bias=None, idx=None, w=None, eps=1e-5,
+                           gating=GATING_PAIR):
+    """resid += y_add (in place, if given); u = RMSNorm(resid) in u's dtype
+    (written in place); returns the next layer's (topk_idx, topk_w) from u."""
+    lib = load_library()
+    T, d = resid.shape
+    dims = make_dims(T, d, 128, u.dtype, gating=gating)
+    idx = idx if idx is not None else torch.empty((T, TOP_K), dtype=torch.int32, device=resid.device)
+    w = w if w is not None else torch.empty((T, TOP_K), dtype=torch.float32, device=resid.device)
+    _check("moe_rmsnorm_residual_route", lib.moe_rmsnorm_residual_route(
+        ctypes.byref(dims), ptr(resid), ptr(y_add), ptr(u), eps, ptr(w_gate), ptr(logit_bias), ptr(idx), ptr(w),
+        stream_handle()))
+    return idx, w
+
+
+class RoutedFFN:
+    """The layer from a given routing (moe_ffn_forward_routed), with
+    preallocated output and workspace."""
+
+    def __init__(self, x, w1, w3, w2, variant=VARIANT_AUTO, y=None, workspace=None, counts=None, capacity=0):
+        self.lib = load_library()
+        self.dims = _layer_dims(x, w1, variant, capacity=capacity)
+        T, d = x.shape
+        self.args = (x, w1, w3, w2)
+        self.y = y if y is not None else torch.empty((T, d), dtype=x.dtype, device=x.device)
+        self.counts = counts
+        self.ws = workspace if workspace is not None else alloc_workspace(T, d, w1.shape[1], x.dtype, variant,
+                                                                          x.device)
+        self.ws_bytes = ctypes.c_size_t(self.ws.numel())
+
+    def __call__(self, topk_idx, topk_w):
+        x, w1, w3, w2 = self.args
+        _check("moe_ffn_forward_routed", self.lib.moe_ffn_forward_routed(
+            ctypes.byref(self.dims), ptr(x), ptr(topk_idx), ptr(topk_w), ptr(w1), ptr(w3), ptr(w2), ptr(self.y),
+            ptr(self.counts), ptr(self.ws), ctypes.byref(self.ws_bytes), stream_handle()))
+        return self.y
 
 
 def load_balance_loss(logits, topk_idx):

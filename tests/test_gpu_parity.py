@@ -533,6 +533,51 @@ def test_prefill_workloads_sampled(name):
         assert c.max() > 0.35 and c.min() < 0.06
 
 
+# --------------------------------------------------------------------------- router fused into the RMSNorm glue
+
+
+@pytest.mark.parametrize("T,d,dtype,with_y", [(300, 256, "bf16", True), (77, 4096, "bf16", True),
+                                             (33, 8192, "bf16", False), (50, 128, "f32", True)])
+def test_rmsnorm_residual_route(T, d, dtype, with_y):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator(device="cuda").manual_seed(T + d)
+    resid = torch.randn((T, d), generator=g, device="cuda", dtype=torch.float32) * 3.0
+    y = (torch.randn((T, d), generator=g, device="cuda", dtype=torch.float32)).to(tdt) if with_y else None
+    lw = inputs.make_layer_weights(d, 256, 8, dtype, seed=d, device="cuda")
+    r0 = resid.clone()
+    u = torch.empty((T, d), dtype=tdt, device="cuda")
+    idx, w = moe.rmsnorm_residual_route(resid, y, u, lw["w_gate"])
+    torch.cuda.synchronize()
+    ref_resid = r0 + (y.float() if with_y else 0.0)
+    assert torch.equal(resid, ref_resid)  # one fp32 add, exactly
+    tol = 1e-2 if dtype == "bf16" else 1e-5
+    np.testing.assert_allclose(O._f64(u.cpu()), O.rmsnorm(O._f64(ref_resid.cpu())), rtol=tol, atol=tol)
+    # routing from the GPU's own rounded u, against the oracle router
+    logits = O.router_logits(_cpu(u), _cpu(lw["w_gate"]))
+    ref_idx = O.select_top_k(logits)
+    ref = {"logits": logits, "idx": ref_idx, "gates": O.masked_softmax_gates(logits, ref_idx)}
+    _check_routing(idx.cpu().numpy().astype(np.int64), w.cpu().numpy().astype(np.float64), ref)
+    # the same pair and gates as the unfused router on that u
+    i2, w2 = moe.router_topk(u, lw["w_gate"])
+    clear = O.second_third_gap(logits) > GAP
+    np.testing.assert_array_equal(idx.cpu().numpy()[clear], i2.cpu().numpy()[clear])
+    np.testing.assert_allclose(w.cpu().numpy()[clear], w2.cpu().numpy()[clear], atol=2e-6, rtol=0)
+
+
+@pytest.mark.parametrize("T,d,f", [(40, 256, 512), (700, 256, 512)])
+def test_ffn_forward_routed_matches_the_layer(T, d, f):
+    # given the layer's own routing, the routed entry point returns the same bits
+    layer = _layer(T, d, f, seed=90 + T)
+    y, idx, w, counts = moe.ffn_forward(layer["x"], layer["w_gate"], layer["w1"], layer["w3"], layer["w2"],
+                                        return_routing=True)
+    counts2 = torch.empty_like(counts)
+    rf = moe.RoutedFFN(layer["x"], layer["w1"], layer["w3"], layer["w2"], counts=counts2)
+    y2 = rf(idx, w)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+    assert torch.equal(counts, counts2)
+
+
 # --------------------------------------------------------------------------- stacked layers (RMSNorm + residual glue)
 
 
@@ -554,10 +599,12 @@ def _check_stack_layer(stack, layer_idx, u, y, idx, sample):
     assert np.abs(yg - ref["y"]).max() <= _tol("bf16", ref["y"])
 
 
-def test_stack_small_every_layer():
+@pytest.mark.parametrize("fused", [True, False])
+def test_stack_small_every_layer(fused):
+    # fused: the glue after each layer computes the next layer's routing
     from sparse_mixture_experts_kept_amd.stack import MoEStack
     T, d, f, L = 300, 256, 512, 4
-    stack = MoEStack(T, d, f, L, seed=31)
+    stack = MoEStack(T, d, f, L, seed=31, fused=fused)
     g = torch.Generator(device="cuda").manual_seed(32)
     x0 = torch.randn((T, d), generator=g, device="cuda", dtype=torch.float32)
     stack.load_input(x0)
