@@ -126,8 +126,8 @@ moe_status moe_router_topk(const moe_dims* dims, const void* x, const void* w_ga
  * t's j-th expert).  It groups each expert's tokens so the expert GEMMs read
  * them contiguously; it changes no value ("Mixtral & Sparse MoE (2024) > The
  * Solution", routing paragraph: each token is routed on its own).
- *   topk_idx [T, k] int32 (values must lie in [0, E); other values are
- *   undefined behaviour).
+ *   topk_idx [T, k] int32 (an id outside [0, E) gets no row: its slot is
+ *   treated like a dropped one, slot_rows = -1).
  *   Outputs: expert_offsets [E + 1] int32 (exclusive prefix sum of the per-
  *   expert rows; offsets[E] = T * k without a capacity), sorted_slots
  *   [T * k] int32 (slots of expert 0 in increasing slot id, then expert 1,
@@ -202,7 +202,7 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
  * The whole layer from a routing computed elsewhere (by
  * moe_rmsnorm_residual_route, or any top-2 pairs and gates): permutation,
  * both expert projections and the combine, as moe_ffn_forward without its
- * router.  topk_idx [T, 2] int32 (values in [0, E)), topk_w [T, 2] fp32, as
+ * router.  topk_idx [T, 2] int32 (an id outside [0, E) adds nothing), topk_w [T, 2] fp32, as
  * moe_router_topk writes them; dims->capacity applies; dims->gating is not
  * used.  Workspace as moe_ffn_forward (same size query).
  */

@@ -145,7 +145,10 @@ __global__ void __launch_bounds__(kPermThreads) permute_kernel(const int32_t* __
 #pragma unroll
     for (int i = 0; i < kSlotsPerThread; ++i) {
       const int e = ids[i];
-      if (e < 0) continue;
+      if (e < 0) {  // past the end, or an id outside [0, E): no row, like a dropped slot
+        if (s0 + i < n_slots) slot_rows[s0 + i] = -1;
+        continue;
+      }
       int r = 0, off = 0;
 #pragma unroll
       for (int ee = 0; ee < kExperts; ++ee)

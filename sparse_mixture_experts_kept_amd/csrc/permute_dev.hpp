@@ -76,6 +76,7 @@ __device__ inline void permute_block(const int32_t* __restrict__ idx, int32_t n_
       if (lane == 0) wave_cnt[wave][ee] = __popcll(m);
     }
     __syncthreads();
+    if (e < 0 && s < n_slots) slot_rows[s] = -1;  // an id outside [0, E): no row, like a dropped slot
     if (e >= 0) {
       int r = base[e] + rank;  // the slot's rank among its expert's slots
       for (int w = 0; w < wave; ++w) r += wave_cnt[w][e];

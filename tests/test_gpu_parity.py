@@ -431,6 +431,35 @@ def test_capacity_permutation_exact(T, capacity):
     np.testing.assert_array_equal(got_sorted, o_sorted[keep[o_sorted]])
 
 
+@pytest.mark.parametrize("T", [300, 3000])
+def test_out_of_range_ids_get_no_row(T):
+    # ids outside [0, 8) (ballot form for T <= 512, chunked form above) are
+    # left out like dropped slots, and the routed layer adds nothing for them
+    rng = np.random.default_rng(T)
+    idx = O.select_top_k(rng.standard_normal((T, 8)), 2).astype(np.int32)
+    bad = rng.random((T, 2)) < 0.05
+    idx_bad = np.where(bad, np.where(rng.random((T, 2)) < 0.5, -3, 9), idx).astype(np.int32)
+    offs, sorted_slots, slot_rows = moe.permute(torch.from_numpy(idx_bad).cuda())
+    rows = slot_rows.cpu().numpy().reshape(T, 2)
+    assert (rows[bad] == -1).all() and (rows[~bad] >= 0).all()
+    counts = np.bincount(idx[~bad], minlength=8)
+    np.testing.assert_array_equal(np.diff(offs.cpu().numpy()), counts)
+    if T == 300:
+        layer = _layer(T, 256, 512, seed=61)
+        w = torch.full((T, 2), 0.5, dtype=torch.float32, device="cuda")
+        rf = moe.RoutedFFN(layer["x"], layer["w1"], layer["w3"], layer["w2"])
+        y = rf(torch.from_numpy(idx_bad).cuda(), w).float().cpu().numpy()
+        keep = ~bad
+        ref = np.zeros((T, 256))
+        widen = _widen_experts(layer)
+        xs = O._f64(_cpu(layer["x"]))
+        for e in range(8):
+            tok, slot = np.nonzero((idx_bad == e) & keep)
+            if tok.size:
+                ref[tok] += 0.5 * O.swiglu_expert(xs[tok], *widen(e))
+        assert np.abs(y - ref).max() <= _tol("bf16", ref)
+
+
 @pytest.mark.parametrize("T", [37, 5000])
 def test_load_balance_loss(T):
     layer = _layer(T, 256, 256, seed=81)
