@@ -119,7 +119,7 @@ moe_status down_prefill(const moe_dims* dims, const bf16_t* h, const int32_t* of
 size_t align256(size_t v) { return (v + 255) & ~size_t{255}; }
 
 struct Workspace {
-  size_t idx, w, offsets, sorted, rows, h, y_rows, y_rows2, total;
+  size_t idx, w, offsets, sorted, rows, gcounts, h, y_rows, y_rows2, total;
 };
 
 Workspace plan_workspace(const moe_dims* dims) {
@@ -131,6 +131,7 @@ Workspace plan_workspace(const moe_dims* dims) {
   ws.offsets = o; o += align256((dims->E + 1) * 4);
   ws.sorted = o; o += align256(slots * 4);
   ws.rows = o; o += align256(slots * 4);
+  ws.gcounts = o; o += align256(static_cast<size_t>((dims->T + 15) / 16) * dims->E * 4);  // router group counts
   ws.h = o; o += align256(slots * dims->f * elem_size(dims->dtype));
   ws.y_rows = o; o += align256(slots * dims->d * 4);
   ws.y_rows2 = o; o += align256(slots * dims->d * 4);  // second partial of the split down projection
@@ -139,12 +140,12 @@ Workspace plan_workspace(const moe_dims* dims) {
 }
 
 moe_status run_router(const moe_dims* dims, const void* x, const void* w_gate, const float* bias, int32_t* idx,
-                      float* w, float* logits, hipStream_t s) {
+                      float* w, float* logits, hipStream_t s, int32_t* group_counts = nullptr) {
   int n_cu = 0;
   moe_status st = cu_count(&n_cu);
   if (st != MOE_OK) return st;
-  return hip_status(
-      moe::launch_router(dims->dtype, x, w_gate, bias, idx, w, logits, dims->T, dims->d, dims->gating, n_cu, s));
+  return hip_status(moe::launch_router(dims->dtype, x, w_gate, bias, idx, w, logits, dims->T, dims->d, dims->gating,
+                                      n_cu, s, group_counts));
 }
 
 moe_status run_up(const moe_dims* dims, const void* x, const int32_t* offs, const int32_t* sorted, const void* w1,
@@ -346,6 +347,15 @@ moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_g
     if (st != MOE_OK) return st;
     // (bf16 decode then runs the streaming up and down projections through
     // run_experts below.)
+  } else if (dims->dtype == MOE_BF16 && dims->T <= moe::kMaxGroupPermuteTokens) {
+    // The router counts each 16-token group's slots per expert; the
+    // permutation then runs one wave per group.
+    int32_t* gcounts = reinterpret_cast<int32_t*>(ws + plan.gcounts);
+    st = run_router(dims, x, w_gate, logit_bias, idx, w, nullptr, s, gcounts);
+    if (st != MOE_OK) return st;
+    st = hip_status(moe::launch_permute_groups(idx, static_cast<int32_t>(dims->T), gcounts, offs, sorted, rows,
+                                               expert_counts_out, dims->capacity, s));
+    if (st != MOE_OK) return st;
   } else {
     st = run_router(dims, x, w_gate, logit_bias, idx, w, nullptr, s);
     if (st != MOE_OK) return st;

@@ -57,6 +57,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
 
 // Find the expert owning global m-tile `mt` given per-expert row counts in
 // offsets[0..E]; returns -1 when mt is past the last tile.  `bm` = tile rows.

@@ -15,13 +15,22 @@ constexpr int kDtypeBF16 = 1;
 constexpr int kGatingPair = 0;  // softmax over the kept pair (weights sum to 1)
 constexpr int kGatingFull = 1;  // softmax over all scores, pair not renormalised
 
+// group_counts (bf16 only, may be null): [ceil(T/16), 8] int32, the slots of
+// each 16-token group per expert, for launch_permute_groups.
 hipError_t launch_router(int dtype, const void* x, const void* wg, const float* bias, int32_t* idx, float* w,
-                         float* logits, int64_t T, int d, int gating, int n_cu, hipStream_t s);
+                         float* logits, int64_t T, int d, int gating, int n_cu, hipStream_t s,
+                         int32_t* group_counts = nullptr);
 
 // capacity > 0: each expert keeps its first `capacity` slots (slot order);
 // dropped slots get slot_rows = -1.
 hipError_t launch_permute(const int32_t* idx, int32_t n_slots, int32_t* offsets, int32_t* sorted_slots,
                           int32_t* slot_rows, int32_t* counts_out, int capacity, hipStream_t s);
+// The same permutation from the router's per-group counts: one wave per
+// 16-token group.  n_tokens <= kMaxGroupPermuteTokens.
+constexpr int64_t kMaxGroupPermuteTokens = 65536;
+hipError_t launch_permute_groups(const int32_t* idx, int32_t n_tokens, const int32_t* group_counts, int32_t* offsets,
+                                 int32_t* sorted_slots, int32_t* slot_rows, int32_t* counts_out, int capacity,
+                                 hipStream_t s);
 // loss[0] = E * sum_e f_e * P_e from the scores [T, E] and the pairs [T, k].
 hipError_t launch_load_balance_loss(const float* logits, const int32_t* idx, int64_t T, float* loss, hipStream_t s);
 

@@ -182,7 +182,88 @@ __global__ void __launch_bounds__(kPermThreads) permute_small_kernel(const int32
   permute_block(idx, n_slots, offsets, sorted_slots, slot_rows, counts_out, capacity);
 }
 
+// One wave per 16-token group (32 slots, lane s < 32 holds slot 32g + s):
+// the slots of the earlier groups and of all groups per expert come from
+// the router's group counts (each lane adds a strided share, then a wave
+// sum), the kept offsets from the totals, and a slot's rank is its group's
+// prefix plus its rank among the group's slots of that expert (ballot).
+// Same stable order and capacity rule as the one-workgroup form.
+__global__ void __launch_bounds__(kWave) permute_groups_kernel(const int32_t* __restrict__ idx, int32_t n_tokens,
+                                                               const int32_t* __restrict__ group_counts,
+                                                               int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ sorted_slots,
+                                                               int32_t* __restrict__ slot_rows,
+                                                               int32_t* __restrict__ counts_out, int capacity) {
+  const int lane = threadIdx.x;
+  const int g = blockIdx.x;
+  const int n_groups = (n_tokens + 15) / 16;
+  int tot[kExperts], pre[kExperts];
+#pragma unroll
+  for (int e = 0; e < kExperts; ++e) tot[e] = pre[e] = 0;
+  for (int h = lane; h < n_groups; h += kWave) {
+    const int4 a = *reinterpret_cast<const int4*>(group_counts + kExperts * h);
+    const int4 b = *reinterpret_cast<const int4*>(group_counts + kExperts * h + 4);
+    const int c[kExperts] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < kExperts; ++e) {
+      tot[e] += c[e];
+      pre[e] += h < g ? c[e] : 0;
+    }
+  }
+  int off[kExperts];
+  int run = 0;
+#pragma unroll
+  for (int e = 0; e < kExperts; ++e) {
+    tot[e] = wave_sum_int(tot[e]);
+    pre[e] = wave_sum_int(pre[e]);
+    off[e] = run;
+    run += kept_rows(tot[e], capacity);
+  }
+  if (g == 0 && lane <= kExperts) {
+    int v = run, c = 0;
+#pragma unroll
+    for (int e = 0; e < kExperts; ++e)
+      if (lane == e) {
+        v = off[e];
+        c = tot[e];
+      }
+    offsets[lane] = v;
+    if (counts_out && lane < kExperts) counts_out[lane] = c;
+  }
+  const int n_slots = n_tokens * kTopK;
+  const int s = g * 32 + lane;
+  const int e = (lane < 32 && s < n_slots) ? valid_expert(idx[s]) : -1;
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int r = 0, o = 0;
+#pragma unroll
+  for (int ee = 0; ee < kExperts; ++ee) {
+    const unsigned long long m = __ballot(e == ee);
+    if (e == ee) {
+      r = pre[ee] + __popcll(m & below);
+      o = off[ee];
+    }
+  }
+  if (lane < 32 && s < n_slots) {
+    if (e < 0 || (capacity > 0 && r >= capacity)) {
+      slot_rows[s] = -1;  // dropped, or an id outside [0, E)
+    } else {
+      sorted_slots[o + r] = s;
+      slot_rows[s] = o + r;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_permute_groups(const int32_t* idx, int32_t n_tokens, const int32_t* group_counts, int32_t* offsets,
+                                 int32_t* sorted_slots, int32_t* slot_rows, int32_t* counts_out, int capacity,
+                                 hipStream_t s) {
+  if (n_tokens > kMaxGroupPermuteTokens) return hipErrorInvalidValue;
+  const int groups = (n_tokens + 15) / 16;
+  hipLaunchKernelGGL(permute_groups_kernel, dim3(groups), dim3(kWave), 0, s, idx, n_tokens, group_counts, offsets,
+                     sorted_slots, slot_rows, counts_out, capacity);
+  return hipGetLastError();
+}
 
 hipError_t launch_permute(const int32_t* idx, int32_t n_slots, int32_t* offsets, int32_t* sorted_slots,
                           int32_t* slot_rows, int32_t* counts_out, int capacity, hipStream_t s) {

@@ -313,10 +313,12 @@ __host__ __device__ inline int router_slices(int d, int cap) {
 
 // Reduce the slice partials of one 16-token group (parked in LDS as
 // part[slice][lane] = f32x4) and route its tokens; run by one wave.
+// With group_counts, also the group's slots per expert (group_counts[8*group + e]).
 __device__ __forceinline__ void router_finish_group(const f32x4 (*part)[kWave], int slices, int group, int T,
                                                     const float* __restrict__ bias, int lane, int gating,
                                                     int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-                                                    float* __restrict__ logits_out) {
+                                                    float* __restrict__ logits_out,
+                                                    int32_t* __restrict__ group_counts) {
   f32x4 sum = part[0][lane];
   for (int sl = 1; sl < slices; ++sl) {
     const f32x4 v = part[sl][lane];
@@ -330,14 +332,29 @@ __device__ __forceinline__ void router_finish_group(const f32x4 (*part)[kWave], 
     sc[4 + q] = __shfl(sum[q], (lane % 16) + 16, kWave);
   }
   const int t = group * 16 + lane;
+  int32_t pair[kTopK] = {-1, -1};
   if (lane < 16 && t < T) {
 #pragma unroll
     for (int e = 0; e < kExperts; ++e) sc[e] += bias ? bias[e] : 0.0f;
-    select_top2(sc, gating, idx_out + kTopK * t, w_out + kTopK * t);
+    float gate[kTopK];
+    select_top2(sc, gating, pair, gate);
+    idx_out[kTopK * t] = pair[0];
+    idx_out[kTopK * t + 1] = pair[1];
+    w_out[kTopK * t] = gate[0];
+    w_out[kTopK * t + 1] = gate[1];
     if (logits_out) {
 #pragma unroll
       for (int e = 0; e < kExperts; ++e) logits_out[static_cast<int64_t>(t) * kExperts + e] = sc[e];
     }
+  }
+  if (group_counts) {
+    int mine = 0;  // lane e < 8: the group's slots on expert e
+#pragma unroll
+    for (int e = 0; e < kExperts; ++e) {
+      const int c = __popcll(__ballot(pair[0] == e)) + __popcll(__ballot(pair[1] == e));
+      if (lane == e) mine = c;
+    }
+    if (lane < kExperts) group_counts[kExperts * group + lane] = mine;
   }
 }
 
@@ -347,13 +364,14 @@ __global__ void __launch_bounds__(1024) router_mfma_kernel(const bf16_t* __restr
                                                            const float* __restrict__ bias,
                                                            int32_t* __restrict__ idx_out, float* __restrict__ w_out,
                                                            float* __restrict__ logits_out, int T, int d,
-                                                           int gating) {
+                                                           int gating, int32_t* __restrict__ group_counts) {
   __shared__ f32x4 part[16][kWave];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int slices = router_slices(d, 16);
   if (wave < slices) part[wave][lane] = router_scores_partial(x, wg, T, d, blockIdx.x, wave, slices, lane);
   __syncthreads();
-  if (wave == 0) router_finish_group(part, slices, blockIdx.x, T, bias, lane, gating, idx_out, w_out, logits_out);
+  if (wave == 0)
+    router_finish_group(part, slices, blockIdx.x, T, bias, lane, gating, idx_out, w_out, logits_out, group_counts);
 }
 
 // Small batches: routing and the expert-major permutation in one workgroup
@@ -377,13 +395,16 @@ __global__ void __launch_bounds__(kPermThreads) route_permute_kernel(
 }
 
 hipError_t launch_router(int dtype, const void* x, const void* wg, const float* bias, int32_t* idx, float* w,
-                         float* logits, int64_t T, int d, int gating, int n_cu, hipStream_t s) {
+                         float* logits, int64_t T, int d, int gating, int n_cu, hipStream_t s,
+                         int32_t* group_counts) {
   if (dtype == kDtypeBF16) {
     const int64_t groups = (T + 15) / 16;
     hipLaunchKernelGGL(router_mfma_kernel, dim3(groups), dim3(1024), 0, s, static_cast<const bf16_t*>(x),
-                       static_cast<const bf16_t*>(wg), bias, idx, w, logits, static_cast<int>(T), d, gating);
+                       static_cast<const bf16_t*>(wg), bias, idx, w, logits, static_cast<int>(T), d, gating,
+                       group_counts);
     return hipGetLastError();
   }
+  if (group_counts) return hipErrorInvalidValue;  // only the bf16 router counts per group
   const int threads = 256;
   const size_t elem = dtype == kDtypeBF16 ? 2 : 4;
   const size_t lds = kExperts * static_cast<size_t>(d) * elem;
