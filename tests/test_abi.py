@@ -84,6 +84,10 @@ def test_bad_dims_are_rejected(kw, status):
     assert lib.moe_ffn_forward(ctypes.byref(dims), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, None,
                                None, ctypes.byref(n), None) == status
     assert lib.moe_load_balance_loss(ctypes.byref(dims), FAKE, FAKE, FAKE, None) == status
+    assert lib.moe_ffn_forward_routed(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                      ctypes.byref(n), None) == status
+    assert lib.moe_rmsnorm_residual_route(ctypes.byref(dims), FAKE, None, FAKE, 1e-5, FAKE, None, FAKE, FAKE,
+                                          None) == status
 
 
 @needs_no_gpu
@@ -167,6 +171,42 @@ def test_zero_tokens_is_a_no_op():
                                None, ctypes.byref(n), None) == moe.MOE_OK
     assert lib.moe_rmsnorm_residual(0, 256, None, None, None, 1e-5, 1, None) == moe.MOE_OK
     assert lib.moe_load_balance_loss(ctypes.byref(dims), None, None, None, None) == moe.MOE_OK
+    assert lib.moe_ffn_forward_routed(ctypes.byref(dims), None, None, None, None, None, None, None, None, None,
+                                      ctypes.byref(n), None) == moe.MOE_OK
+    assert lib.moe_rmsnorm_residual_route(ctypes.byref(dims), None, None, None, 1e-5, None, None, None, None,
+                                          None) == moe.MOE_OK
+
+
+@needs_no_gpu
+def test_routed_and_fused_glue_validation():
+    lib = _lib()
+    dims = _dims()
+    INV = moe.MOE_ERR_INVALID_ARGUMENT
+    n = ctypes.c_size_t(1 << 40)
+    # routed layer: no routing (NULL ids or gates), misaligned ids
+    assert lib.moe_ffn_forward_routed(ctypes.byref(dims), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                      ctypes.byref(n), None) == INV
+    assert lib.moe_ffn_forward_routed(ctypes.byref(dims), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                      ctypes.byref(n), None) == INV
+    assert lib.moe_ffn_forward_routed(ctypes.byref(dims), FAKE, MISALIGNED, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                                      FAKE, ctypes.byref(n), None) == INV
+    # the size query needs no routing and matches moe_ffn_forward's
+    q1, q2 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.moe_ffn_forward_routed(ctypes.byref(dims), None, None, None, None, None, None, None, None, None,
+                                      ctypes.byref(q1), None) == moe.MOE_OK
+    assert lib.moe_ffn_forward(ctypes.byref(dims), None, None, None, None, None, None, None, None, None, None,
+                               None, ctypes.byref(q2), None) == moe.MOE_OK
+    assert q1.value == q2.value > 0
+    # fused glue: required pointers, alignment, and the d limit of the register-resident row
+    assert lib.moe_rmsnorm_residual_route(ctypes.byref(dims), None, None, FAKE, 1e-5, FAKE, None, FAKE, FAKE,
+                                          None) == INV
+    assert lib.moe_rmsnorm_residual_route(ctypes.byref(dims), FAKE, None, FAKE, 1e-5, None, None, FAKE, FAKE,
+                                          None) == INV
+    assert lib.moe_rmsnorm_residual_route(ctypes.byref(dims), FAKE, MISALIGNED, FAKE, 1e-5, FAKE, None, FAKE, FAKE,
+                                          None) == INV
+    wide = _dims(d=8192 + 128)
+    assert lib.moe_rmsnorm_residual_route(ctypes.byref(wide), FAKE, None, FAKE, 1e-5, FAKE, None, FAKE, FAKE,
+                                          None) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_binding_refuses_cpu_tensors():
