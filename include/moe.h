@@ -63,7 +63,8 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 /* Kernel family for the expert GEMMs.  AUTO picks DECODE (weight streaming,
  * token groups of 16 on MFMA) when T <= 64 and PREFILL (LDS-tiled grouped
- * GEMM) otherwise.  Both compute the same function; the choice only affects
+ * GEMM) otherwise; DECODE forced streams up to T = 128 (more rows per expert
+ * use register-direct kernels).  Both compute the same function; the choice only affects
  * speed.  PREFILL needs d >= 256, f >= 256 and x below 4 GiB (T * d < 2^31);
  * other bf16 layers always run DECODE.  MOE_F32 always uses its own fp32
  * kernels. */

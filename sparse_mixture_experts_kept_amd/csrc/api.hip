@@ -12,7 +12,11 @@ namespace {
 
 using moe::bf16_t;
 
+// AUTO takes the streaming kernels up to here: measured on the full-size
+// layer, the grouped GEMM is faster from T = 96 on (four token groups per
+// pass load twice the weight bytes in token rows per stage).
 constexpr int64_t kDecodeMaxTokens = 64;
+constexpr int64_t kRoutePermuteMaxTokens = 64;  // routing fused with the permutation (one workgroup)
 constexpr size_t kRouterLdsLimit = 128 * 1024;
 constexpr int kMaxDevices = 64;
 
@@ -162,7 +166,7 @@ moe_status run_up(const moe_dims* dims, const void* x, const int32_t* offs, cons
   const moe_status st = cu_count(&n_cu);
   if (st != MOE_OK) return st;
   if (use_decode(dims)) {
-    if (dims->T <= kDecodeMaxTokens)
+    if (dims->T <= moe::kStreamMaxTokens)
       return hip_status(moe::launch_up_decode_stream(xb, offs, sorted, w1b, w3b, hb, dims->T, dims->d, dims->f, n_cu, s));
     return hip_status(moe::launch_up_decode(xb, offs, sorted, w1b, w3b, hb, dims->T, dims->d, dims->f, s));
   }
@@ -180,7 +184,7 @@ moe_status run_down(const moe_dims* dims, const void* h, const int32_t* offs, co
   const moe_status st = cu_count(&n_cu);
   if (st != MOE_OK) return st;
   if (use_decode(dims)) {
-    if (dims->T <= kDecodeMaxTokens)
+    if (dims->T <= moe::kStreamMaxTokens)
       return hip_status(moe::launch_down_decode_stream(hb, offs, w2b, y_rows, dims->T, dims->d, dims->f, n_cu, s));
     return hip_status(moe::launch_down_decode(hb, offs, w2b, y_rows, dims->T, dims->d, dims->f, 1, 0, s));
   }
@@ -339,7 +343,7 @@ moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_g
     st = hip_status(moe::launch_permute(pair, static_cast<int32_t>(dims->T * dims->k), offs, sorted, rows,
                                         expert_counts_out, dims->capacity, s));
     if (st != MOE_OK) return st;
-  } else if (dims->T <= kDecodeMaxTokens) {
+  } else if (dims->T <= kRoutePermuteMaxTokens) {
     // Small batch: routing and permutation in one workgroup.
     st = hip_status(moe::launch_route_permute(dims->dtype, x, w_gate, logit_bias, idx, w,
                                               static_cast<int32_t>(dims->T), dims->d, dims->gating,

@@ -113,7 +113,7 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
   constexpr int kLoads = kLoadsPerBlock * (NB + MAXG);  // load instructions per stage
   constexpr int kRowsPerPass = 16 * MAXG;
   static_assert(W == 256 || W == 512, "row run per stage");
-  static_assert(NB % 2 == 0 && NB <= 4 && MAXG <= 2, "unit shape");
+  static_assert(NB % 2 == 0 && NB <= 4 && MAXG <= 4, "unit shape");
   static_assert((S - 1) * kLoads <= 63, "vmcnt holds at most 63 loads in flight");
   __shared__ __align__(16) bf16_t ring[S][kStageElems];
 
@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(kWave) decode_stream_kernel(const bf16_t* __re
   __amdgpu_buffer_rsrc_t ra, rb;
   // (Fixed extents: an array sized by a template parameter and passed to
   // the buffer-load builtin keeps clang from emitting the launch stub.)
-  uint32_t t_off[2][8];
+  uint32_t t_off[4][8];
   const __amdgpu_buffer_rsrc_t rt =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(act), 0, act_bytes, kBufferFlags);
 #define SET_ISSUE_UNIT(U_)                                                                                   \
@@ -353,20 +353,22 @@ hipError_t launch_stream(const bf16_t* act, const int32_t* sorted_slots, const i
 hipError_t launch_up_decode_stream(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots,
                                    const bf16_t* w1, const bf16_t* w3, bf16_t* h, int64_t T, int d, int f, int n_cu,
                                    hipStream_t s) {
-  if (T > 64) return hipErrorInvalidValue;
+  if (T > kStreamMaxTokens) return hipErrorInvalidValue;
   if (T <= 32) {
     if (d % 256 == 0) return launch_stream<true, 512, 2, 1, 3>(x, sorted_slots, offs, w1, w3, h, d, f, T, n_cu, s);
     return launch_stream<true, 256, 2, 1, 6>(x, sorted_slots, offs, w1, w3, h, d, f, T, n_cu, s);
   }
-  return launch_stream<true, 256, 2, 2, 4>(x, sorted_slots, offs, w1, w3, h, d, f, T, n_cu, s);
+  if (T <= 64) return launch_stream<true, 256, 2, 2, 4>(x, sorted_slots, offs, w1, w3, h, d, f, T, n_cu, s);
+  return launch_stream<true, 256, 2, 4, 3>(x, sorted_slots, offs, w1, w3, h, d, f, T, n_cu, s);
 }
 
 hipError_t launch_down_decode_stream(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int64_t T,
                                      int d, int f, int n_cu, hipStream_t s) {
-  if (T > 64) return hipErrorInvalidValue;
+  if (T > kStreamMaxTokens) return hipErrorInvalidValue;
   const int n_slots = static_cast<int>(T) * kTopK;
   if (T <= 32) return launch_stream<false, 256, 4, 1, 3>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s);
-  return launch_stream<false, 256, 2, 2, 4>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s);
+  if (T <= 64) return launch_stream<false, 256, 2, 2, 4>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s);
+  return launch_stream<false, 256, 2, 4, 3>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s);
 }
 
 // Tails of the prefill layer (rows of an expert past its last full 256-row

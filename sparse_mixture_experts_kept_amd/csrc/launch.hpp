@@ -96,9 +96,12 @@ hipError_t launch_up_decode(const bf16_t* x, const int32_t* offs, const int32_t*
 hipError_t launch_down_decode(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int64_t T, int d,
                               int f, int split, int64_t split_stride, hipStream_t s);
 
-// Decode batches of at most 64 tokens (rows per expert <= T): the weight
-// streams of the touched experts through per-wave LDS rings, 2 * n_cu
-// single-wave workgroups.  Returns hipErrorInvalidValue for T > 64.
+// Decode batches of at most kStreamMaxTokens tokens: the weight streams of
+// the touched experts through per-wave LDS rings, 2 * n_cu single-wave
+// workgroups, token groups of 16 (up to 1, 2 or 4 per pass for T <= 32, 64,
+// 128; an expert with more rows takes more passes).  Returns
+// hipErrorInvalidValue above kStreamMaxTokens.
+constexpr int64_t kStreamMaxTokens = 128;
 hipError_t launch_up_decode_stream(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots,
                                    const bf16_t* w1, const bf16_t* w3, bf16_t* h, int64_t T, int d, int f, int n_cu,
                                    hipStream_t s);

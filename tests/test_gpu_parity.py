@@ -132,6 +132,25 @@ def test_bf16_decode_kernels(T, d, f):
     run_and_check(_layer(T, d, f, seed=200 + T), variant=moe.VARIANT_DECODE)
 
 
+@pytest.mark.parametrize("T,d,f,variant", [(96, 256, 512, moe.VARIANT_AUTO), (128, 384, 640, moe.VARIANT_DECODE),
+                                           (65, 128, 256, moe.VARIANT_DECODE), (100, 4096, 256, moe.VARIANT_AUTO)])
+def test_decode_streaming_up_to_128_tokens(T, d, f, variant):
+    # 64 < T <= 128: the streaming kernels with four token groups (64 rows)
+    # per pass, routed by the MFMA router and the group permutation
+    run_and_check(_layer(T, d, f, seed=600 + T), variant=variant)
+
+
+@pytest.mark.parametrize("T", [128, 90])
+def test_decode_streaming_two_experts_full_128(T):
+    # every token on two experts: T rows each, two passes of 64 when T > 64
+    layer = _layer(T, 256, 512, seed=27 + T)
+    b = torch.zeros(8, dtype=torch.float32)
+    b[1], b[5] = 60.0, 40.0
+    layer["logit_bias"] = b.cuda()
+    out = run_and_check(layer, variant=moe.VARIANT_DECODE)
+    np.testing.assert_array_equal(out["counts"].cpu().numpy(), [0, T, 0, 0, 0, T, 0, 0])
+
+
 @pytest.mark.parametrize("T", [64, 29])
 def test_decode_streaming_two_experts_full(T):
     # every token on experts 3 and 6: two experts with T rows each (the
