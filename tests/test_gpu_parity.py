@@ -132,12 +132,12 @@ def test_bf16_decode_kernels(T, d, f):
     run_and_check(_layer(T, d, f, seed=200 + T), variant=moe.VARIANT_DECODE)
 
 
-@pytest.mark.parametrize("T,d,f,variant", [(96, 256, 512, moe.VARIANT_AUTO), (128, 384, 640, moe.VARIANT_DECODE),
-                                           (65, 128, 256, moe.VARIANT_DECODE), (100, 4096, 256, moe.VARIANT_AUTO)])
-def test_decode_streaming_up_to_128_tokens(T, d, f, variant):
-    # 64 < T <= 128: the streaming kernels with four token groups (64 rows)
-    # per pass, routed by the MFMA router and the group permutation
-    run_and_check(_layer(T, d, f, seed=600 + T), variant=variant)
+@pytest.mark.parametrize("T,d,f", [(96, 256, 512), (128, 384, 640), (65, 128, 256), (100, 4096, 256)])
+def test_decode_streaming_up_to_128_tokens(T, d, f):
+    # 64 < T <= 128 with the decode kernels: the streaming kernels with four
+    # token groups (64 rows) per pass, routed by the MFMA router and the group
+    # permutation
+    run_and_check(_layer(T, d, f, seed=600 + T), variant=moe.VARIANT_DECODE)
 
 
 @pytest.mark.parametrize("T", [128, 90])
