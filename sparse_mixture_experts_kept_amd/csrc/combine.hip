@@ -26,24 +26,28 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
        i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
     const int64_t t = i / vec_per_row;
     const int c = static_cast<int>(i - t * vec_per_row) * 4;
-    const int64_t r0 = slot_rows[2 * t];
-    const int64_t r1 = slot_rows[2 * t + 1];
+    const int64_t s0 = slot_rows[2 * t];
+    const int64_t s1 = slot_rows[2 * t + 1];
+    // a dropped slot (row -1) loads row 0, whose value the selects below
+    // discard: the loads stay unconditional (one batch per thread)
+    const int64_t r0 = s0 >= 0 ? s0 : 0;
+    const int64_t r1 = s1 >= 0 ? s1 : 0;
     const float g0 = topk_w[2 * t];
     const float g1 = topk_w[2 * t + 1];
-    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 a = r0 >= 0 ? *reinterpret_cast<const float4*>(y_rows + r0 * d + c) : zero;
-    float4 b = r1 >= 0 ? *reinterpret_cast<const float4*>(y_rows + r1 * d + c) : zero;
+    float4 a = *reinterpret_cast<const float4*>(y_rows + r0 * d + c);
+    float4 b = *reinterpret_cast<const float4*>(y_rows + r1 * d + c);
     if (y_rows2) {  // second partial sum of a split reduction, added first
-      const float4 a2 = r0 >= 0 ? *reinterpret_cast<const float4*>(y_rows2 + r0 * d + c) : zero;
-      const float4 b2 = r1 >= 0 ? *reinterpret_cast<const float4*>(y_rows2 + r1 * d + c) : zero;
+      const float4 a2 = *reinterpret_cast<const float4*>(y_rows2 + r0 * d + c);
+      const float4 b2 = *reinterpret_cast<const float4*>(y_rows2 + r1 * d + c);
       a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
       b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
     }
+    const bool k0 = s0 >= 0, k1 = s1 >= 0;
     float o[4];
-    o[0] = g0 * a.x + g1 * b.x;
-    o[1] = g0 * a.y + g1 * b.y;
-    o[2] = g0 * a.z + g1 * b.z;
-    o[3] = g0 * a.w + g1 * b.w;
+    o[0] = (k0 ? g0 * a.x : 0.0f) + (k1 ? g1 * b.x : 0.0f);
+    o[1] = (k0 ? g0 * a.y : 0.0f) + (k1 ? g1 * b.y : 0.0f);
+    o[2] = (k0 ? g0 * a.z : 0.0f) + (k1 ? g1 * b.z : 0.0f);
+    o[3] = (k0 ? g0 * a.w : 0.0f) + (k1 ? g1 * b.w : 0.0f);
     if constexpr (sizeof(TO) == 4) {
       *reinterpret_cast<float4*>(y + t * d + c) = make_float4(o[0], o[1], o[2], o[3]);
     } else {
