@@ -118,6 +118,18 @@ def test_bf16_prefill_kernels(T, d, f):
     run_and_check(_layer(T, d, f, seed=T), variant=moe.VARIANT_PREFILL)
 
 
+@pytest.mark.parametrize("T", [65536, 70000])
+def test_large_batch_permutation_paths(T):
+    # up to 65536 tokens the router counts its 16-token groups and the
+    # permutation runs one wave per group; above, one workgroup scans all slots
+    layer = _layer(T, 256, 256, seed=T)
+    rng = np.random.default_rng(T)
+    sample = np.sort(rng.choice(T, size=64, replace=False))
+    sample[-1] = T - 1
+    out = run_and_check(layer, variant=moe.VARIANT_PREFILL, sample=sample)
+    assert int(out["counts"].sum()) == 2 * T
+
+
 @pytest.mark.parametrize("T", [1, 2, 5, 17])
 def test_bf16_prefill_kernels_tiny_batches(T):
     run_and_check(_layer(T, 256, 512, seed=100 + T), variant=moe.VARIANT_PREFILL)
