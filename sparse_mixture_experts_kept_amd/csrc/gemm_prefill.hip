@@ -52,6 +52,8 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr int kXcds = 8;
 constexpr int kGroupN = 4;     // n-tiles per group in the tile order
 constexpr int kThinRows = 32;  // m-tiles with at most this many rows take the thin path
+constexpr int kSmallRows = 64;    // ... at most this many, the small path
+constexpr int kMediumRows = 128;  // ... and at most this many, the medium path
 static_assert(kThinRows == kTailPartRows, "the streamed tails are the thin tiles");
 constexpr int kSlotElems = kBM * kBK;  // one 32 KiB slot (kBM == kBN)
 // Word 3 of a raw buffer resource on gfx9 (no format conversion).
@@ -566,6 +568,262 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
             const int n = n0 + wave * 64 + j * 16 + 4 * elg;
             if (n >= N) continue;
             const f32x4 v = tacc[i][j];
+            *reinterpret_cast<float4*>(C + orow * N + n) = make_float4(v[0], v[1], v[2], v[3]);
+          }
+        }
+      }
+      continue;
+    }
+
+    if (rows - m0 <= kSmallRows) {
+      // Small tile: 33..64 rows.  As the thin tile with four row blocks
+      // (64 rows x 64 weight rows per wave: 4 x 4 MFMA tiles), loads three
+      // stages ahead: the weight tiles in slots 1-4, the 64 token rows (8 KiB
+      // per stage, wave w filling rows 16w..16w+15) in 4 sub-slots of slot 0.
+      uint32_t ta_off[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int lc = (j & 1) ? lc_odd : lc_even;  // swizzle of LDS row 16*wave + 8*j + ld_row
+        if constexpr (SWIGLU)
+          ta_off[j] = ((static_cast<uint32_t>(gather[row_begin + min(m0 + wave * 16 + j * 8 + ld_row, rows - 1)]) /
+                        kTopK) * static_cast<uint32_t>(K) + lc) * 2u;
+        else
+          ta_off[j] = (static_cast<uint32_t>(min(wave * 16 + j * 8 + ld_row, rows - 1 - m0)) *
+                           static_cast<uint32_t>(K) + lc) * 2u;
+      }
+      constexpr int kThinSub = kSmallRows * kBK;  // elements of one token sub-slot
+      constexpr int kThinLoads = 10;              // loads per wave and stage: 8 weight + 2 token
+#define LOAD_THIN(KT_)                                                                                   \
+  {                                                                                                      \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                      \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, LDS_PTR(&ring[1 + ((KT_) & 3)][(wave * 64 + j * 8) * kBK]), \
+                                               16, b_off[j], (KT_) * (kBK * 2), 0, 0);                  \
+    }                                                                                                    \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                                      \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc,                                                   \
+                                               LDS_PTR(&ring[0][((KT_) & 3) * kThinSub + (wave * 16 + j * 8) * kBK]), \
+                                               16, ta_off[j], (KT_) * (kBK * 2), 0, 0);                 \
+    }                                                                                                    \
+  }
+      // this wave's B-tile rows: SwiGLU = 32 gate rows and the matching 32 up rows
+      int tb_row[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (SWIGLU)
+          tb_row[j] = (wave >> 1) * 128 + (j >= 2 ? 64 : 0) + (wave & 1) * 32 + (j & 1) * 16 + l16;
+        else
+          tb_row[j] = wave * 64 + j * 16 + l16;
+      }
+      f32x4 tacc[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int st = 0; st < 3 && st < kt_n; ++st) LOAD_THIN(st);
+      for (int kt = 0; kt < kt_n; ++kt) {
+        // stages kt+1 and kt+2 (if any) may stay in flight
+        const int after = min(2, kt_n - 1 - kt);
+        if (after == 2)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kThinLoads));
+        else if (after == 1)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kThinLoads));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        lds_barrier();  // stage kt landed for all waves; stage kt-1 fully read
+        if (kt + 3 < kt_n) LOAD_THIN(kt + 3);  // into the slots of stage kt-1
+        bf16x8 ta[2][4], tb[2][4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            tb[hh][j] = *reinterpret_cast<const bf16x8*>(&ring[1 + (kt & 3)][lds_off(tb_row[j], hh * 4 + lg)]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            ta[hh][i] = *reinterpret_cast<const bf16x8*>(
+                &ring[0][(kt & 3) * kThinSub + lds_off(i * 16 + l16, hh * 4 + lg)]);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              tacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tb[hh][j], ta[hh][i], tacc[i][j], 0, 0, 0);
+      }
+#undef LOAD_THIN
+      // every wave's reads of the last stage are done before the next tile refills the slots
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & lgkm0_mask());
+      lds_barrier();
+      // Epilogue: tacc[i][j][q] is row m0 + i*16 + l16, B-tile row tb_row[j]'s
+      // block at 4*lg + q.
+      // (the lane index re-read: address terms formed here, as in the main epilogue)
+      int elane = lane;
+      asm volatile("" : "+v"(elane));
+      const int el16 = elane % 16, elg = elane / 16;
+      if (plane) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int brow = SWIGLU ? (wave >> 1) * 128 + (j >= 2 ? 64 : 0) + (wave & 1) * 32 + (j & 1) * 16
+                                    : wave * 64 + j * 16;
+            const f32x4 v = tacc[i][j];
+            *reinterpret_cast<float4*>(plane + (i * 16 + el16) * kBN + brow + 4 * elg) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          }
+        continue;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + i * 16 + el16;
+        if (m >= rows) continue;
+        const int64_t orow = row_begin + m;
+        if constexpr (SWIGLU) {
+          bf16_t* C = static_cast<bf16_t*>(Cout);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int n = n0 + (wave >> 1) * 64 + (wave & 1) * 32 + j * 16 + 4 * elg;
+            const f32x4 g = tacc[i][j];
+            const f32x4 u = tacc[i][j + 2];
+            uint2 p;
+            p.x = pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
+            p.y = pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
+            *reinterpret_cast<uint2*>(C + orow * N + n) = p;
+          }
+        } else {
+          float* C = static_cast<float*>(Cout) + ks * split_stride;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = n0 + wave * 64 + j * 16 + 4 * elg;
+            if (n >= N) continue;
+            const f32x4 v = tacc[i][j];
+            *reinterpret_cast<float4*>(C + orow * N + n) = make_float4(v[0], v[1], v[2], v[3]);
+          }
+        }
+      }
+      continue;
+    }
+
+    if (rows - m0 <= kMediumRows) {
+      // Medium tile: a tile with 65..128 rows (an expert's only or last
+      // m-tile).  As the thin tile, the four waves split the 256 weight rows
+      // (64 each) and take every token row: 128 rows x 64 weight rows per
+      // wave (8 x 4 MFMA tiles), half the MFMAs of a full tile.  Loads run
+      // two stages ahead: the weight tiles in slots 1-3, the 128 token rows
+      // (16 KiB per stage; wave w fills rows 32w..32w+31) in four sub-slots,
+      // two in slot 0 and two in slot 4.  Each stage waits for its own
+      // loads, then a barrier, which also frees the slots of the stage before.
+      constexpr int kMedSub = kMediumRows * kBK;  // elements of one token sub-slot
+      constexpr int kMedLoads = 12;               // loads per wave and stage: 8 weight + 4 token
+      uint32_t ma_off[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int lc = (j & 1) ? lc_odd : lc_even;  // swizzle of LDS row 32*wave + 8*j + ld_row
+        if constexpr (SWIGLU)
+          ma_off[j] = ((static_cast<uint32_t>(gather[row_begin + min(m0 + wave * 32 + j * 8 + ld_row, rows - 1)]) /
+                        kTopK) * static_cast<uint32_t>(K) + lc) * 2u;
+        else
+          ma_off[j] = (static_cast<uint32_t>(min(wave * 32 + j * 8 + ld_row, rows - 1 - m0)) *
+                           static_cast<uint32_t>(K) + lc) * 2u;
+      }
+#define MED_A(KT_) (&ring[((KT_) & 2) ? 4 : 0][((KT_) & 1) * kMedSub])
+#define LOAD_MED(KT_)                                                                                    \
+  {                                                                                                      \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                      \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, LDS_PTR(&ring[1 + (KT_) % 3][(wave * 64 + j * 8) * kBK]), \
+                                               16, b_off[j], (KT_) * (kBK * 2), 0, 0);                  \
+    }                                                                                                    \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                                      \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, LDS_PTR(MED_A(KT_) + (wave * 32 + j * 8) * kBK), 16, \
+                                               ma_off[j], (KT_) * (kBK * 2), 0, 0);                     \
+    }                                                                                                    \
+  }
+      int mb_row[4];  // this wave's B-tile rows (as the thin tile)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (SWIGLU)
+          mb_row[j] = (wave >> 1) * 128 + (j >= 2 ? 64 : 0) + (wave & 1) * 32 + (j & 1) * 16 + l16;
+        else
+          mb_row[j] = wave * 64 + j * 16 + l16;
+      }
+      f32x4 macc[8][4];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) macc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int st = 0; st < 2 && st < kt_n; ++st) LOAD_MED(st);
+      for (int kt = 0; kt < kt_n; ++kt) {
+        // stage kt+1 (if any) may stay in flight
+        if (kt + 1 < kt_n)
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kMedLoads));
+        else
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        lds_barrier();  // stage kt landed for all waves; stage kt-1 fully read
+        if (kt + 2 < kt_n) LOAD_MED(kt + 2);  // into the slots of stage kt-1 (weights) and kt-2 (tokens)
+        const bf16_t* sa = MED_A(kt);
+        const bf16_t* sb = ring[1 + kt % 3];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          bf16x8 ma[8], mb[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            mb[j] = *reinterpret_cast<const bf16x8*>(sb + lds_off(mb_row[j], hh * 4 + lg));
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            ma[i] = *reinterpret_cast<const bf16x8*>(sa + lds_off(i * 16 + l16, hh * 4 + lg));
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              macc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mb[j], ma[i], macc[i][j], 0, 0, 0);
+        }
+      }
+#undef LOAD_MED
+#undef MED_A
+      // every wave's reads of the last stage are done before the next tile refills the slots
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & lgkm0_mask());
+      lds_barrier();
+      // Epilogue: macc[i][j][q] is row m0 + i*16 + l16, B-tile row mb_row[j]'s
+      // block at 4*lg + q.  (Lane index re-read: address terms formed here.)
+      int elane = lane;
+      asm volatile("" : "+v"(elane));
+      const int el16 = elane % 16, elg = elane / 16;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int m = m0 + i * 16 + el16;
+        if (m >= rows) continue;
+        const int64_t orow = row_begin + m;
+        if (plane) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int brow = SWIGLU ? (wave >> 1) * 128 + (j >= 2 ? 64 : 0) + (wave & 1) * 32 + (j & 1) * 16
+                                    : wave * 64 + j * 16;
+            const f32x4 v = macc[i][j];
+            *reinterpret_cast<float4*>(plane + (i * 16 + el16) * kBN + brow + 4 * elg) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          }
+          continue;
+        }
+        if constexpr (SWIGLU) {
+          bf16_t* C = static_cast<bf16_t*>(Cout);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int n = n0 + (wave >> 1) * 64 + (wave & 1) * 32 + j * 16 + 4 * elg;
+            const f32x4 g = macc[i][j];
+            const f32x4 u = macc[i][j + 2];
+            uint2 p;
+            p.x = pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
+            p.y = pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
+            *reinterpret_cast<uint2*>(C + orow * N + n) = p;
+          }
+        } else {
+          float* C = static_cast<float*>(Cout) + ks * split_stride;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = n0 + wave * 64 + j * 16 + 4 * elg;
+            if (n >= N) continue;
+            const f32x4 v = macc[i][j];
             *reinterpret_cast<float4*>(C + orow * N + n) = make_float4(v[0], v[1], v[2], v[3]);
           }
         }
