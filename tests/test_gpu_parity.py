@@ -311,13 +311,14 @@ def test_staged_path_under_the_oracle_assignment(variant):
     assert np.abs(yg - ref["y"]).max() <= _tol("bf16", ref["y"])
 
 
-def test_prefill_crafted_expert_sizes():
+@pytest.mark.parametrize("counts", [[1, 32, 33, 256, 289, 0, 520, 269], [64, 65, 128, 129, 356, 320, 0, 322]])
+def test_prefill_crafted_expert_sizes(counts):
     """Per-expert row counts chosen to hit every m-tile shape of the prefill
-    GEMMs: 1, 32 (thin path), 33 (full path, mostly padding), 256 (exactly
-    one tile), 289 (full tile + 33), 0 (empty expert), 520 (two tiles + a
-    thin tail of 8), 269 (full + thin 13).  h and y_rows are checked element
-    by element against the oracle's SwiGLU and down projection."""
-    counts = [1, 32, 33, 256, 289, 0, 520, 269]
+    GEMMs: 1 and 32 (thin path), 33 and 64 (small path), 65 and 128 (medium
+    path), 129 and 256 (full tile), 0 (empty expert), and after a full tile a
+    last tile of 33 or 64 (small), 66 or 100 (medium), or a thin tail of 8 or
+    13.  h and y_rows are checked element by element against the oracle's
+    SwiGLU and down projection."""
     T, d, f = sum(counts) // 2, 256, 512
     layer = _layer(T, d, f, seed=21)
     rng = np.random.default_rng(21)
@@ -570,6 +571,38 @@ def test_prefill_remainder_split(T, d, f, seed, bias7, tail_parts):
     y2 = moe.ffn_forward(layer["x"], layer["w_gate"], layer["w1"], layer["w3"], layer["w2"],
                          logit_bias=layer.get("logit_bias"), variant=moe.VARIANT_PREFILL)
     assert torch.equal(out["y"], y2)
+
+
+def test_prefill_tile_shapes_in_remainder_pieces():
+    # Crafted expert sizes (four full tiles each, then a last tile of 33-129
+    # rows) whose units leave a partial round in both projections: the split
+    # remainder units include small (33-64 rows) and medium (65-128 rows)
+    # tiles, whose partial tiles are summed by the fixup launch.  Routed entry
+    # point, random gates; the oracle sums each slot's expert output.
+    tails = [64, 65, 129, 33, 128, 57, 40, 100]
+    counts = [4 * 256 + c for c in tails]
+    T, d, f = sum(counts) // 2, 4096, 1024
+    plan = _unit_plan(counts, T, d, f, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert plan["up"]["parts"] >= 2 and plan["down"]["parts"] >= 2, plan
+    layer = _layer(T, d, f, seed=44)
+    rng = np.random.default_rng(44)
+    ids = rng.permutation(np.repeat(np.arange(8), counts)).astype(np.int32).reshape(T, 2)
+    g0 = rng.uniform(0.5, 1.0, T)
+    gates = np.stack([g0, 1.0 - g0], axis=1).astype(np.float32)
+    counts_out = torch.empty(8, dtype=torch.int32, device="cuda")
+    rf = moe.RoutedFFN(layer["x"], layer["w1"], layer["w3"], layer["w2"], counts=counts_out)
+    y = rf(torch.from_numpy(ids).cuda(), torch.from_numpy(gates).cuda()).clone()
+    y2 = rf(torch.from_numpy(ids).cuda(), torch.from_numpy(gates).cuda())  # the layer's own output buffer
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(counts_out.cpu().numpy(), counts)
+    assert torch.equal(y, y2)
+    xs = O._f64(_cpu(layer["x"]))
+    widen = _widen_experts(layer)
+    ref = np.zeros((T, d))
+    for e in range(8):
+        tok, slot = np.nonzero(ids == e)
+        np.add.at(ref, tok, gates[tok, slot].astype(np.float64)[:, None] * O.swiglu_expert(xs[tok], *widen(e)))
+    assert np.abs(O._f64(y.cpu()) - ref).max() <= _tol("bf16", ref)
 
 
 # --------------------------------------------------------------------------- full Mixtral-sized layers (sampled)
