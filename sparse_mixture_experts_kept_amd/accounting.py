@@ -86,13 +86,20 @@ def down_bytes(T: int, d: int, f: int, k: int, n_touched: int, elem_bytes: int =
     return (T * k * f + n_touched * d * f) * elem_bytes + T * k * d * out_bytes
 
 
-def prefill_rows_issued(counts, tile_rows: int = 256, tail_rows: int = 32, group_rows: int = 16):
+# Row heights of the prefill GEMM's tile paths: an m-tile with r rows left runs
+# on the smallest of these that holds r (thin, small, medium, large, full).
+PREFILL_TILE_ROWS = (32, 64, 128, 160, 256)
+
+
+def prefill_rows_issued(counts, tile_rows: int = 256, tail_rows: int = 32, group_rows: int = 16,
+                        tile_heights=PREFILL_TILE_ROWS):
     """Rows the prefill path runs through the matrix cores for these
-    per-expert counts: each expert's rows in m-tiles of ``tile_rows``, except
-    a last tile of at most ``tail_rows`` rows after at least one full tile,
-    which goes to the streaming kernels in token groups of ``group_rows``.
-    Returns (rows needed, rows issued in GEMM tiles, rows issued in tails);
-    the padding waste is issued / needed - 1."""
+    per-expert counts: each expert's rows in m-tiles of ``tile_rows``; an
+    m-tile with r < tile_rows rows issues the smallest of ``tile_heights``
+    that holds r, except a last tile of at most ``tail_rows`` rows after at
+    least one full tile, which goes to the streaming kernels in token groups
+    of ``group_rows``.  Returns (rows needed, rows issued in GEMM tiles, rows
+    issued in tails); the padding waste is issued / needed - 1."""
     needed = gemm = tails = 0
     for c in counts:
         c = int(c)
@@ -105,5 +112,5 @@ def prefill_rows_issued(counts, tile_rows: int = 256, tail_rows: int = 32, group
             gemm += (tiles - 1) * tile_rows
             tails += -(-last // group_rows) * group_rows
         else:
-            gemm += tiles * tile_rows
+            gemm += (tiles - 1) * tile_rows + min(h for h in tile_heights if h >= last)
     return needed, gemm, tails

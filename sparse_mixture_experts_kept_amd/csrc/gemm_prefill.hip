@@ -325,6 +325,158 @@ __device__ __forceinline__ int first_thin_from(const int32_t* offs, int n_tiles_
     __builtin_amdgcn_sched_barrier(0);                                                  \
   }
 
+// One direct global->LDS load of 16 bytes per lane (1 KiB per wave) at byte
+// offsets voff (per lane) + soff (uniform) from the resource's base.  (A
+// plain function: the compiler's host pass does not resolve this builtin
+// when it is called from a device-function template.)
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, bf16_t* lds, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, LDS_PTR(lds), 16, voff, soff, 0, 0);
+}
+
+// Medium tile: a tile with 65..128 rows (an expert's only or last m-tile).
+// As the thin tile, the four waves split the 256 weight rows (64 each) and
+// take every token row: 128 rows x 64 weight rows per wave (8 x 4 MFMA
+// tiles), half the MFMAs of a full tile.  Loads run two stages ahead: the
+// weight tiles in slots 0-2, the 128 token rows (16 KiB per stage; wave w
+// fills rows 32w..32w+31) in three sub-slots in slots 3-4.  Each stage
+// waits for its own loads, then a barrier, which also frees the slots of the
+// stage before.
+template <bool SWIGLU>
+__device__ __forceinline__ void medium_tile(bf16_t (*ring)[kSlotElems], __amdgpu_buffer_rsrc_t a_rsrc,
+                                            __amdgpu_buffer_rsrc_t b_rsrc, const uint32_t (&b_off)[8],
+                                            const int32_t* __restrict__ gather, int row_begin, int rows, int m0, int n0,
+                                            int K, int N, int wave, int lane, int lc_even, int lc_odd, int kt_n,
+                                            float* plane, void* Cout, int ks, int64_t split_stride) {
+  constexpr int RB = kMediumRows / 16;  // row blocks of 16
+  constexpr int kSub = RB * 16 * kBK;    // elements of one token sub-slot
+  constexpr int kALoads = RB / 2;        // token loads per wave and stage (8 rows each)
+  constexpr int kLoads = 8 + kALoads;    // loads per wave and stage
+  static_assert(3 * kSub <= 2 * kSlotElems, "three token sub-slots fit in slots 3-4");
+  bf16_t* const flat = &ring[0][0];
+  const int ld_row = lane / 8, l16 = lane % 16, lg = lane / 16;
+  uint32_t ma_off[kALoads];
+#pragma unroll
+  for (int j = 0; j < kALoads; ++j) {
+    const int lc = (j & 1) ? lc_odd : lc_even;  // swizzle of LDS row 32*wave + 8*j + ld_row
+    if constexpr (SWIGLU)
+      ma_off[j] = ((static_cast<uint32_t>(gather[row_begin + min(m0 + wave * 32 + j * 8 + ld_row, rows - 1)]) /
+                    kTopK) * static_cast<uint32_t>(K) + lc) * 2u;
+    else
+      ma_off[j] = (static_cast<uint32_t>(min(wave * 32 + j * 8 + ld_row, rows - 1 - m0)) *
+                       static_cast<uint32_t>(K) + lc) * 2u;
+  }
+#define MED_A(KT_) (flat + 3 * kSlotElems + ((KT_) % 3) * kSub)
+#define LOAD_MED(KT_)                                                                                    \
+  {                                                                                                        \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                                          \
+        load_lds16(b_rsrc, &ring[(KT_) % 3][(wave * 64 + j * 8) * kBK], b_off[j], (KT_) * (kBK * 2));      \
+    _Pragma("unroll") for (int j = 0; j < kALoads; ++j)                                                    \
+        load_lds16(a_rsrc, MED_A(KT_) + (wave * 32 + j * 8) * kBK, ma_off[j], (KT_) * (kBK * 2));    \
+  }
+  // Fragment reads: every row read sits at 16*block + l16, whose swizzle
+  // (row >> 1) & 7 is (l16 >> 1) & 7 for any block, so a read is a uniform
+  // block base plus one of two per-lane offsets (k-half 0 or 1).
+  const int rd_lane0 = l16 * kBK + ((lg ^ ((l16 >> 1) & 7)) << 3);
+  const int rd_lane1 = rd_lane0 ^ 32;  // logical chunk 4 + lg
+  int mb_base[4];                      // this wave's B-tile row blocks (as the thin tile), in elements
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (SWIGLU)
+      mb_base[j] = ((wave >> 1) * 128 + (j >= 2 ? 64 : 0) + (wave & 1) * 32 + (j & 1) * 16) * kBK;
+    else
+      mb_base[j] = (wave * 64 + j * 16) * kBK;
+  }
+  f32x4 macc[RB][4];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) macc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int st = 0; st < 2 && st < kt_n; ++st) LOAD_MED(st);
+  for (int kt = 0; kt < kt_n; ++kt) {
+    // stage kt+1 (if any) may stay in flight
+    if (kt + 1 < kt_n)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLoads));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_barrier();  // stage kt landed for all waves; stage kt-1 fully read
+    if (kt + 2 < kt_n) LOAD_MED(kt + 2);  // into the slots of stage kt-1
+    const bf16_t* sa = MED_A(kt);
+    const bf16_t* sb = ring[kt % 3];
+    // Both k-halves' fragments are read up front (the second half's reads
+    // land while the first half's MFMAs run); left to itself the scheduler
+    // reads one fragment per MFMA row and waits for each.
+    bf16x8 ma[2][RB], mb[2][4];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int rd = hh ? rd_lane1 : rd_lane0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mb[hh][j] = *reinterpret_cast<const bf16x8*>(sb + mb_base[j] + rd);
+#pragma unroll
+      for (int i = 0; i < RB; ++i) ma[hh][i] = *reinterpret_cast<const bf16x8*>(sa + i * 16 * kBK + rd);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          macc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mb[hh][j], ma[hh][i], macc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#undef LOAD_MED
+#undef MED_A
+  // every wave's reads of the last stage are done before the next tile refills the slots
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & lgkm0_mask());
+  lds_barrier();
+  // Epilogue: macc[i][j][q] is row m0 + i*16 + l16, B-tile row block j's
+  // row 4*lg + q.  (Lane index re-read: address terms formed here.)
+  int elane = lane;
+  asm volatile("" : "+v"(elane));
+  const int el16 = elane % 16, elg = elane / 16;
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int m = m0 + i * 16 + el16;
+    if (m >= rows) continue;
+    const int64_t orow = row_begin + m;
+    if (plane) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int brow = SWIGLU ? (wave >> 1) * 128 + (j >= 2 ? 64 : 0) + (wave & 1) * 32 + (j & 1) * 16
+                                : wave * 64 + j * 16;
+        const f32x4 v = macc[i][j];
+        *reinterpret_cast<float4*>(plane + (i * 16 + el16) * kBN + brow + 4 * elg) =
+            make_float4(v[0], v[1], v[2], v[3]);
+      }
+      continue;
+    }
+    if constexpr (SWIGLU) {
+      bf16_t* C = static_cast<bf16_t*>(Cout);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = n0 + (wave >> 1) * 64 + (wave & 1) * 32 + j * 16 + 4 * elg;
+        const f32x4 g = macc[i][j];
+        const f32x4 u = macc[i][j + 2];
+        uint2 p;
+        p.x = pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
+        p.y = pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
+        *reinterpret_cast<uint2*>(C + orow * N + n) = p;
+      }
+    } else {
+      float* C = static_cast<float*>(Cout) + ks * split_stride;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = n0 + wave * 64 + j * 16 + 4 * elg;
+        if (n >= N) continue;
+        const f32x4 v = macc[i][j];
+        *reinterpret_cast<float4*>(C + orow * N + n) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+}
+
 // SPLITK > 1 (down projection only): each tile's reduction is cut into
 // SPLITK equal parts run as separate work units; part s writes its partial
 // sums to Cout + s * split_stride (a separate buffer per part; the consumer
@@ -513,6 +665,7 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
             ta[hh][i] = *reinterpret_cast<const bf16x8*>(
                 &ring[0][(kt & 7) * kThinSub + lds_off(i * 16 + l16, hh * 4 + lg)]);
         }
+        __builtin_amdgcn_sched_barrier(0);  // all reads issued before the MFMAs (as the split tiles)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -520,6 +673,7 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               tacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tb[hh][j], ta[hh][i], tacc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
 #undef LOAD_THIN
       // every wave's reads of the last stage are done before the next tile refills the slots
@@ -642,6 +796,7 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
             ta[hh][i] = *reinterpret_cast<const bf16x8*>(
                 &ring[0][(kt & 3) * kThinSub + lds_off(i * 16 + l16, hh * 4 + lg)]);
         }
+        __builtin_amdgcn_sched_barrier(0);  // all reads issued before the MFMAs (as the split tiles)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -649,6 +804,7 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
 #pragma unroll
             for (int j = 0; j < 4; ++j)
               tacc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tb[hh][j], ta[hh][i], tacc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
 #undef LOAD_THIN
       // every wave's reads of the last stage are done before the next tile refills the slots
@@ -705,129 +861,8 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
     }
 
     if (rows - m0 <= kMediumRows) {
-      // Medium tile: a tile with 65..128 rows (an expert's only or last
-      // m-tile).  As the thin tile, the four waves split the 256 weight rows
-      // (64 each) and take every token row: 128 rows x 64 weight rows per
-      // wave (8 x 4 MFMA tiles), half the MFMAs of a full tile.  Loads run
-      // two stages ahead: the weight tiles in slots 1-3, the 128 token rows
-      // (16 KiB per stage; wave w fills rows 32w..32w+31) in four sub-slots,
-      // two in slot 0 and two in slot 4.  Each stage waits for its own
-      // loads, then a barrier, which also frees the slots of the stage before.
-      constexpr int kMedSub = kMediumRows * kBK;  // elements of one token sub-slot
-      constexpr int kMedLoads = 12;               // loads per wave and stage: 8 weight + 4 token
-      uint32_t ma_off[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int lc = (j & 1) ? lc_odd : lc_even;  // swizzle of LDS row 32*wave + 8*j + ld_row
-        if constexpr (SWIGLU)
-          ma_off[j] = ((static_cast<uint32_t>(gather[row_begin + min(m0 + wave * 32 + j * 8 + ld_row, rows - 1)]) /
-                        kTopK) * static_cast<uint32_t>(K) + lc) * 2u;
-        else
-          ma_off[j] = (static_cast<uint32_t>(min(wave * 32 + j * 8 + ld_row, rows - 1 - m0)) *
-                           static_cast<uint32_t>(K) + lc) * 2u;
-      }
-#define MED_A(KT_) (&ring[((KT_) & 2) ? 4 : 0][((KT_) & 1) * kMedSub])
-#define LOAD_MED(KT_)                                                                                    \
-  {                                                                                                      \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                      \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, LDS_PTR(&ring[1 + (KT_) % 3][(wave * 64 + j * 8) * kBK]), \
-                                               16, b_off[j], (KT_) * (kBK * 2), 0, 0);                  \
-    }                                                                                                    \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                                      \
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, LDS_PTR(MED_A(KT_) + (wave * 32 + j * 8) * kBK), 16, \
-                                               ma_off[j], (KT_) * (kBK * 2), 0, 0);                     \
-    }                                                                                                    \
-  }
-      int mb_row[4];  // this wave's B-tile rows (as the thin tile)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if constexpr (SWIGLU)
-          mb_row[j] = (wave >> 1) * 128 + (j >= 2 ? 64 : 0) + (wave & 1) * 32 + (j & 1) * 16 + l16;
-        else
-          mb_row[j] = wave * 64 + j * 16 + l16;
-      }
-      f32x4 macc[8][4];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) macc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int st = 0; st < 2 && st < kt_n; ++st) LOAD_MED(st);
-      for (int kt = 0; kt < kt_n; ++kt) {
-        // stage kt+1 (if any) may stay in flight
-        if (kt + 1 < kt_n)
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(kMedLoads));
-        else
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-        lds_barrier();  // stage kt landed for all waves; stage kt-1 fully read
-        if (kt + 2 < kt_n) LOAD_MED(kt + 2);  // into the slots of stage kt-1 (weights) and kt-2 (tokens)
-        const bf16_t* sa = MED_A(kt);
-        const bf16_t* sb = ring[1 + kt % 3];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          bf16x8 ma[8], mb[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            mb[j] = *reinterpret_cast<const bf16x8*>(sb + lds_off(mb_row[j], hh * 4 + lg));
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            ma[i] = *reinterpret_cast<const bf16x8*>(sa + lds_off(i * 16 + l16, hh * 4 + lg));
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              macc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mb[j], ma[i], macc[i][j], 0, 0, 0);
-        }
-      }
-#undef LOAD_MED
-#undef MED_A
-      // every wave's reads of the last stage are done before the next tile refills the slots
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0) & lgkm0_mask());
-      lds_barrier();
-      // Epilogue: macc[i][j][q] is row m0 + i*16 + l16, B-tile row mb_row[j]'s
-      // block at 4*lg + q.  (Lane index re-read: address terms formed here.)
-      int elane = lane;
-      asm volatile("" : "+v"(elane));
-      const int el16 = elane % 16, elg = elane / 16;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_barrier(0);
-        const int m = m0 + i * 16 + el16;
-        if (m >= rows) continue;
-        const int64_t orow = row_begin + m;
-        if (plane) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int brow = SWIGLU ? (wave >> 1) * 128 + (j >= 2 ? 64 : 0) + (wave & 1) * 32 + (j & 1) * 16
-                                    : wave * 64 + j * 16;
-            const f32x4 v = macc[i][j];
-            *reinterpret_cast<float4*>(plane + (i * 16 + el16) * kBN + brow + 4 * elg) =
-                make_float4(v[0], v[1], v[2], v[3]);
-          }
-          continue;
-        }
-        if constexpr (SWIGLU) {
-          bf16_t* C = static_cast<bf16_t*>(Cout);
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int n = n0 + (wave >> 1) * 64 + (wave & 1) * 32 + j * 16 + 4 * elg;
-            const f32x4 g = macc[i][j];
-            const f32x4 u = macc[i][j + 2];
-            uint2 p;
-            p.x = pack_bf16x2(silu(g[0]) * u[0], silu(g[1]) * u[1]);
-            p.y = pack_bf16x2(silu(g[2]) * u[2], silu(g[3]) * u[3]);
-            *reinterpret_cast<uint2*>(C + orow * N + n) = p;
-          }
-        } else {
-          float* C = static_cast<float*>(Cout) + ks * split_stride;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int n = n0 + wave * 64 + j * 16 + 4 * elg;
-            if (n >= N) continue;
-            const f32x4 v = macc[i][j];
-            *reinterpret_cast<float4*>(C + orow * N + n) = make_float4(v[0], v[1], v[2], v[3]);
-          }
-        }
-      }
+      medium_tile<SWIGLU>(ring, a_rsrc, b_rsrc, b_off, gather, row_begin, rows, m0, n0, K, N, wave, lane, lc_even,
+                          lc_odd, kt_n, plane, Cout, ks, split_stride);
       continue;
     }
 

@@ -41,15 +41,19 @@ def test_layer_flops_and_bytes():
 
 
 def test_prefill_rows_issued():
-    # one expert per case: a full tile, a ragged tile, a streamed tail, and a
-    # small expert that still takes a whole tile
+    # one expert per case: a full tile, ragged last tiles of each height, a
+    # streamed tail, and experts with a single short tile
     assert A.prefill_rows_issued([256]) == (256, 256, 0)
-    assert A.prefill_rows_issued([300]) == (300, 512, 0)
+    assert A.prefill_rows_issued([300]) == (300, 256 + 64, 0)
+    assert A.prefill_rows_issued([256 + 100]) == (356, 256 + 128, 0)
+    assert A.prefill_rows_issued([256 + 129]) == (385, 256 + 160, 0)
+    assert A.prefill_rows_issued([256 + 161]) == (417, 512, 0)
     assert A.prefill_rows_issued([1025]) == (1025, 1024, 16)
     assert A.prefill_rows_issued([256 + 32]) == (288, 256, 32)
-    assert A.prefill_rows_issued([256 + 33]) == (289, 512, 0)
-    assert A.prefill_rows_issued([20]) == (20, 256, 0)
+    assert A.prefill_rows_issued([256 + 33]) == (289, 256 + 64, 0)
+    assert A.prefill_rows_issued([20]) == (20, 32, 0)
+    assert A.prefill_rows_issued([160]) == (160, 160, 0)
     assert A.prefill_rows_issued([0, 0]) == (0, 0, 0)
     counts = [1024, 300, 1025, 20]
     n, g, t = A.prefill_rows_issued(counts)
-    assert n == sum(counts) and g == 1024 + 512 + 1024 + 256 and t == 16
+    assert n == sum(counts) and g == 1024 + 320 + 1024 + 32 and t == 16
