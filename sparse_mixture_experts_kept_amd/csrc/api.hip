@@ -369,9 +369,10 @@ moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_g
   }
   if (dims->dtype == MOE_BF16 && !use_decode(dims)) {
     // Prefill.  The down projection's reduction is split in two when the
-    // layer has fewer than two full 256 x 256 tiles per CU (twice the work
-    // units to spread); the combine then adds the two partial sums in a
-    // fixed order.
+    // layer has fewer full 256 x 256 tiles than CUs (twice the work units to
+    // spread); the combine then adds the two partial sums in a fixed order.
+    // From one full round on, the unsplit GEMM hands its short tails to the
+    // streaming kernel instead of running them as thin tiles on a few XCDs.
     int n_cu = 0;
     st = cu_count(&n_cu);
     if (st != MOE_OK) return st;
@@ -383,7 +384,7 @@ moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_g
                     static_cast<const bf16_t*>(w3), static_cast<bf16_t*>(h), n_cu, second, second_bytes, s);
     if (st != MOE_OK) return st;
     const int64_t full_units = (dims->T * dims->k / 256) * (dims->d / 256);
-    const int split = full_units >= 2 * n_cu ? 1 : 2;
+    const int split = full_units >= n_cu ? 1 : 2;
     float* y_rows2 = split == 2 ? second : nullptr;
     st = down_prefill(dims, static_cast<const bf16_t*>(h), offs, static_cast<const bf16_t*>(w2), y_rows, n_cu, split,
                       split == 2 ? y_rows2 - y_rows : 0, split == 2 ? nullptr : second, second_bytes, s);

@@ -514,7 +514,7 @@ def _unit_plan(counts, T, d, f, n_cu, k=2):
     last whole round of the grid are split in P parts when P >= 2."""
     G = (n_cu // 8) * 8
     planes = (T * k * d * 4) // (256 * 256 * 4)
-    down_unsplit = (T * k // 256) * (d // 256) >= 2 * n_cu
+    down_unsplit = (T * k // 256) * (d // 256) >= n_cu
     out = {}
     for name, N, K, TN in (("up", f, d, 128), ("down", d, f, 256)):
         ntn = -(-N // TN)
@@ -603,6 +603,21 @@ def test_prefill_tile_shapes_in_remainder_pieces():
         tok, slot = np.nonzero(ids == e)
         np.add.at(ref, tok, gates[tok, slot].astype(np.float64)[:, None] * O.swiglu_expert(xs[tok], *widen(e)))
     assert np.abs(O._f64(y.cpu()) - ref).max() <= _tol("bf16", ref)
+
+
+def test_down_unsplit_from_one_full_round():
+    # 2100 tokens at d=4096: 16 full m-tiles x 16 n-tiles = one full round of
+    # down-projection tiles, so the reduction is not split and the experts'
+    # short tails (rows past their second full tile) go to the streaming
+    # kernel, its reduction split in parts and summed by the fixup launch.
+    T, d, f = 2100, 4096, 512
+    layer = inputs.make_custom(T, d, f, seed=47, device="cpu")
+    layer = {k2: (v.cuda() if torch.is_tensor(v) else v) for k2, v in layer.items()}
+    out = run_and_check(layer, variant=moe.VARIANT_PREFILL)
+    counts = out["counts"].cpu().tolist()
+    plan = _unit_plan(counts, T, d, f, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert (T * 2 // 256) * (d // 256) == 256, plan
+    assert plan["tail_parts"] >= 2, (counts, plan)
 
 
 # --------------------------------------------------------------------------- full Mixtral-sized layers (sampled)
