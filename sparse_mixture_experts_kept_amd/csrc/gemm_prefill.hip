@@ -366,12 +366,12 @@ __device__ __forceinline__ void medium_tile(bf16_t (*ring)[kSlotElems], __amdgpu
                        static_cast<uint32_t>(K) + lc) * 2u;
   }
 #define MED_A(KT_) (flat + 3 * kSlotElems + ((KT_) % 3) * kSub)
-#define LOAD_MED(KT_)                                                                                    \
-  {                                                                                                        \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                                          \
-        load_lds16(b_rsrc, &ring[(KT_) % 3][(wave * 64 + j * 8) * kBK], b_off[j], (KT_) * (kBK * 2));      \
-    _Pragma("unroll") for (int j = 0; j < kALoads; ++j)                                                    \
-        load_lds16(a_rsrc, MED_A(KT_) + (wave * 32 + j * 8) * kBK, ma_off[j], (KT_) * (kBK * 2));    \
+#define LOAD_MED(KT_)                                                                                 \
+  {                                                                                                   \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                                     \
+        load_lds16(b_rsrc, &ring[(KT_) % 3][(wave * 64 + j * 8) * kBK], b_off[j], (KT_) * (kBK * 2)); \
+    _Pragma("unroll") for (int j = 0; j < kALoads; ++j)                                               \
+        load_lds16(a_rsrc, MED_A(KT_) + (wave * 32 + j * 8) * kBK, ma_off[j], (KT_) * (kBK * 2));     \
   }
   // Fragment reads: every row read sits at 16*block + l16, whose swizzle
   // (row >> 1) & 7 is (l16 >> 1) & 7 for any block, so a read is a uniform
