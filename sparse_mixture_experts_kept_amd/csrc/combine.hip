@@ -14,57 +14,60 @@
 
 namespace moe {
 
+// One token row per workgroup pass: the row's slot rows and gates are read
+// once (uniform), each thread takes float4 columns c = 4 * (threadIdx.x +
+// 256 * j), and the column loop is unrolled so that several rows' loads are
+// in flight per thread.
 template <typename TO>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ y_rows,
                                                       const float* __restrict__ y_rows2,
                                                       const int32_t* __restrict__ slot_rows,
                                                       const float* __restrict__ topk_w, TO* __restrict__ y,
                                                       int64_t T, int d) {
-  const int vec_per_row = d / 4;
-  const int64_t total = T * vec_per_row;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < total;
-       i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
-    const int64_t t = i / vec_per_row;
-    const int c = static_cast<int>(i - t * vec_per_row) * 4;
+  for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
     const int64_t s0 = slot_rows[2 * t];
     const int64_t s1 = slot_rows[2 * t + 1];
     // a dropped slot (row -1) loads row 0, whose value the selects below
-    // discard: the loads stay unconditional (one batch per thread)
-    const int64_t r0 = s0 >= 0 ? s0 : 0;
-    const int64_t r1 = s1 >= 0 ? s1 : 0;
+    // discard: the loads stay unconditional
+    const float* row0 = y_rows + (s0 >= 0 ? s0 : 0) * d;
+    const float* row1 = y_rows + (s1 >= 0 ? s1 : 0) * d;
+    const float* row0b = y_rows2 ? y_rows2 + (s0 >= 0 ? s0 : 0) * d : nullptr;
+    const float* row1b = y_rows2 ? y_rows2 + (s1 >= 0 ? s1 : 0) * d : nullptr;
     const float g0 = topk_w[2 * t];
     const float g1 = topk_w[2 * t + 1];
-    float4 a = *reinterpret_cast<const float4*>(y_rows + r0 * d + c);
-    float4 b = *reinterpret_cast<const float4*>(y_rows + r1 * d + c);
-    if (y_rows2) {  // second partial sum of a split reduction, added first
-      const float4 a2 = *reinterpret_cast<const float4*>(y_rows2 + r0 * d + c);
-      const float4 b2 = *reinterpret_cast<const float4*>(y_rows2 + r1 * d + c);
-      a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
-      b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
-    }
     const bool k0 = s0 >= 0, k1 = s1 >= 0;
-    float o[4];
-    o[0] = (k0 ? g0 * a.x : 0.0f) + (k1 ? g1 * b.x : 0.0f);
-    o[1] = (k0 ? g0 * a.y : 0.0f) + (k1 ? g1 * b.y : 0.0f);
-    o[2] = (k0 ? g0 * a.z : 0.0f) + (k1 ? g1 * b.z : 0.0f);
-    o[3] = (k0 ? g0 * a.w : 0.0f) + (k1 ? g1 * b.w : 0.0f);
-    if constexpr (sizeof(TO) == 4) {
-      *reinterpret_cast<float4*>(y + t * d + c) = make_float4(o[0], o[1], o[2], o[3]);
-    } else {
-      uint2 p;
-      p.x = pack_bf16x2(o[0], o[1]);
-      p.y = pack_bf16x2(o[2], o[3]);
-      *reinterpret_cast<uint2*>(y + t * d + c) = p;
+#pragma unroll 4
+    for (int c = static_cast<int>(threadIdx.x) * 4; c < d; c += 4 * 256) {
+      float4 a = *reinterpret_cast<const float4*>(row0 + c);
+      float4 b = *reinterpret_cast<const float4*>(row1 + c);
+      if (y_rows2) {  // second partial sum of a split reduction, added first
+        const float4 a2 = *reinterpret_cast<const float4*>(row0b + c);
+        const float4 b2 = *reinterpret_cast<const float4*>(row1b + c);
+        a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
+        b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
+      }
+      float o[4];
+      o[0] = (k0 ? g0 * a.x : 0.0f) + (k1 ? g1 * b.x : 0.0f);
+      o[1] = (k0 ? g0 * a.y : 0.0f) + (k1 ? g1 * b.y : 0.0f);
+      o[2] = (k0 ? g0 * a.z : 0.0f) + (k1 ? g1 * b.z : 0.0f);
+      o[3] = (k0 ? g0 * a.w : 0.0f) + (k1 ? g1 * b.w : 0.0f);
+      if constexpr (sizeof(TO) == 4) {
+        *reinterpret_cast<float4*>(y + t * d + c) = make_float4(o[0], o[1], o[2], o[3]);
+      } else {
+        uint2 p;
+        p.x = pack_bf16x2(o[0], o[1]);
+        p.y = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<uint2*>(y + t * d + c) = p;
+      }
     }
   }
 }
 
 hipError_t launch_combine(int dtype, const float* y_rows, const float* y_rows2, const int32_t* slot_rows,
                           const float* topk_w, void* y, int64_t T, int d, int n_cu, hipStream_t s) {
-  const int64_t total = T * (d / 4);
-  int64_t blocks = (total + 255) / 256;
+  if (T <= 0) return hipSuccess;
   const int64_t cap = static_cast<int64_t>(n_cu) * 16;
-  if (blocks > cap) blocks = cap;
+  const int64_t blocks = T < cap ? T : cap;
   if (dtype == kDtypeBF16)
     hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, y_rows, y_rows2, slot_rows, topk_w,
                        static_cast<bf16_t*>(y), T, d);
