@@ -201,6 +201,10 @@ def main():
                        "routing": "near-uniform (router std 0.02)", "counts": layer.counts.cpu().tolist()},
             "layer_frac_of_bf16_peak": flops / sec / A.PEAK_BF16_FLOPS,
             "stage_ms": stages,
+            "stage_ms_note": "each stage through its standalone entry point (the binding's output allocation and "
+                             "launch gaps included; the permute stage is the general one-workgroup permutation, "
+                             "which the layer replaces by the router's group counts and one wave per 16-token "
+                             "group); the up stage is the roofline's GEMM + tail pair",
             "roofline": {"kernel": "up projection + SwiGLU: grouped_gemm_prefill_kernel<true, 1> + tail "
                                    "decode_stream_kernel<true, true, ...>",
                          "bound": "mfma", "achieved": up_flops / up_s / 1e12, "peak": A.PEAK_BF16_FLOPS / 1e12,
