@@ -620,6 +620,34 @@ def test_down_unsplit_from_one_full_round():
     assert plan["tail_parts"] >= 2, (counts, plan)
 
 
+@pytest.mark.parametrize("d,out", [(1152, "f32"), (5120, "f32"), (1152, "bf16"), (128, "bf16")])
+def test_combine_row_widths(d, out):
+    # The combine takes one token row per workgroup pass, 256 threads over the
+    # row's float4 columns: rows of 288 and 1280 float4 (a partial second or
+    # fifth pass) and of 32 (most threads idle).  Dropped slots (-1) add
+    # nothing.  The oracle adds each kept slot's gated row in fp64; the GPU
+    # rounds its fp32 products and sum once more (and to bf16).
+    T = 37
+    rng = np.random.default_rng(d)
+    y_rows = rng.standard_normal((2 * T, d)).astype(np.float32)
+    rows = rng.permutation(2 * T).astype(np.int32).reshape(T, 2)
+    rows[rng.random((T, 2)) < 0.1] = -1
+    g0 = rng.uniform(0.5, 1.0, T)
+    gates = np.stack([g0, 1.0 - g0], axis=1).astype(np.float32)
+    dtype = torch.float32 if out == "f32" else torch.bfloat16
+    y = moe.combine(torch.from_numpy(y_rows).cuda(), torch.from_numpy(rows.reshape(-1)).cuda(),
+                    torch.from_numpy(gates).cuda(), dtype)
+    torch.cuda.synchronize()
+    ref = np.zeros((T, d))
+    for t in range(T):
+        for j in range(2):
+            if rows[t, j] >= 0:
+                ref[t] += np.float64(gates[t, j]) * y_rows[rows[t, j]].astype(np.float64)
+    got = y.float().cpu().numpy().astype(np.float64)
+    tol = 1e-6 if out == "f32" else 2.0 ** -8
+    assert np.all(np.abs(got - ref) <= tol * np.abs(ref) + 1e-6), np.abs(got - ref).max()
+
+
 # --------------------------------------------------------------------------- full Mixtral-sized layers (sampled)
 
 
