@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--cpu-repeats", type=int, default=3)
     p.add_argument("--only", choices=["prefill", "skewed", "decode", "sweep", "stack", "all"], default="all")
     p.add_argument("--sweep-steps", type=int, default=10)
+    p.add_argument("--sweep-t", default=None,
+                   help="comma-separated token counts to run in the T-sweep (default: the whole sweep)")
     p.add_argument("--stack-steps", type=int, default=3)
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
@@ -308,7 +310,12 @@ def main():
         _log("sweep: generating a T=8192 layer")
         L = inputs.make_custom(8192, d, f, dtype="bf16", seed=6, device=dev)
         rows = []
-        for T in (1, 4, 16, 32, 64, 96, 128, 192, 256, 512, 1024, 2048, 4096, 8192):
+        sweep_ts = (1, 4, 16, 32, 64, 96, 128, 192, 256, 512, 1024, 2048, 4096, 8192)
+        if args.sweep_t:
+            sweep_ts = tuple(int(v) for v in args.sweep_t.split(","))
+            if any(t < 1 or t > 8192 for t in sweep_ts):
+                raise SystemExit("--sweep-t: token counts from 1 to 8192")
+        for T in sweep_ts:
             x = L["x"][:T].contiguous()
             row = {"T": T}
             for name, v in (("auto", moe.VARIANT_AUTO), ("decode", moe.VARIANT_DECODE),
