@@ -58,6 +58,9 @@ static_assert(kThinRows == kTailPartRows, "the streamed tails are the thin tiles
 constexpr int kSlotElems = kBM * kBK;  // one 32 KiB slot (kBM == kBN)
 // Word 3 of a raw buffer resource on gfx9 (no format conversion).
 constexpr int kBufferFlags = 0x00020000;
+// num_records of the GEMM's resources: every unsigned 32-bit byte offset but
+// the last is in range (offsets here stay below T*d*2 < 2^32).
+constexpr int kWholeRange = static_cast<int>(0xFFFFFFFFu);
 
 #define GLOBAL_PTR(p) ((const __attribute__((address_space(1))) void*)(p))
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
@@ -592,11 +595,15 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       b_off[j] = (static_cast<uint32_t>(j * 8 + ld_row) * static_cast<uint32_t>(K) + ((j & 1) ? lc_odd : lc_even)) * 2u;
-    // Raw buffer resources (stride 0; loads past num_records would read zero).
-    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a_base), 0, 0x7FFFFFFF,
-                                                                           kBufferFlags);
-    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(b_base), 0, 0x7FFFFFFF,
-                                                                           kBufferFlags);
+    // Raw buffer resources (stride 0).  A load whose offset reaches
+    // num_records would read zeros, so the range covers every 32-bit offset:
+    // the gathered token rows of x reach T*d*2 bytes (up to 4 GiB), and no
+    // load here relies on the range check (rows are clamped, weight blocks
+    // stay inside their expert).
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(a_base), 0,
+                                                                           kWholeRange, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(b_base), 0,
+                                                                           kWholeRange, kBufferFlags);
 
     if (rows - m0 <= kThinRows) {
       // Thin tile: an expert's last m-tile with at most 32 rows.  The four

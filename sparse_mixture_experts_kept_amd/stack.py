@@ -60,20 +60,25 @@ class MoEStack:
         self.resid.copy_(x0)
         self._glue(None, 0)
 
-    def forward(self, capture=()):
+    def forward(self, capture=(), rows=None):
         """Run all layers on the loaded input.  ``capture``: layer indices whose
-        input u_l, output y_l and expert ids are cloned and returned as
-        {l: (u_l, y_l, topk_idx_l)}."""
+        input u_l, output y_l and expert ids are copied and returned as
+        {l: (u_l, y_l, topk_idx_l)}; ``rows`` (a device index tensor or None)
+        keeps only those token rows of each."""
         out = {}
+
+        def keep(t):
+            return t.clone() if rows is None else t.index_select(0, rows)
+
         for layer_idx in range(self.L):
-            u_in = self.u.clone() if layer_idx in capture else None
+            u_in = keep(self.u) if layer_idx in capture else None
             if self.fused:
-                idx_in = self.idx.clone() if layer_idx in capture else None
+                idx_in = keep(self.idx) if layer_idx in capture else None
                 y = self.routed[layer_idx](self.idx, self.w)
             else:
                 y = self.layers[layer_idx]()
-                idx_in = self.layers[layer_idx].idx.clone() if layer_idx in capture else None
+                idx_in = keep(self.layers[layer_idx].idx) if layer_idx in capture else None
             if layer_idx in capture:
-                out[layer_idx] = (u_in, y.clone(), idx_in)
+                out[layer_idx] = (u_in, keep(y), idx_in)
             self._glue(y, layer_idx + 1 if layer_idx + 1 < self.L else None)
         return out
