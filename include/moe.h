@@ -135,10 +135,16 @@ moe_status moe_router_topk(const moe_dims* dims, const void* x, const void* w_ga
  *   ...: a stable order; entries past offsets[E] are left as they were),
  *   slot_rows [T * k] int32 (inverse: position of slot s in sorted_slots, or
  *   -1 for a slot dropped by dims->capacity).
- *   Deterministic.  Runs as one workgroup.
+ *   workspace: caller-owned device memory, 16-byte aligned, for per-group
+ *   counts (ceil(T/16) * E int32 when 512 < T <= 65536; at least 256 bytes
+ *   otherwise); workspace == NULL is a size query as in moe_ffn_forward.
+ *   Deterministic (no atomics).  Up to 512 tokens one workgroup; up to 65536
+ *   tokens one launch counts each 16-token group's slots per expert and a
+ *   second places them, one wave per group; beyond, one workgroup.
  */
 moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* expert_offsets,
-                       int32_t* sorted_slots, int32_t* slot_rows, void* stream);
+                       int32_t* sorted_slots, int32_t* slot_rows, void* workspace, size_t* workspace_bytes,
+                       void* stream);
 
 /*
  * Both expert projections for every slot, in expert-major order:
@@ -200,6 +206,31 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
                            void* stream);
 
 /*
+ * moe_ffn_forward with its stages timed, for measurement: the same launches
+ * on the same stream, with an event recorded at each stage boundary.
+ *   stage_events: 8 hipEvent_t handles (passed as void*), created by the
+ *   caller; event i is recorded before stage i and event i+1 after it, for
+ *   the stages router, permute, up GEMM, up remainder fixup and expert
+ *   tails, down GEMM, down tails and fixup, combine.  A
+ *   stage the chosen kernels do not have gets two back-to-back events.
+ *   up_gemm_clock: NULL, or int64 [4 * G] in device memory with G the
+ *   CU count rounded down to a multiple of 8 (256 on MI355X); when the layer
+ *   runs the prefill up GEMM, its clock-recording twin (same kernel, plus
+ *   two counter reads) stores per workgroup b the shader clock counter at
+ *   start and end and the constant 100 MHz reference counter at start and
+ *   end in [4b .. 4b+3]; otherwise the buffer is left as it was.
+ * The sum of the seven stages is the layer: moe_ffn_forward's output and
+ * routing are computed exactly as by moe_ffn_forward.  Other arguments,
+ * errors and workspace as moe_ffn_forward (a NULL stage_events array or
+ * event -> MOE_ERR_INVALID_ARGUMENT).  The events' timing is the caller's.
+ */
+moe_status moe_ffn_forward_timed(const moe_dims* dims, const void* x, const void* w_gate,
+                                 const float* logit_bias, const void* w1, const void* w3,
+                                 const void* w2, void* y, int32_t* topk_idx_out, float* topk_w_out,
+                                 int32_t* expert_counts_out, void* workspace, size_t* workspace_bytes,
+                                 void* stream, void* const* stage_events, int64_t* up_gemm_clock);
+
+/*
  * The whole layer from a routing computed elsewhere (by
  * moe_rmsnorm_residual_route, or any top-2 pairs and gates): permutation,
  * both expert projections and the combine, as moe_ffn_forward without its
@@ -211,6 +242,35 @@ moe_status moe_ffn_forward_routed(const moe_dims* dims, const void* x, const int
                                   const float* topk_w, const void* w1, const void* w3, const void* w2,
                                   void* y, int32_t* expert_counts_out, void* workspace,
                                   size_t* workspace_bytes, void* stream);
+
+/*
+ * One stacked block's MoE half with the combine fused into the glue that
+ * follows it: moe_ffn_forward_routed on x (the layer's input u_l) and its
+ * routing, except that the gate-weighted pair of each token's expert rows is
+ * added straight into the fp32 residual instead of being written as y, then
+ * u_out = resid / sqrt(mean(resid^2) + eps) and, when w_gate_next is given,
+ * the next layer's pair and gates from the rounded u_out, as
+ * moe_rmsnorm_residual_route computes them.  The added row is the layer's
+ * output y rounded to dtype exactly as moe_combine rounds it, so the result
+ * equals moe_ffn_forward_routed followed by moe_rmsnorm_residual_route bit
+ * for bit, without y's round trip through memory.  ("Mixtral & Sparse MoE
+ * (2024) > The Solution", routing paragraph: outputs combined by the routing
+ * scores; "Mixtral > Architecture Overview", layer-components list: the
+ * blocks are stacked on a residual stream.)
+ *   resid [T, d] fp32 in/out, u_out [T, d] (dtype) output; u_out may be x
+ *   and topk_idx_next / topk_w_next may be topk_idx / topk_w (each is read
+ *   before it is overwritten).  w_gate_next [E, d], logit_bias_next [E] or
+ *   NULL; with w_gate_next NULL no routing is computed (after the last
+ *   layer).  Limits: d <= 8192, and E * d * elem_size <= 128 KiB when
+ *   routing.  Workspace and its size query as moe_ffn_forward.
+ */
+moe_status moe_ffn_forward_routed_residual(const moe_dims* dims, const void* x, const int32_t* topk_idx,
+                                           const float* topk_w, const void* w1, const void* w3,
+                                           const void* w2, float* resid, void* u_out, float eps,
+                                           const void* w_gate_next, const float* logit_bias_next,
+                                           int32_t* topk_idx_next, float* topk_w_next,
+                                           int32_t* expert_counts_out, void* workspace,
+                                           size_t* workspace_bytes, void* stream);
 
 /*
  * Auxiliary load-balancing loss, loss[0] = E * sum_e f_e * P_e, with f_e the

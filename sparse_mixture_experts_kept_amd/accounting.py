@@ -114,3 +114,16 @@ def prefill_rows_issued(counts, tile_rows: int = 256, tail_rows: int = 32, group
         else:
             gemm += (tiles - 1) * tile_rows + min(h for h in tile_heights if h >= last)
     return needed, gemm, tails
+
+
+def prefill_gemm_rows(counts, tile_rows: int = 256, tail_rows: int = 32) -> int:
+    """Rows (unpadded) the prefill GEMM launch computes itself: every row
+    but an expert's short tail (a last tile of at most ``tail_rows`` rows
+    after at least one full tile), which its own launch computes."""
+    rows = 0
+    for c in counts:
+        c = int(c)
+        tiles = -(-c // tile_rows)
+        last = c - (tiles - 1) * tile_rows
+        rows += c - (last if tiles >= 2 and last <= tail_rows else 0)
+    return rows

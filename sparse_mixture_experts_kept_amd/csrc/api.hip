@@ -70,6 +70,21 @@ bool use_decode(const moe_dims* dims) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Stage boundaries of the layer (moe_ffn_forward_timed): an event is
+// recorded on the layer's stream after each stage (the up GEMM's own, event
+// 3, right after the GEMM launch), and the up GEMM may run as its
+// clock-recording twin.  Null marks record nothing.
+constexpr int kStageEvents = 8;
+struct StageMarks {
+  void* const* ev = nullptr;  // kStageEvents hipEvent_t
+  long long* clk = nullptr;   // 4 int64 per workgroup of the up GEMM
+};
+moe_status mark(const StageMarks* m, int i, hipStream_t s) {
+  if (!m || !m->ev) return MOE_OK;
+  return hip_status(hipEventRecord(static_cast<hipEvent_t>(m->ev[i]), s));
+}
+long long* up_clock(const StageMarks* m) { return m ? m->clk : nullptr; }
+
 // Prefill projections hand the short expert tails (the rows past an expert's
 // last full 256-row tile, when at most 32) to the streaming kernels, which
 // spread each tail's weight stream over the whole chip; inside the prefill
@@ -87,10 +102,12 @@ bool tails_streamable(const moe_dims* dims) {
 // cut along the reduction and their partial tiles summed by a fixup launch).
 moe_status up_prefill(const moe_dims* dims, const bf16_t* x, const int32_t* offs, const int32_t* sorted,
                       const bf16_t* w1, const bf16_t* w3, bf16_t* h, int n_cu, float* partials,
-                      int64_t partial_bytes, hipStream_t s) {
+                      int64_t partial_bytes, hipStream_t s, const StageMarks* marks = nullptr) {
   const bool tails = kUpTailsStreamed && tails_streamable(dims);
   moe_status st = hip_status(moe::launch_up_prefill(x, offs, sorted, w1, w3, h, dims->d, dims->f, n_cu, tails,
-                                                    partials, partial_bytes, s));
+                                                    partials, partial_bytes, s, up_clock(marks),
+                                                    marks && marks->ev ? static_cast<hipEvent_t>(marks->ev[3])
+                                                                       : nullptr));
   if (st != MOE_OK || !tails) return st;
   return hip_status(moe::launch_up_tail_stream(x, offs, sorted, w1, w3, h, dims->T, dims->d, dims->f, n_cu, s));
 }
@@ -101,13 +118,14 @@ moe_status up_prefill(const moe_dims* dims, const bf16_t* x, const int32_t* offs
 // launch after the tails completes both.
 moe_status down_prefill(const moe_dims* dims, const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows,
                         int n_cu, int split, int64_t split_stride, float* partials, int64_t partial_bytes,
-                        hipStream_t s) {
+                        hipStream_t s, const StageMarks* marks = nullptr) {
   const bool tails = split == 1 && tails_streamable(dims);
   const int64_t plane_bytes = std::min<int64_t>(partial_bytes, int64_t{n_cu} * 256 * 256 * 4);
   float* tail_part = partials && partial_bytes > plane_bytes ? partials + plane_bytes / 4 : nullptr;
   const int64_t tail_bytes = tail_part ? partial_bytes - plane_bytes : 0;
   moe_status st = hip_status(moe::launch_down_prefill(h, offs, w2, y_rows, dims->d, dims->f, n_cu, split,
                                                       split_stride, tails, partials, plane_bytes, s));
+  if (st == MOE_OK) st = mark(marks, 5, s);
   if (st != MOE_OK) return st;
   if (tails) {
     st = hip_status(moe::launch_down_tail_stream(h, offs, w2, y_rows, dims->T, dims->d, dims->f, n_cu, tail_part,
@@ -138,7 +156,10 @@ Workspace plan_workspace(const moe_dims* dims) {
   ws.gcounts = o; o += align256(static_cast<size_t>((dims->T + 15) / 16) * dims->E * 4);  // router group counts
   ws.h = o; o += align256(slots * dims->f * elem_size(dims->dtype));
   ws.y_rows = o; o += align256(slots * dims->d * 4);
-  ws.y_rows2 = o; o += align256(slots * dims->d * 4);  // second partial of the split down projection
+  // Second partial of the split down projection (and the prefill GEMMs'
+  // partial tiles): only the bf16 prefill kernels use it.
+  ws.y_rows2 = o;
+  if (dims->dtype == MOE_BF16 && !use_decode(dims)) o += align256(slots * dims->d * 4);
   ws.total = o;
   return ws;
 }
@@ -192,10 +213,17 @@ moe_status run_down(const moe_dims* dims, const void* h, const int32_t* offs, co
 }
 
 moe_status run_experts(const moe_dims* dims, const void* x, const int32_t* offs, const int32_t* sorted,
-                       const void* w1, const void* w3, const void* w2, void* h, float* y_rows, hipStream_t s) {
-  const moe_status st = run_up(dims, x, offs, sorted, w1, w3, h, s);
+                       const void* w1, const void* w3, const void* w2, void* h, float* y_rows, hipStream_t s,
+                       const StageMarks* marks = nullptr) {
+  // (the decode and fp32 paths have no separate tail stage: marks 3/4 and 5/6 coincide)
+  moe_status st = run_up(dims, x, offs, sorted, w1, w3, h, s);
+  if (st == MOE_OK) st = mark(marks, 3, s);
+  if (st == MOE_OK) st = mark(marks, 4, s);
   if (st != MOE_OK) return st;
-  return run_down(dims, h, offs, w2, y_rows, s);
+  st = run_down(dims, h, offs, w2, y_rows, s);
+  if (st == MOE_OK) st = mark(marks, 5, s);
+  if (st == MOE_OK) st = mark(marks, 6, s);
+  return st;
 }
 
 moe_status run_combine(const moe_dims* dims, const float* y_rows, const int32_t* slot_rows, const float* w, void* y,
@@ -237,16 +265,31 @@ moe_status moe_router_topk(const moe_dims* dims, const void* x, const void* w_ga
 }
 
 moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* expert_offsets, int32_t* sorted_slots,
-                       int32_t* slot_rows, void* stream) {
+                       int32_t* slot_rows, void* workspace, size_t* workspace_bytes, void* stream) {
   moe_status st = check_dims(dims);
   if (st != MOE_OK) return st;
+  if (!workspace_bytes) return MOE_ERR_INVALID_ARGUMENT;
+  // Group counts [ceil(T/16), 8] for the multi-workgroup form (a token
+  // count the one-workgroup forms handle still asks for a minimal workspace).
+  const bool groups = dims->T * dims->k > moe::kPermuteSmallSlots && dims->T <= moe::kMaxGroupPermuteTokens;
+  const size_t need = groups ? align256(static_cast<size_t>((dims->T + 15) / 16) * dims->E * 4) : 256;
+  if (!workspace) {
+    *workspace_bytes = need;
+    return MOE_OK;
+  }
   if (dims->T == 0) return MOE_OK;
+  if (*workspace_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (!expert_offsets || !topk_idx || !sorted_slots || !slot_rows) return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned(topk_idx, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_slots, 4) || !aligned(slot_rows, 4))
+  if (!aligned(topk_idx, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_slots, 4) || !aligned(slot_rows, 4) ||
+      !aligned(workspace, 16))
     return MOE_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (groups)
+    return hip_status(moe::launch_permute_counted(topk_idx, static_cast<int32_t>(dims->T),
+                                                  static_cast<int32_t*>(workspace), expert_offsets, sorted_slots,
+                                                  slot_rows, nullptr, dims->capacity, s));
   return hip_status(moe::launch_permute(topk_idx, static_cast<int32_t>(dims->T * dims->k), expert_offsets,
-                                        sorted_slots, slot_rows, nullptr, dims->capacity,
-                                        static_cast<hipStream_t>(stream)));
+                                        sorted_slots, slot_rows, nullptr, dims->capacity, s));
 }
 
 moe_status moe_grouped_swiglu(const moe_dims* dims, const void* x, const int32_t* expert_offsets,
@@ -300,12 +343,38 @@ moe_status moe_combine(const moe_dims* dims, const float* y_rows, const int32_t*
 
 namespace {
 
+// The glue that takes the place of the combine in
+// moe_ffn_forward_routed_residual (null: the combine writes y).
+struct ResidualGlue {
+  float* resid;
+  void* u;
+  float eps;
+  const void* wg;
+  const float* bias;
+  int32_t* idx;
+  float* w;
+};
+
+moe_status combine_or_glue(const moe_dims* dims, const float* y_rows, const float* y_rows2, const int32_t* rows,
+                           const float* gate, void* y, const ResidualGlue* glue, int n_cu, hipStream_t s) {
+  if (!glue)
+    return hip_status(moe::launch_combine(dims->dtype, y_rows, y_rows2, rows, gate, y, dims->T, dims->d, n_cu, s));
+  return hip_status(moe::launch_combine_rmsnorm_route(dims->dtype, y_rows, y_rows2, rows, gate, glue->resid, glue->u,
+                                                      glue->wg, glue->bias, glue->idx, glue->w, dims->T, dims->d,
+                                                      glue->eps, dims->gating, n_cu, s));
+}
+
+struct ResidualGlue;
+moe_status combine_or_glue(const moe_dims* dims, const float* y_rows, const float* y_rows2, const int32_t* rows,
+                           const float* gate, void* y, const ResidualGlue* glue, int n_cu, hipStream_t s);
+
 // The whole layer.  routed_idx / routed_w given: the routing was computed by
 // the caller (e.g. by moe_rmsnorm_residual_route) and the router is skipped.
 moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_gate, const float* logit_bias,
                             const int32_t* routed_idx, const float* routed_w, const void* w1, const void* w3,
                             const void* w2, void* y, int32_t* topk_idx_out, float* topk_w_out,
-                            int32_t* expert_counts_out, void* workspace, size_t* workspace_bytes, void* stream) {
+                            int32_t* expert_counts_out, void* workspace, size_t* workspace_bytes, void* stream,
+                            const StageMarks* marks = nullptr, const ResidualGlue* glue = nullptr) {
   const bool routed = routed_idx != nullptr;
   moe_status st = check_dims(dims);
   if (st != MOE_OK) return st;
@@ -319,9 +388,11 @@ moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_g
   }
   if (dims->T == 0) return MOE_OK;
   if (*workspace_bytes < plan.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  if (!x || (!routed && !w_gate) || (routed && !routed_w) || !w1 || !w3 || !w2 || !y) return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned(workspace, 256) || !aligned(x, 16) || (w_gate && !aligned(w_gate, 16)) || !aligned(w1, 16) ||
-      !aligned(w3, 16) || !aligned(w2, 16) || !aligned(y, 16) || (logit_bias && !aligned(logit_bias, 16)) ||
+  if (!x || (!routed && !w_gate) || (routed && !routed_w) || !w1 || !w3 || !w2 || (!glue && !y))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(workspace, 256) || !aligned(x, 16) || (w_gate && !aligned(w_gate, 16)) ||
+      !aligned(w1, 16) || !aligned(w3, 16) || !aligned(w2, 16) || (y && !aligned(y, 16)) ||
+      (logit_bias && !aligned(logit_bias, 16)) ||
       (topk_idx_out && !aligned(topk_idx_out, 8)) || (topk_w_out && !aligned(topk_w_out, 8)) ||
       (routed_idx && !aligned(routed_idx, 8)) || (routed_w && !aligned(routed_w, 8)) ||
       (expert_counts_out && !aligned(expert_counts_out, 4)))
@@ -339,7 +410,11 @@ moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_g
   void* h = ws + plan.h;
   float* y_rows = reinterpret_cast<float*>(ws + plan.y_rows);
 
+  st = mark(marks, 0, s);
+  if (st != MOE_OK) return st;
   if (routed) {
+    st = mark(marks, 1, s);
+    if (st != MOE_OK) return st;
     st = hip_status(moe::launch_permute(pair, static_cast<int32_t>(dims->T * dims->k), offs, sorted, rows,
                                         expert_counts_out, dims->capacity, s));
     if (st != MOE_OK) return st;
@@ -356,17 +431,23 @@ moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_g
     // permutation then runs one wave per group.
     int32_t* gcounts = reinterpret_cast<int32_t*>(ws + plan.gcounts);
     st = run_router(dims, x, w_gate, logit_bias, idx, w, nullptr, s, gcounts);
+    if (st == MOE_OK) st = mark(marks, 1, s);
     if (st != MOE_OK) return st;
     st = hip_status(moe::launch_permute_groups(idx, static_cast<int32_t>(dims->T), gcounts, offs, sorted, rows,
                                                expert_counts_out, dims->capacity, s));
     if (st != MOE_OK) return st;
   } else {
     st = run_router(dims, x, w_gate, logit_bias, idx, w, nullptr, s);
+    if (st == MOE_OK) st = mark(marks, 1, s);
     if (st != MOE_OK) return st;
     st = hip_status(moe::launch_permute(idx, static_cast<int32_t>(dims->T * dims->k), offs, sorted, rows,
                                         expert_counts_out, dims->capacity, s));
     if (st != MOE_OK) return st;
   }
+  // (routing and permutation in one launch: the routing stage holds both)
+  if (!routed && dims->T <= kRoutePermuteMaxTokens) st = mark(marks, 1, s);
+  if (st == MOE_OK) st = mark(marks, 2, s);
+  if (st != MOE_OK) return st;
   if (dims->dtype == MOE_BF16 && !use_decode(dims)) {
     // Prefill.  The down projection's reduction is split in two when the
     // layer has fewer full 256 x 256 tiles than CUs (twice the work units to
@@ -381,20 +462,25 @@ moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_g
     float* second = reinterpret_cast<float*>(ws + plan.y_rows2);
     const int64_t second_bytes = static_cast<int64_t>(plan.total - plan.y_rows2);
     st = up_prefill(dims, static_cast<const bf16_t*>(x), offs, sorted, static_cast<const bf16_t*>(w1),
-                    static_cast<const bf16_t*>(w3), static_cast<bf16_t*>(h), n_cu, second, second_bytes, s);
+                    static_cast<const bf16_t*>(w3), static_cast<bf16_t*>(h), n_cu, second, second_bytes, s, marks);
+    if (st == MOE_OK) st = mark(marks, 4, s);
     if (st != MOE_OK) return st;
     const int64_t full_units = (dims->T * dims->k / 256) * (dims->d / 256);
     const int split = full_units >= n_cu ? 1 : 2;
     float* y_rows2 = split == 2 ? second : nullptr;
     st = down_prefill(dims, static_cast<const bf16_t*>(h), offs, static_cast<const bf16_t*>(w2), y_rows, n_cu, split,
-                      split == 2 ? y_rows2 - y_rows : 0, split == 2 ? nullptr : second, second_bytes, s);
+                      split == 2 ? y_rows2 - y_rows : 0, split == 2 ? nullptr : second, second_bytes, s, marks);
+    if (st == MOE_OK) st = mark(marks, 6, s);
     if (st != MOE_OK) return st;
-    return hip_status(
-        moe::launch_combine(dims->dtype, y_rows, y_rows2, rows, gate, y, dims->T, dims->d, n_cu, s));
+    st = combine_or_glue(dims, y_rows, y_rows2, rows, gate, y, glue, n_cu, s);
+    return st == MOE_OK ? mark(marks, 7, s) : st;
   }
-  st = run_experts(dims, x, offs, sorted, w1, w3, w2, h, y_rows, s);
+  st = run_experts(dims, x, offs, sorted, w1, w3, w2, h, y_rows, s, marks);
   if (st != MOE_OK) return st;
-  return run_combine(dims, y_rows, rows, gate, y, s);
+  int n_cu = 0;
+  st = cu_count(&n_cu);
+  if (st == MOE_OK) st = combine_or_glue(dims, y_rows, nullptr, rows, gate, y, glue, n_cu, s);
+  return st == MOE_OK ? mark(marks, 7, s) : st;
 }
 
 }  // namespace
@@ -409,6 +495,22 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
                           expert_counts_out, workspace, workspace_bytes, stream);
 }
 
+moe_status moe_ffn_forward_timed(const moe_dims* dims, const void* x, const void* w_gate, const float* logit_bias,
+                                 const void* w1, const void* w3, const void* w2, void* y, int32_t* topk_idx_out,
+                                 float* topk_w_out, int32_t* expert_counts_out, void* workspace,
+                                 size_t* workspace_bytes, void* stream, void* const* stage_events,
+                                 int64_t* up_gemm_clock) {
+  if (!stage_events) return MOE_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < kStageEvents; ++i)
+    if (!stage_events[i]) return MOE_ERR_INVALID_ARGUMENT;
+  if (up_gemm_clock && !aligned(up_gemm_clock, 8)) return MOE_ERR_INVALID_ARGUMENT;
+  StageMarks marks;
+  marks.ev = stage_events;
+  marks.clk = reinterpret_cast<long long*>(up_gemm_clock);
+  return ffn_forward_impl(dims, x, w_gate, logit_bias, nullptr, nullptr, w1, w3, w2, y, topk_idx_out, topk_w_out,
+                          expert_counts_out, workspace, workspace_bytes, stream, &marks);
+}
+
 moe_status moe_ffn_forward_routed(const moe_dims* dims, const void* x, const int32_t* topk_idx, const float* topk_w,
                                   const void* w1, const void* w3, const void* w2, void* y,
                                   int32_t* expert_counts_out, void* workspace, size_t* workspace_bytes,
@@ -416,6 +518,29 @@ moe_status moe_ffn_forward_routed(const moe_dims* dims, const void* x, const int
   // (a NULL topk_idx leaves no router and no routing: INVALID_ARGUMENT, except for the size query)
   return ffn_forward_impl(dims, x, nullptr, nullptr, topk_idx, topk_w, w1, w3, w2, y, nullptr, nullptr,
                           expert_counts_out, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_ffn_forward_routed_residual(const moe_dims* dims, const void* x, const int32_t* topk_idx,
+                                           const float* topk_w, const void* w1, const void* w3, const void* w2,
+                                           float* resid, void* u_out, float eps, const void* w_gate_next,
+                                           const float* logit_bias_next, int32_t* topk_idx_next,
+                                           float* topk_w_next, int32_t* expert_counts_out, void* workspace,
+                                           size_t* workspace_bytes, void* stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (dims->d > moe::kMaxNormRouteD) return MOE_ERR_UNSUPPORTED;
+  if (w_gate_next && static_cast<size_t>(dims->E) * dims->d * elem_size(dims->dtype) > kRouterLdsLimit)
+    return MOE_ERR_UNSUPPORTED;
+  if (workspace && dims->T > 0) {
+    if (!resid || !u_out || (w_gate_next && (!topk_idx_next || !topk_w_next))) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned(resid, 16) || !aligned(u_out, 16) || (w_gate_next && !aligned(w_gate_next, 16)) ||
+        (logit_bias_next && !aligned(logit_bias_next, 16)) || (topk_idx_next && !aligned(topk_idx_next, 8)) ||
+        (topk_w_next && !aligned(topk_w_next, 8)))
+      return MOE_ERR_INVALID_ARGUMENT;
+  }
+  const ResidualGlue glue{resid, u_out, eps, w_gate_next, logit_bias_next, topk_idx_next, topk_w_next};
+  return ffn_forward_impl(dims, x, nullptr, nullptr, topk_idx, topk_w, w1, w3, w2, nullptr, nullptr, nullptr,
+                          expert_counts_out, workspace, workspace_bytes, stream, nullptr, &glue);
 }
 
 moe_status moe_rmsnorm_residual_route(const moe_dims* dims, float* resid, const void* y_add, void* u_out, float eps,

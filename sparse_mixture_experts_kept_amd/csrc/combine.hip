@@ -40,17 +40,17 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     for (int c = static_cast<int>(threadIdx.x) * 4; c < d; c += 4 * 256) {
       float4 a = *reinterpret_cast<const float4*>(row0 + c);
       float4 b = *reinterpret_cast<const float4*>(row1 + c);
-      if (y_rows2) {  // second partial sum of a split reduction, added first
+      if (y_rows2) {  // second partial sum of a split reduction, added to the first
         const float4 a2 = *reinterpret_cast<const float4*>(row0b + c);
         const float4 b2 = *reinterpret_cast<const float4*>(row1b + c);
-        a.x += a2.x; a.y += a2.y; a.z += a2.z; a.w += a2.w;
-        b.x += b2.x; b.y += b2.y; b.z += b2.z; b.w += b2.w;
+        a.x = __fadd_rn(a.x, a2.x); a.y = __fadd_rn(a.y, a2.y); a.z = __fadd_rn(a.z, a2.z); a.w = __fadd_rn(a.w, a2.w);
+        b.x = __fadd_rn(b.x, b2.x); b.y = __fadd_rn(b.y, b2.y); b.z = __fadd_rn(b.z, b2.z); b.w = __fadd_rn(b.w, b2.w);
       }
       float o[4];
-      o[0] = (k0 ? g0 * a.x : 0.0f) + (k1 ? g1 * b.x : 0.0f);
-      o[1] = (k0 ? g0 * a.y : 0.0f) + (k1 ? g1 * b.y : 0.0f);
-      o[2] = (k0 ? g0 * a.z : 0.0f) + (k1 ? g1 * b.z : 0.0f);
-      o[3] = (k0 ? g0 * a.w : 0.0f) + (k1 ? g1 * b.w : 0.0f);
+      o[0] = combine_pair(a.x, b.x, g0, g1, k0, k1);
+      o[1] = combine_pair(a.y, b.y, g0, g1, k0, k1);
+      o[2] = combine_pair(a.z, b.z, g0, g1, k0, k1);
+      o[3] = combine_pair(a.w, b.w, g0, g1, k0, k1);
       if constexpr (sizeof(TO) == 4) {
         *reinterpret_cast<float4*>(y + t * d + c) = make_float4(o[0], o[1], o[2], o[3]);
       } else {

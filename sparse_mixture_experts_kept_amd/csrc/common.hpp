@@ -38,6 +38,14 @@ __device__ __forceinline__ float silu(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
 }
 
+// One output element of the gate-weighted combine, the two slots added in
+// slot order: g0*a + g1*b, a dropped slot (k = false) adding nothing.  Each
+// operation rounds once (no contraction into a fused multiply-add), so every
+// kernel that combines gives the same bits.
+__device__ __forceinline__ float combine_pair(float a, float b, float g0, float g1, bool k0, bool k1) {
+  return __fadd_rn(k0 ? __fmul_rn(g0, a) : 0.0f, k1 ? __fmul_rn(g1, b) : 0.0f);
+}
+
 template <typename T>
 __device__ __forceinline__ float to_f32(T v);
 template <>

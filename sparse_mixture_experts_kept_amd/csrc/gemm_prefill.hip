@@ -484,14 +484,23 @@ __device__ __forceinline__ void medium_tile(bf16_t (*ring)[kSlotElems], __amdgpu
 // SPLITK equal parts run as separate work units; part s writes its partial
 // sums to Cout + s * split_stride (a separate buffer per part; the consumer
 // adds them in a fixed order).
-template <bool SWIGLU, int SPLITK>
+// CLOCKED: the same kernel, which also stores per workgroup the shader
+// clock counter and the constant-rate (100 MHz) reference counter at its
+// start and end, clk[4b .. 4b+3] = {cycles0, cycles1, ref0, ref1}: the
+// clock the GEMM ran at, measured while it runs.
+template <bool SWIGLU, int SPLITK, bool CLOCKED>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restrict__ gather,
                             const int32_t* __restrict__ offs, const bf16_t* __restrict__ B0,
                             const bf16_t* __restrict__ B1, void* __restrict__ Cout, int N, int K,
                             int64_t split_stride, int thin_elsewhere, float* __restrict__ partials,
-                            int planes) {
+                            int planes, long long* __restrict__ clk) {
   static_assert(!SWIGLU || SPLITK == 1, "the SwiGLU epilogue needs the full reduction");
+  long long cyc0 = 0, ref0 = 0;
+  if constexpr (CLOCKED) {
+    cyc0 = __builtin_amdgcn_s_memtime();
+    ref0 = __builtin_amdgcn_s_memrealtime();
+  }
   // One LDS object for all slots: A slots 0-1, B slots 2-4.
   __shared__ __align__(16) bf16_t ring[5][kSlotElems];
 
@@ -954,6 +963,17 @@ grouped_gemm_prefill_kernel(const bf16_t* __restrict__ A, const int32_t* __restr
       }
     }
   }
+  if constexpr (CLOCKED) {
+    const long long cyc1 = __builtin_amdgcn_s_memtime();
+    const long long ref1 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) {
+      long long* c = clk + 4 * static_cast<int64_t>(blockIdx.x);
+      c[0] = cyc0;
+      c[1] = cyc1;
+      c[2] = ref0;
+      c[3] = ref1;
+    }
+  }
 }
 
 // Sum over parts p = 0..P-1 of src[p * stride .. +3] (or +1), added in part
@@ -1096,14 +1116,27 @@ bool prefill_fits(int64_t T, int d, int f) {
   return d % 128 == 0 && f % 128 == 0 && d >= 256 && f >= 256 && T * d * 2 < (int64_t{1} << 32);
 }
 
+int prefill_grid(int n_cu) { return (n_cu / kXcds) * kXcds; }
+
 hipError_t launch_up_prefill(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
                              const bf16_t* w3, bf16_t* h, int d, int f, int n_cu, bool thin_elsewhere,
-                             float* partials, int64_t partial_bytes, hipStream_t s) {
-  const int grid = (n_cu / kXcds) * kXcds;
+                             float* partials, int64_t partial_bytes, hipStream_t s, long long* clk,
+                             hipEvent_t after_gemm) {
+  const int grid = prefill_grid(n_cu);
   const int planes = plane_count(partials, partial_bytes);
   float* part = planes >= 2 ? partials : nullptr;
-  hipLaunchKernelGGL((grouped_gemm_prefill_kernel<true, 1>), dim3(grid), dim3(kThreads), 0, s, x, sorted_slots, offs,
-                     w1, w3, static_cast<void*>(h), f, d, int64_t{0}, thin_elsewhere ? 1 : 0, part, planes);
+  if (clk)
+    hipLaunchKernelGGL((grouped_gemm_prefill_kernel<true, 1, true>), dim3(grid), dim3(kThreads), 0, s, x, sorted_slots,
+                       offs, w1, w3, static_cast<void*>(h), f, d, int64_t{0}, thin_elsewhere ? 1 : 0, part, planes,
+                       clk);
+  else
+    hipLaunchKernelGGL((grouped_gemm_prefill_kernel<true, 1, false>), dim3(grid), dim3(kThreads), 0, s, x,
+                       sorted_slots, offs, w1, w3, static_cast<void*>(h), f, d, int64_t{0}, thin_elsewhere ? 1 : 0,
+                       part, planes, static_cast<long long*>(nullptr));
+  if (after_gemm) {
+    const hipError_t err = hipEventRecord(after_gemm, s);
+    if (err != hipSuccess) return err;
+  }
   if (part)
     hipLaunchKernelGGL((remainder_fixup_kernel<true>), dim3(2 * grid), dim3(kThreads), 0, s, offs,
                        static_cast<const float*>(part), static_cast<void*>(h), f, d, grid, planes,
@@ -1114,19 +1147,20 @@ hipError_t launch_up_prefill(const bf16_t* x, const int32_t* offs, const int32_t
 hipError_t launch_down_prefill(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int d, int f,
                                int n_cu, int split, int64_t split_stride, bool thin_elsewhere, float* partials,
                                int64_t partial_bytes, hipStream_t s) {
-  const int grid = (n_cu / kXcds) * kXcds;
+  const int grid = prefill_grid(n_cu);
   // each work unit needs K/split to be a multiple of 64 and at least 2 stages
   if (split == 2 && f % 128 == 0 && f / 2 >= 2 * kBK) {
-    hipLaunchKernelGGL((grouped_gemm_prefill_kernel<false, 2>), dim3(grid), dim3(kThreads), 0, s, h,
+    hipLaunchKernelGGL((grouped_gemm_prefill_kernel<false, 2, false>), dim3(grid), dim3(kThreads), 0, s, h,
                        static_cast<const int32_t*>(nullptr), offs, w2, static_cast<const bf16_t*>(nullptr),
                        static_cast<void*>(y_rows), d, f, split_stride, thin_elsewhere ? 1 : 0,
-                       static_cast<float*>(nullptr), 0);
+                       static_cast<float*>(nullptr), 0, static_cast<long long*>(nullptr));
   } else {
     const int planes = plane_count(partials, partial_bytes);
     float* part = planes >= 2 ? partials : nullptr;
-    hipLaunchKernelGGL((grouped_gemm_prefill_kernel<false, 1>), dim3(grid), dim3(kThreads), 0, s, h,
+    hipLaunchKernelGGL((grouped_gemm_prefill_kernel<false, 1, false>), dim3(grid), dim3(kThreads), 0, s, h,
                        static_cast<const int32_t*>(nullptr), offs, w2, static_cast<const bf16_t*>(nullptr),
-                       static_cast<void*>(y_rows), d, f, int64_t{0}, thin_elsewhere ? 1 : 0, part, planes);
+                       static_cast<void*>(y_rows), d, f, int64_t{0}, thin_elsewhere ? 1 : 0, part, planes,
+                       static_cast<long long*>(nullptr));
   }
   return hipGetLastError();
 }

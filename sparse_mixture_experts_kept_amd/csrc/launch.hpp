@@ -21,6 +21,8 @@ hipError_t launch_router(int dtype, const void* x, const void* wg, const float* 
                          float* logits, int64_t T, int d, int gating, int n_cu, hipStream_t s,
                          int32_t* group_counts = nullptr);
 
+// Slot counts up to this take the one-workgroup ballot form (one slot per thread).
+constexpr int64_t kPermuteSmallSlots = 1024;
 // capacity > 0: each expert keeps its first `capacity` slots (slot order);
 // dropped slots get slot_rows = -1.
 hipError_t launch_permute(const int32_t* idx, int32_t n_slots, int32_t* offsets, int32_t* sorted_slots,
@@ -31,6 +33,11 @@ constexpr int64_t kMaxGroupPermuteTokens = 65536;
 hipError_t launch_permute_groups(const int32_t* idx, int32_t n_tokens, const int32_t* group_counts, int32_t* offsets,
                                  int32_t* sorted_slots, int32_t* slot_rows, int32_t* counts_out, int capacity,
                                  hipStream_t s);
+// The same from the ids alone: a first launch counts each group's slots
+// per expert into group_counts [ceil(n_tokens/16), 8] int32.
+hipError_t launch_permute_counted(const int32_t* idx, int32_t n_tokens, int32_t* group_counts, int32_t* offsets,
+                                  int32_t* sorted_slots, int32_t* slot_rows, int32_t* counts_out, int capacity,
+                                  hipStream_t s);
 // loss[0] = E * sum_e f_e * P_e from the scores [T, E] and the pairs [T, k].
 hipError_t launch_load_balance_loss(const float* logits, const int32_t* idx, int64_t T, float* loss, hipStream_t s);
 
@@ -64,9 +71,16 @@ bool prefill_fits(int64_t T, int d, int f);
 // partials (may be null): an fp32 buffer of partial_bytes for the remainder
 // split of the work units (the up projection's, then the down projection's:
 // both launches are stream-ordered); it adds a fixup launch.
+// clk (may be null): launch the clock-recording twin of the up GEMM, which
+// stores per workgroup {shader cycles at start, at end, 100 MHz reference
+// ticks at start, at end} in clk[4 * prefill_grid(n_cu)] int64.
+// after_gemm (may be null): recorded on s right after the GEMM launch
+// (before the remainder fixup).
+int prefill_grid(int n_cu);
 hipError_t launch_up_prefill(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
                              const bf16_t* w3, bf16_t* h, int d, int f, int n_cu, bool thin_elsewhere,
-                             float* partials, int64_t partial_bytes, hipStream_t s);
+                             float* partials, int64_t partial_bytes, hipStream_t s, long long* clk = nullptr,
+                             hipEvent_t after_gemm = nullptr);
 // split == 2: two partial sums over the two halves of f, the second at
 // y_rows + split_stride; otherwise one full sum in y_rows, and with
 // partials the remainder units' rows are completed by
@@ -125,5 +139,13 @@ constexpr int kMaxNormRouteD = 8192;
 hipError_t launch_rmsnorm_route(int dtype, float* resid, const void* y_add, void* u, const void* wg,
                                 const float* bias, int32_t* idx, float* w, int64_t T, int d, float eps, int gating,
                                 int n_cu, hipStream_t s);
+// The same glue with the layer's combine fused in: resid += the gate-weighted
+// pair of y_rows rows (plus y_rows2, the second partial, if given) of each
+// token, rounded to dtype exactly as launch_combine rounds y; then RMSNorm
+// and (wg != nullptr) the next layer's routing.  y is never written.
+hipError_t launch_combine_rmsnorm_route(int dtype, const float* y_rows, const float* y_rows2, const int32_t* slot_rows,
+                                        const float* gates, float* resid, void* u, const void* wg, const float* bias,
+                                        int32_t* idx, float* w, int64_t T, int d, float eps, int gating, int n_cu,
+                                        hipStream_t s);
 
 }  // namespace moe

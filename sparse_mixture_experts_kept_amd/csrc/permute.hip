@@ -6,7 +6,10 @@
 // changes no value.
 //
 // Up to 1024 slots: one slot per thread, wave ballots (permute_dev.hpp).
-// More: one workgroup of 1024 threads; thread i owns 8 consecutive slots of each
+// Up to 65536 tokens (moe_permute, or the layer from the router's counts):
+// per-group counts, then one wave per 16-token group places its 32 slots
+// (permute_groups_kernel).  Beyond, or without a group-count buffer: one
+// workgroup of 1024 threads; thread i owns 8 consecutive slots of each
 // chunk of 8192.  Pass 1: per-thread counts per expert, summed over the
 // workgroup -> offsets (exclusive scan over the 8 experts).  Pass 2, chunk by
 // chunk in slot order: per-thread counts packed two experts per 32-bit word
@@ -253,7 +256,42 @@ __global__ void __launch_bounds__(kWave) permute_groups_kernel(const int32_t* __
   }
 }
 
+// The valid slots of each 16-token group per expert, group_counts[8g + e]
+// (what the bf16 router writes for the layer): one wave per group, four
+// groups per workgroup, lane s < 32 holding slot 32g + s.
+constexpr int kCountWaves = 4;
+__global__ void __launch_bounds__(kCountWaves * kWave) group_counts_kernel(const int32_t* __restrict__ idx,
+                                                                           int32_t n_tokens,
+                                                                           int32_t* __restrict__ group_counts) {
+  const int lane = threadIdx.x % kWave;
+  const int g = blockIdx.x * kCountWaves + threadIdx.x / kWave;
+  const int n_groups = (n_tokens + 15) / 16;
+  if (g >= n_groups) return;
+  const int s = g * 32 + lane;
+  const int e = (lane < 32 && s < n_tokens * kTopK) ? valid_expert(idx[s]) : -1;
+  int mine = 0;
+#pragma unroll
+  for (int ee = 0; ee < kExperts; ++ee) {
+    const int c = __popcll(__ballot(e == ee));
+    if (lane == ee) mine = c;
+  }
+  if (lane < kExperts) group_counts[kExperts * g + lane] = mine;
+}
+
 }  // namespace
+
+hipError_t launch_permute_counted(const int32_t* idx, int32_t n_tokens, int32_t* group_counts, int32_t* offsets,
+                                  int32_t* sorted_slots, int32_t* slot_rows, int32_t* counts_out, int capacity,
+                                  hipStream_t s) {
+  if (n_tokens > kMaxGroupPermuteTokens) return hipErrorInvalidValue;
+  const int groups = (n_tokens + 15) / 16;
+  hipLaunchKernelGGL(group_counts_kernel, dim3((groups + kCountWaves - 1) / kCountWaves), dim3(kCountWaves * kWave),
+                     0, s, idx, n_tokens, group_counts);
+  const hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_permute_groups(idx, n_tokens, group_counts, offsets, sorted_slots, slot_rows, counts_out, capacity,
+                               s);
+}
 
 hipError_t launch_permute_groups(const int32_t* idx, int32_t n_tokens, const int32_t* group_counts, int32_t* offsets,
                                  int32_t* sorted_slots, int32_t* slot_rows, int32_t* counts_out, int capacity,

@@ -4,10 +4,12 @@
 #pragma once
 
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace moe {
 
 constexpr int kPermThreads = 1024;
+static_assert(kPermThreads == kPermuteSmallSlots, "the ballot form holds one slot per thread");
 constexpr int kPermWaves = kPermThreads / kWave;
 
 // Ids outside [0, E) are skipped (never used as an index).

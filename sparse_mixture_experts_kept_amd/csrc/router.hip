@@ -178,8 +178,22 @@ __device__ __forceinline__ void store8(T* p, const T* in) {
   }
 }
 
-template <typename T>
-__global__ void __launch_bounds__(256) rmsnorm_route_kernel(float* __restrict__ resid, const T* __restrict__ y_add,
+// The addend of the glue: the layer's output y_add [T, d] (dtype, or none),
+// or (COMBINE) the layer's combine itself, y[t] = g0 * y_rows[slot_rows[2t]]
+// + g1 * y_rows[slot_rows[2t+1]] (each row plus its second partial y_rows2
+// when the down projection split its reduction), computed and rounded to the
+// dtype exactly as combine_kernel does it, so y is never written.
+struct GlueAddend {
+  const void* y_add;
+  const float* y_rows;
+  const float* y_rows2;
+  const int32_t* slot_rows;
+  const float* gates;
+};
+
+// With wg == nullptr the routing is skipped (the glue after the last layer).
+template <typename T, bool COMBINE>
+__global__ void __launch_bounds__(256) rmsnorm_route_kernel(float* __restrict__ resid, GlueAddend add,
                                                             T* __restrict__ u, const T* __restrict__ wg,
                                                             const float* __restrict__ bias,
                                                             int32_t* __restrict__ idx_out, float* __restrict__ w_out,
@@ -187,7 +201,8 @@ __global__ void __launch_bounds__(256) rmsnorm_route_kernel(float* __restrict__ 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* wg_s = reinterpret_cast<T*>(smem_raw);
   float b[kExperts];
-  stage_router(wg, bias, wg_s, d, b);
+  if (wg) stage_router(wg, bias, wg_s, d, b);
+  const T* __restrict__ y_add = static_cast<const T*>(add.y_add);
   constexpr int kVec = 8;                       // elements per lane and step
   constexpr int kSteps = kMaxNormRouteD / (kWave * kVec);
   const int lane = threadIdx.x % kWave;
@@ -196,6 +211,21 @@ __global__ void __launch_bounds__(256) rmsnorm_route_kernel(float* __restrict__ 
   for (int64_t t = static_cast<int64_t>(blockIdx.x) * waves_per_block + threadIdx.x / kWave; t < T_tokens;
        t += n_waves) {
     float* r = resid + t * d;
+    // COMBINE: the token's two rows and gates (a dropped slot, row -1, reads
+    // row 0 and adds nothing, as in combine_kernel)
+    int64_t s0 = 0, s1 = 0;
+    float g0 = 0.0f, g1 = 0.0f;
+    bool k0 = false, k1 = false;
+    if constexpr (COMBINE) {
+      s0 = add.slot_rows[2 * t];
+      s1 = add.slot_rows[2 * t + 1];
+      g0 = add.gates[2 * t];
+      g1 = add.gates[2 * t + 1];
+      k0 = s0 >= 0;
+      k1 = s1 >= 0;
+      s0 = k0 ? s0 : 0;
+      s1 = k1 ? s1 : 0;
+    }
     float v[kSteps][kVec];
     float ss = 0.0f;
 #pragma unroll
@@ -208,11 +238,33 @@ __global__ void __launch_bounds__(256) rmsnorm_route_kernel(float* __restrict__ 
         const float4 r1 = *reinterpret_cast<const float4*>(r + i + 4);
         v[j][0] = r0.x; v[j][1] = r0.y; v[j][2] = r0.z; v[j][3] = r0.w;
         v[j][4] = r1.x; v[j][5] = r1.y; v[j][6] = r1.z; v[j][7] = r1.w;
-        if (y_add) {
+        bool added = false;
+        if constexpr (COMBINE) {
+          float a[kVec], c[kVec];
+          load8(add.y_rows + s0 * d + i, a);
+          load8(add.y_rows + s1 * d + i, c);
+          if (add.y_rows2) {
+            float a2[kVec], c2[kVec];
+            load8(add.y_rows2 + s0 * d + i, a2);
+            load8(add.y_rows2 + s1 * d + i, c2);
+#pragma unroll
+            for (int q = 0; q < kVec; ++q) {
+              a[q] = __fadd_rn(a[q], a2[q]);
+              c[q] = __fadd_rn(c[q], c2[q]);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < kVec; ++q)
+            v[j][q] += to_f32<T>(from_f32<T>(combine_pair(a[q], c[q], g0, g1, k0, k1)));
+          added = true;
+        } else if (y_add) {
           float ya[kVec];
           load8(y_add + t * d + i, ya);
 #pragma unroll
           for (int q = 0; q < kVec; ++q) v[j][q] += ya[q];
+          added = true;
+        }
+        if (added) {
           *reinterpret_cast<float4*>(r + i) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
           *reinterpret_cast<float4*>(r + i + 4) = make_float4(v[j][4], v[j][5], v[j][6], v[j][7]);
         }
@@ -237,43 +289,61 @@ __global__ void __launch_bounds__(256) rmsnorm_route_kernel(float* __restrict__ 
           uf[q] = to_f32<T>(uq[q]);
         }
         store8(u + t * d + i, uq);
+        if (wg) {
 #pragma unroll
-        for (int e = 0; e < kExperts; ++e) {
-          float wf[kVec];
-          load8(wg_s + e * d + i, wf);
+          for (int e = 0; e < kExperts; ++e) {
+            float wf[kVec];
+            load8(wg_s + e * d + i, wf);
 #pragma unroll
-          for (int q = 0; q < kVec; ++q) acc[e] = fmaf(uf[q], wf[q], acc[e]);
+            for (int q = 0; q < kVec; ++q) acc[e] = fmaf(uf[q], wf[q], acc[e]);
+          }
         }
       }
     }
+    if (wg) {
 #pragma unroll
-    for (int e = 0; e < kExperts; ++e) acc[e] = wave_sum(acc[e]) + b[e];
-    if (lane == 0) select_top2(acc, gating, idx_out + kTopK * t, w_out + kTopK * t);
+      for (int e = 0; e < kExperts; ++e) acc[e] = wave_sum(acc[e]) + b[e];
+      if (lane == 0) select_top2(acc, gating, idx_out + kTopK * t, w_out + kTopK * t);
+    }
   }
 }
+
+namespace {
+template <typename T, bool COMBINE>
+hipError_t launch_glue(float* resid, const GlueAddend& add, void* u, const void* wg, const float* bias, int32_t* idx,
+                       float* w, int64_t n_tokens, int d, float eps, int gating, int n_cu, hipStream_t s) {
+  const size_t lds = wg ? kExperts * static_cast<size_t>(d) * sizeof(T) : 0;
+  if (lds > 64 * 1024) {
+    const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&rmsnorm_route_kernel<T, COMBINE>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (err != hipSuccess) return err;
+  }
+  int64_t blocks = (n_tokens + 3) / 4;  // 4 waves, a row each
+  const int64_t cap = static_cast<int64_t>(n_cu) * 2;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL((rmsnorm_route_kernel<T, COMBINE>), dim3(blocks), dim3(256), lds, s, resid, add,
+                     static_cast<T*>(u), static_cast<const T*>(wg), bias, idx, w, n_tokens, d, eps, gating);
+  return hipGetLastError();
+}
+}  // namespace
 
 hipError_t launch_rmsnorm_route(int dtype, float* resid, const void* y_add, void* u, const void* wg,
                                 const float* bias, int32_t* idx, float* w, int64_t T, int d, float eps, int gating,
                                 int n_cu, hipStream_t s) {
-  const size_t lds = kExperts * static_cast<size_t>(d) * (dtype == kDtypeBF16 ? 2 : 4);
-  const void* fn = dtype == kDtypeBF16 ? reinterpret_cast<const void*>(&rmsnorm_route_kernel<bf16_t>)
-                                       : reinterpret_cast<const void*>(&rmsnorm_route_kernel<float>);
-  if (lds > 64 * 1024) {
-    const hipError_t err = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    if (err != hipSuccess) return err;
-  }
-  int64_t blocks = (T + 3) / 4;  // 4 waves, a row each
-  const int64_t cap = static_cast<int64_t>(n_cu) * 2;
-  if (blocks > cap) blocks = cap;
+  const GlueAddend add{y_add, nullptr, nullptr, nullptr, nullptr};
   if (dtype == kDtypeBF16)
-    hipLaunchKernelGGL(rmsnorm_route_kernel<bf16_t>, dim3(blocks), dim3(256), lds, s, resid,
-                       static_cast<const bf16_t*>(y_add), static_cast<bf16_t*>(u), static_cast<const bf16_t*>(wg),
-                       bias, idx, w, T, d, eps, gating);
-  else
-    hipLaunchKernelGGL(rmsnorm_route_kernel<float>, dim3(blocks), dim3(256), lds, s, resid,
-                       static_cast<const float*>(y_add), static_cast<float*>(u), static_cast<const float*>(wg), bias,
-                       idx, w, T, d, eps, gating);
-  return hipGetLastError();
+    return launch_glue<bf16_t, false>(resid, add, u, wg, bias, idx, w, T, d, eps, gating, n_cu, s);
+  return launch_glue<float, false>(resid, add, u, wg, bias, idx, w, T, d, eps, gating, n_cu, s);
+}
+
+hipError_t launch_combine_rmsnorm_route(int dtype, const float* y_rows, const float* y_rows2, const int32_t* slot_rows,
+                                        const float* gates, float* resid, void* u, const void* wg, const float* bias,
+                                        int32_t* idx, float* w, int64_t T, int d, float eps, int gating, int n_cu,
+                                        hipStream_t s) {
+  const GlueAddend add{nullptr, y_rows, y_rows2, slot_rows, gates};
+  if (dtype == kDtypeBF16)
+    return launch_glue<bf16_t, true>(resid, add, u, wg, bias, idx, w, T, d, eps, gating, n_cu, s);
+  return launch_glue<float, true>(resid, add, u, wg, bias, idx, w, T, d, eps, gating, n_cu, s);
 }
 
 // bf16 scores on MFMA: one 16-token group times the 8 router rows (padded to

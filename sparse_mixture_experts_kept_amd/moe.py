@@ -24,7 +24,10 @@ E_EXPERTS, TOP_K = 8, 2
 
 EXPORTED = ("moe_status_string", "moe_version", "moe_router_topk", "moe_permute", "moe_grouped_swiglu",
             "moe_expert_up", "moe_expert_down", "moe_combine", "moe_ffn_forward", "moe_rmsnorm_residual",
-            "moe_load_balance_loss", "moe_ffn_forward_routed", "moe_rmsnorm_residual_route")
+            "moe_load_balance_loss", "moe_ffn_forward_routed", "moe_rmsnorm_residual_route",
+            "moe_ffn_forward_timed", "moe_ffn_forward_routed_residual")
+# Stage boundaries moe_ffn_forward_timed records (8 events delimit these 7 stages).
+STAGES = ("router", "permute", "up_gemm", "up_tails", "down_gemm", "down_tails", "combine")
 
 
 class MoeError(RuntimeError):
@@ -57,7 +60,7 @@ def load_library(path: str = LIB_PATH):
         "moe_status_string": (ctypes.c_char_p, [I32]),
         "moe_version": (ctypes.c_char_p, []),
         "moe_router_topk": (I32, [D, P, P, P, P, P, P, P]),
-        "moe_permute": (I32, [D, P, P, P, P, P]),
+        "moe_permute": (I32, [D, P, P, P, P, P, SZ, P]),
         "moe_grouped_swiglu": (I32, [D, P, P, P, P, P, P, P, P, P]),
         "moe_expert_up": (I32, [D, P, P, P, P, P, P, P]),
         "moe_expert_down": (I32, [D, P, P, P, P, P]),
@@ -67,6 +70,8 @@ def load_library(path: str = LIB_PATH):
         "moe_load_balance_loss": (I32, [D, P, P, P, P]),
         "moe_ffn_forward_routed": (I32, [D, P, P, P, P, P, P, P, P, P, SZ, P]),
         "moe_rmsnorm_residual_route": (I32, [D, P, P, P, F32, P, P, P, P, P]),
+        "moe_ffn_forward_timed": (I32, [D, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P, P]),
+        "moe_ffn_forward_routed_residual": (I32, [D, P, P, P, P, P, P, P, P, F32, P, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -141,7 +146,7 @@ def router_topk(x, w_gate, logit_bias=None, return_logits=False, gating=GATING_P
     return (idx, w, logits) if return_logits else (idx, w)
 
 
-def permute(topk_idx, d=128, f=128, capacity=0):
+def permute(topk_idx, d=128, f=128, capacity=0, workspace=None):
     """expert_offsets [9], sorted_slots [T*2], slot_rows [T*2] (int32; -1 for
     a slot dropped by the expert capacity)."""
     lib = load_library()
@@ -150,9 +155,21 @@ def permute(topk_idx, d=128, f=128, capacity=0):
     offs = torch.zeros((E_EXPERTS + 1,), dtype=torch.int32, device=topk_idx.device)
     sorted_slots = torch.empty((T * TOP_K,), dtype=torch.int32, device=topk_idx.device)
     slot_rows = torch.empty((T * TOP_K,), dtype=torch.int32, device=topk_idx.device)
+    if workspace is None:
+        workspace = torch.empty((permute_workspace_size(T, capacity),), dtype=torch.uint8, device=topk_idx.device)
+    n = ctypes.c_size_t(workspace.numel())
     _check("moe_permute", lib.moe_permute(ctypes.byref(dims), ptr(topk_idx), ptr(offs), ptr(sorted_slots),
-                                          ptr(slot_rows), stream_handle()))
+                                          ptr(slot_rows), ptr(workspace), ctypes.byref(n), stream_handle()))
     return offs, sorted_slots, slot_rows
+
+
+def permute_workspace_size(T, capacity=0) -> int:
+    """Bytes of the workspace moe_permute needs for T tokens."""
+    lib = load_library()
+    dims = make_dims(T, 128, 128, MOE_BF16, capacity=capacity)
+    n = ctypes.c_size_t(0)
+    _check("moe_permute", lib.moe_permute(ctypes.byref(dims), None, None, None, None, None, ctypes.byref(n), None))
+    return n.value
 
 
 def grouped_swiglu(x, expert_offsets, sorted_slots, w1, w3, w2, variant=VARIANT_AUTO):
@@ -252,6 +269,21 @@ class FFN:
             ptr(self.idx), ptr(self.w), ptr(self.counts), ptr(self.ws), ctypes.byref(self.ws_bytes), s))
         return self.y
 
+    def timed(self, events, up_gemm_clock=None, stream=None):
+        """The same call through moe_ffn_forward_timed: ``events`` are 8
+        recorded-once torch.cuda.Event(enable_timing=True), re-recorded on
+        the layer's stream at the boundaries of STAGES; ``up_gemm_clock``
+        (int64 [4 * workgroups] or None) receives the clock samples of the
+        prefill up GEMM."""
+        x, w_gate, bias, w1, w3, w2 = self.args
+        s = ctypes.c_void_p(stream) if stream is not None else stream_handle()
+        handles = (ctypes.c_void_p * 8)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        _check("moe_ffn_forward_timed", self.lib.moe_ffn_forward_timed(
+            ctypes.byref(self.dims), ptr(x), ptr(w_gate), ptr(bias), ptr(w1), ptr(w3), ptr(w2), ptr(self.y),
+            ptr(self.idx), ptr(self.w), ptr(self.counts), ptr(self.ws), ctypes.byref(self.ws_bytes), s,
+            handles, ptr(up_gemm_clock)))
+        return self.y
+
 
 def ffn_forward(x, w_gate, w1, w3, w2, logit_bias=None, variant=VARIANT_AUTO, return_routing=False,
                 gating=GATING_PAIR, capacity=0):
@@ -300,6 +332,31 @@ class RoutedFFN:
             ctypes.byref(self.dims), ptr(x), ptr(topk_idx), ptr(topk_w), ptr(w1), ptr(w3), ptr(w2), ptr(self.y),
             ptr(self.counts), ptr(self.ws), ctypes.byref(self.ws_bytes), stream_handle()))
         return self.y
+
+
+class RoutedResidualFFN:
+    """One stacked block's MoE half with the combine fused into the glue
+    (moe_ffn_forward_routed_residual): resid += MoE(x) under the given
+    routing, u = RMSNorm(resid), and the next layer's routing, with
+    preallocated workspace."""
+
+    def __init__(self, x, w1, w3, w2, variant=VARIANT_AUTO, workspace=None, counts=None, capacity=0, eps=1e-5):
+        self.lib = load_library()
+        self.dims = _layer_dims(x, w1, variant, capacity=capacity)
+        T, d = x.shape
+        self.args = (x, w1, w3, w2)
+        self.counts, self.eps = counts, eps
+        self.ws = workspace if workspace is not None else alloc_workspace(T, d, w1.shape[1], x.dtype, variant,
+                                                                          x.device)
+        self.ws_bytes = ctypes.c_size_t(self.ws.numel())
+
+    def __call__(self, topk_idx, topk_w, resid, u_out, w_gate_next=None, logit_bias_next=None, idx_next=None,
+                 w_next=None):
+        x, w1, w3, w2 = self.args
+        _check("moe_ffn_forward_routed_residual", self.lib.moe_ffn_forward_routed_residual(
+            ctypes.byref(self.dims), ptr(x), ptr(topk_idx), ptr(topk_w), ptr(w1), ptr(w3), ptr(w2), ptr(resid),
+            ptr(u_out), self.eps, ptr(w_gate_next), ptr(logit_bias_next), ptr(idx_next), ptr(w_next),
+            ptr(self.counts), ptr(self.ws), ctypes.byref(self.ws_bytes), stream_handle()))
 
 
 def load_balance_loss(logits, topk_idx):

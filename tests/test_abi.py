@@ -78,7 +78,7 @@ def test_bad_dims_are_rejected(kw, status):
     dims = _dims(**kw)
     n = ctypes.c_size_t(0)
     assert lib.moe_router_topk(ctypes.byref(dims), FAKE, FAKE, None, FAKE, FAKE, None, None) == status
-    assert lib.moe_permute(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, None) == status
+    assert lib.moe_permute(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(n), None) == status
     assert lib.moe_grouped_swiglu(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
     assert lib.moe_combine(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, None) == status
     assert lib.moe_ffn_forward(ctypes.byref(dims), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, None,
@@ -107,8 +107,11 @@ def test_null_and_misaligned_pointers():
     assert lib.moe_router_topk(None, FAKE, FAKE, None, FAKE, FAKE, None, None) == INV
     assert lib.moe_router_topk(ctypes.byref(dims), None, FAKE, None, FAKE, FAKE, None, None) == INV
     assert lib.moe_router_topk(ctypes.byref(dims), MISALIGNED, FAKE, None, FAKE, FAKE, None, None) == INV
-    assert lib.moe_permute(ctypes.byref(dims), FAKE, None, FAKE, FAKE, None) == INV
-    assert lib.moe_permute(ctypes.byref(dims), FAKE, FAKE, MISALIGNED, FAKE, None) == INV
+    big = ctypes.c_size_t(1 << 20)
+    assert lib.moe_permute(ctypes.byref(dims), FAKE, None, FAKE, FAKE, FAKE, ctypes.byref(big), None) == INV
+    assert lib.moe_permute(ctypes.byref(dims), FAKE, FAKE, MISALIGNED, FAKE, FAKE, ctypes.byref(big), None) == INV
+    assert lib.moe_permute(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, MISALIGNED, ctypes.byref(big), None) == INV
+    assert lib.moe_permute(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == INV
     assert lib.moe_grouped_swiglu(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None) == INV
     assert lib.moe_grouped_swiglu(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, MISALIGNED, FAKE,
                                   None) == INV
@@ -163,7 +166,8 @@ def test_zero_tokens_is_a_no_op():
     dims = _dims(T=0)
     n = ctypes.c_size_t(0)
     assert lib.moe_router_topk(ctypes.byref(dims), None, None, None, None, None, None, None) == moe.MOE_OK
-    assert lib.moe_permute(ctypes.byref(dims), None, None, None, None, None) == moe.MOE_OK
+    assert lib.moe_permute(ctypes.byref(dims), None, None, None, None, None, ctypes.byref(n), None) == moe.MOE_OK
+    assert lib.moe_permute(ctypes.byref(dims), None, None, None, None, FAKE, ctypes.byref(n), None) == moe.MOE_OK
     assert lib.moe_grouped_swiglu(ctypes.byref(dims), None, None, None, None, None, None, None, None, None) == \
         moe.MOE_OK
     assert lib.moe_combine(ctypes.byref(dims), None, None, None, None, None) == moe.MOE_OK
@@ -212,3 +216,53 @@ def test_routed_and_fused_glue_validation():
 def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         moe.ptr(torch.zeros(4))
+
+
+@needs_no_gpu
+def test_permute_workspace_query():
+    # per-group counts (ceil(T/16) x 8 int32) between 512 and 65536 tokens, a minimal 256 bytes otherwise
+    lib = _lib()
+    for T, need in ((16, 256), (512, 256), (513, 33 * 8 * 4 + (256 - 33 * 8 * 4 % 256) % 256), (4096, 8192),
+                    (65536, 131072), (65537, 256)):
+        dims = _dims(T=T)
+        n = ctypes.c_size_t(0)
+        assert lib.moe_permute(ctypes.byref(dims), None, None, None, None, None, ctypes.byref(n), None) == moe.MOE_OK
+        assert n.value == need, (T, n.value)
+    dims = _dims(T=4096)
+    small = ctypes.c_size_t(8191)
+    assert lib.moe_permute(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(small), None) == \
+        moe.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
+@needs_no_gpu
+def test_timed_and_residual_entry_points_validate():
+    lib = _lib()
+    dims = _dims()
+    n = ctypes.c_size_t(1 << 30)
+    INV = moe.MOE_ERR_INVALID_ARGUMENT
+    ws = ctypes.c_void_p(0x200000)
+    events = (ctypes.c_void_p * 8)(*([FAKE] * 8))
+    holes = (ctypes.c_void_p * 8)(*([FAKE] * 7 + [None]))
+    args = (FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None, None, ws, ctypes.byref(n), None)
+    assert lib.moe_ffn_forward_timed(ctypes.byref(dims), *args, None, None) == INV  # no events
+    assert lib.moe_ffn_forward_timed(ctypes.byref(dims), *args, holes, None) == INV  # a NULL event
+    assert lib.moe_ffn_forward_timed(ctypes.byref(dims), *args, events, MISALIGNED) == INV
+    # the fused glue: resid, u_out and (with a next router) its outputs are required
+    r = (FAKE, FAKE, FAKE, FAKE, FAKE)  # x, idx, w, w1, w3
+    assert lib.moe_ffn_forward_routed_residual(ctypes.byref(dims), *r, FAKE, None, FAKE, 1e-5, None, None, None,
+                                               None, None, ws, ctypes.byref(n), None) == INV
+    assert lib.moe_ffn_forward_routed_residual(ctypes.byref(dims), *r, FAKE, FAKE, FAKE, 1e-5, FAKE, None, None,
+                                               FAKE, None, ws, ctypes.byref(n), None) == INV
+    assert lib.moe_ffn_forward_routed_residual(ctypes.byref(dims), *r, FAKE, FAKE, MISALIGNED, 1e-5, None, None,
+                                               None, None, None, ws, ctypes.byref(n), None) == INV
+    big_d = _dims(d=8192 + 128)
+    assert lib.moe_ffn_forward_routed_residual(ctypes.byref(big_d), *r, FAKE, FAKE, FAKE, 1e-5, None, None, None,
+                                               None, None, ws, ctypes.byref(n), None) == moe.MOE_ERR_UNSUPPORTED
+    # size query, as moe_ffn_forward
+    q = ctypes.c_size_t(0)
+    q2 = ctypes.c_size_t(0)
+    assert lib.moe_ffn_forward_routed_residual(ctypes.byref(dims), None, None, None, None, None, None, None, None,
+                                               1e-5, None, None, None, None, None, None, ctypes.byref(q), None) == 0
+    assert lib.moe_ffn_forward(ctypes.byref(dims), None, None, None, None, None, None, None, None, None, None,
+                               None, ctypes.byref(q2), None) == 0
+    assert q.value == q2.value > 0

@@ -332,7 +332,10 @@ def test_router_exact_ties_go_to_lower_index():
 
 
 def test_permute_matches_oracle_bit_exact():
-    for T, bias in ((4096, None), (8192, [3.0, 0, 0, 0, 0, 0, 0, -3.0]), (1, None), (1000, [50.0, 40, 0, 0, 0, 0, 0, 0])):
+    # T <= 512: one workgroup (ballot form); up to 65536: per-group counts and
+    # one wave per 16-token group; beyond: one workgroup over chunks
+    for T, bias in ((4096, None), (8192, [3.0, 0, 0, 0, 0, 0, 0, -3.0]), (1, None), (1000, [50.0, 40, 0, 0, 0, 0, 0, 0]),
+                    (513, None), (65536, None), (70000, [0, 0, 2.0, 0, 0, 0, 0, 0])):
         g = torch.Generator().manual_seed(T)
         logits = torch.randn((T, 8), generator=g)
         if bias is not None:
@@ -804,12 +807,14 @@ def _check_stack_layer(stack, layer_idx, u, y, idx, sample):
     assert np.abs(yg - ref["y"]).max() <= _tol("bf16", ref["y"])
 
 
-@pytest.mark.parametrize("fused", [True, False])
-def test_stack_small_every_layer(fused):
-    # fused: the glue after each layer computes the next layer's routing
+@pytest.mark.parametrize("mode", ["combine", "router", "none"])
+def test_stack_small_every_layer(mode):
+    # combine: each layer's combine adds into the residual and the same launch
+    # routes the next layer; router: the glue after each layer computes the
+    # next layer's routing; none: every step its own launch
     from sparse_mixture_experts_kept_amd.stack import MoEStack
     T, d, f, L = 300, 256, 512, 4
-    stack = MoEStack(T, d, f, L, seed=31, fused=fused)
+    stack = MoEStack(T, d, f, L, seed=31, mode=mode)
     g = torch.Generator(device="cuda").manual_seed(32)
     x0 = torch.randn((T, d), generator=g, device="cuda", dtype=torch.float32)
     stack.load_input(x0)
@@ -827,6 +832,32 @@ def test_stack_small_every_layer(fused):
         _check_stack_layer(stack, layer, u, y, idx, np.arange(T))
         np.testing.assert_array_equal(stack.hist[layer].cpu().numpy(),
                                       np.bincount(idx.cpu().numpy().reshape(-1), minlength=8))
+
+
+@pytest.mark.parametrize("T,d,f,L", [(300, 256, 512, 4), (40, 256, 512, 3), (2100, 4096, 512, 2)])
+def test_stack_combine_fused_into_glue_is_bit_identical(T, d, f, L):
+    """The combine fused into the glue (moe_ffn_forward_routed_residual)
+    against the layer writing y and the glue adding it: the same residual
+    stream bit for bit after every layer, the same routing and histograms.
+    T=40 runs the decode kernels, T=2100 at d=4096 the prefill kernels with
+    streamed expert tails and their split fixup."""
+    from sparse_mixture_experts_kept_amd.stack import MoEStack
+    stacks = {m: MoEStack(T, d, f, L, seed=33, mode=m) for m in ("combine", "router")}
+    g = torch.Generator(device="cuda").manual_seed(34)
+    x0 = torch.randn((T, d), generator=g, device="cuda", dtype=torch.float32)
+    outs = {}
+    for m, st in stacks.items():
+        st.load_input(x0)
+        outs[m] = st.forward(capture=tuple(range(L)))
+    torch.cuda.synchronize()
+    a, b = stacks["combine"], stacks["router"]
+    assert torch.equal(a.resid, b.resid)
+    assert torch.equal(a.hist, b.hist)
+    for layer in range(L):
+        assert torch.equal(outs["combine"][layer][0], outs["router"][layer][0])  # u_l
+        assert torch.equal(outs["combine"][layer][2], outs["router"][layer][2])  # routing of layer l
+    # the last glue is a different kernel in the two modes (no router after it): u within one bf16 rounding
+    assert (a.u.float() - b.u.float()).abs().max().item() <= 2 ** -7 * b.u.float().abs().max().item()
 
 
 class _StackLayers:
@@ -861,6 +892,7 @@ class _StackLayers:
         self.prop = O._f64(x0.index_select(0, rows).cpu())  # oracle-propagated residual
         self.done = 0
         self.results = {}
+        self.u_drift = []  # per layer: max |u_l(GPU) - RMSNorm(oracle residual)| / max |.|
         del stack
 
     def run_until(self, upto):
@@ -886,7 +918,9 @@ class _StackLayers:
             self.results[l] = dict(ids_ok=ids_ok, valid=valid, err=err, tol=_tol("bf16", ref["y"]),
                                    near_ties=int((~clear).sum()))
             # the oracle's own pass of the sampled tokens through layer l
-            self.prop = self.prop + O.moe_ffn(O.rmsnorm(self.prop), wg, None, None, None, widen_expert=widen)["y"]
+            u_o = O.rmsnorm(self.prop)
+            self.u_drift.append(float(np.abs(O._f64(u) - u_o).max() / np.abs(u_o).max()))
+            self.prop = self.prop + O.moe_ffn(u_o, wg, None, None, None, widen_expert=widen)["y"]
             cache.clear()
         self.done = max(self.done, upto)
 
@@ -919,7 +953,8 @@ def test_stack_workload_every_layer(stack_layers, first):
         # 32-layer pass (reported, not gated: the GPU rounds u and y to bf16
         # at every layer)
         drift = np.abs(s.resid_final - s.prop).max() / np.abs(s.prop).max()
-        print(f"stack residual drift after {s.L} layers: {drift:.3e} (relative to max |x_L|)")
+        print(f"stack residual drift after {s.L} layers: {drift:.3e} (relative to max |x_L|); "
+              f"layer inputs u_l: {' '.join(f'{v:.1e}' for v in s.u_drift)}")
         assert np.isfinite(drift)
         _STACK.clear()
         torch.cuda.empty_cache()
