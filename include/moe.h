@@ -244,6 +244,27 @@ moe_status moe_ffn_forward_routed(const moe_dims* dims, const void* x, const int
                                   size_t* workspace_bytes, void* stream);
 
 /*
+ * moe_ffn_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the workspace is a fixed device array
+ * inside the library, 32 MiB (33554432 bytes) per GPU, held from the first
+ * call on that GPU until the process ends.  The call allocates nothing.
+ *   Arguments, outputs and errors as moe_ffn_forward; a layer whose
+ *   workspace (moe_ffn_forward's size query) exceeds 32 MiB is rejected with
+ *   MOE_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (at d = 4096,
+ *   f = 14336: up to 272 tokens on the prefill kernels, 64 on the decode
+ *   kernels).  All calls on one GPU share its array and it keeps the last
+ *   call's contents (the layer writes every region before reading it, so
+ *   nothing needs clearing): calls that overlap on one GPU -- on different
+ *   streams or from different threads without ordering -- race and give
+ *   undefined results.  Calls on one stream are ordered and safe.
+ */
+moe_status moe_ffn_forward_noalloc(const moe_dims* dims, const void* x, const void* w_gate,
+                                   const float* logit_bias, const void* w1, const void* w3,
+                                   const void* w2, void* y, int32_t* topk_idx_out, float* topk_w_out,
+                                   int32_t* expert_counts_out, void* stream);
+
+/*
  * One stacked block's MoE half with the combine fused into the glue that
  * follows it: moe_ffn_forward_routed on x (the layer's input u_l) and its
  * routing, except that the gate-weighted pair of each token's expert rows is

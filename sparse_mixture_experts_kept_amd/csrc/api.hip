@@ -343,6 +343,31 @@ moe_status moe_combine(const moe_dims* dims, const float* y_rows, const int32_t*
 
 namespace {
 
+// Allocation-free form of moe_ffn_forward: its workspace is this file-scope
+// device array (one copy per GPU, held until the process ends).  In host
+// code `scratch` only names the symbol; its device address on the current
+// GPU comes from hipGetSymbolAddress, looked up once per device on the
+// first call there and kept in g_scratch.  The layer's kernels need nothing
+// in it zeroed: every region is written before it is read within a call.
+constexpr size_t kNoAllocScratchBytes = size_t{32} << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+void* g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+moe_status scratch_on_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
+}
+
 // The glue that takes the place of the combine in
 // moe_ffn_forward_routed_residual (null: the combine writes y).
 struct ResidualGlue {
@@ -374,7 +399,8 @@ moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_g
                             const int32_t* routed_idx, const float* routed_w, const void* w1, const void* w3,
                             const void* w2, void* y, int32_t* topk_idx_out, float* topk_w_out,
                             int32_t* expert_counts_out, void* workspace, size_t* workspace_bytes, void* stream,
-                            const StageMarks* marks = nullptr, const ResidualGlue* glue = nullptr) {
+                            bool use_scratch = false, const StageMarks* marks = nullptr,
+                            const ResidualGlue* glue = nullptr) {
   const bool routed = routed_idx != nullptr;
   moe_status st = check_dims(dims);
   if (st != MOE_OK) return st;
@@ -382,15 +408,18 @@ moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_g
   if (!routed && static_cast<size_t>(dims->E) * dims->d * elem_size(dims->dtype) > kRouterLdsLimit)
     return MOE_ERR_UNSUPPORTED;
   const Workspace plan = plan_workspace(dims);
-  if (!workspace) {
+  // The allocation-free form's workspace is the device array `scratch`,
+  // looked up below once the arguments have been checked.
+  if (use_scratch && plan.total > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!use_scratch && !workspace) {
     *workspace_bytes = plan.total;
     return MOE_OK;
   }
   if (dims->T == 0) return MOE_OK;
-  if (*workspace_bytes < plan.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!use_scratch && *workspace_bytes < plan.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (!x || (!routed && !w_gate) || (routed && !routed_w) || !w1 || !w3 || !w2 || (!glue && !y))
     return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned(workspace, 256) || !aligned(x, 16) || (w_gate && !aligned(w_gate, 16)) ||
+  if ((!use_scratch && !aligned(workspace, 256)) || !aligned(x, 16) || (w_gate && !aligned(w_gate, 16)) ||
       !aligned(w1, 16) || !aligned(w3, 16) || !aligned(w2, 16) || (y && !aligned(y, 16)) ||
       (logit_bias && !aligned(logit_bias, 16)) ||
       (topk_idx_out && !aligned(topk_idx_out, 8)) || (topk_w_out && !aligned(topk_w_out, 8)) ||
@@ -398,6 +427,10 @@ moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_g
       (expert_counts_out && !aligned(expert_counts_out, 4)))
     return MOE_ERR_INVALID_ARGUMENT;
 
+  if (use_scratch) {
+    st = scratch_on_device(&workspace);
+    if (st != MOE_OK) return st;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
   int32_t* idx = topk_idx_out ? topk_idx_out : reinterpret_cast<int32_t*>(ws + plan.idx);
@@ -495,6 +528,14 @@ moe_status moe_ffn_forward(const moe_dims* dims, const void* x, const void* w_ga
                           expert_counts_out, workspace, workspace_bytes, stream);
 }
 
+moe_status moe_ffn_forward_noalloc(const moe_dims* dims, const void* x, const void* w_gate, const float* logit_bias,
+                                   const void* w1, const void* w3, const void* w2, void* y, int32_t* topk_idx_out,
+                                   float* topk_w_out, int32_t* expert_counts_out, void* stream) {
+  size_t bytes = kNoAllocScratchBytes;
+  return ffn_forward_impl(dims, x, w_gate, logit_bias, nullptr, nullptr, w1, w3, w2, y, topk_idx_out, topk_w_out,
+                          expert_counts_out, nullptr, &bytes, stream, /*use_scratch=*/true);
+}
+
 moe_status moe_ffn_forward_timed(const moe_dims* dims, const void* x, const void* w_gate, const float* logit_bias,
                                  const void* w1, const void* w3, const void* w2, void* y, int32_t* topk_idx_out,
                                  float* topk_w_out, int32_t* expert_counts_out, void* workspace,
@@ -508,7 +549,7 @@ moe_status moe_ffn_forward_timed(const moe_dims* dims, const void* x, const void
   marks.ev = stage_events;
   marks.clk = reinterpret_cast<long long*>(up_gemm_clock);
   return ffn_forward_impl(dims, x, w_gate, logit_bias, nullptr, nullptr, w1, w3, w2, y, topk_idx_out, topk_w_out,
-                          expert_counts_out, workspace, workspace_bytes, stream, &marks);
+                          expert_counts_out, workspace, workspace_bytes, stream, false, &marks);
 }
 
 moe_status moe_ffn_forward_routed(const moe_dims* dims, const void* x, const int32_t* topk_idx, const float* topk_w,
@@ -540,7 +581,7 @@ moe_status moe_ffn_forward_routed_residual(const moe_dims* dims, const void* x, 
   }
   const ResidualGlue glue{resid, u_out, eps, w_gate_next, logit_bias_next, topk_idx_next, topk_w_next};
   return ffn_forward_impl(dims, x, nullptr, nullptr, topk_idx, topk_w, w1, w3, w2, nullptr, nullptr, nullptr,
-                          expert_counts_out, workspace, workspace_bytes, stream, nullptr, &glue);
+                          expert_counts_out, workspace, workspace_bytes, stream, false, nullptr, &glue);
 }
 
 moe_status moe_rmsnorm_residual_route(const moe_dims* dims, float* resid, const void* y_add, void* u_out, float eps,

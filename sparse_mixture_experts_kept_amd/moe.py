@@ -25,7 +25,7 @@ E_EXPERTS, TOP_K = 8, 2
 EXPORTED = ("moe_status_string", "moe_version", "moe_router_topk", "moe_permute", "moe_grouped_swiglu",
             "moe_expert_up", "moe_expert_down", "moe_combine", "moe_ffn_forward", "moe_rmsnorm_residual",
             "moe_load_balance_loss", "moe_ffn_forward_routed", "moe_rmsnorm_residual_route",
-            "moe_ffn_forward_timed", "moe_ffn_forward_routed_residual")
+            "moe_ffn_forward_timed", "moe_ffn_forward_routed_residual", "moe_ffn_forward_noalloc")
 # Stage boundaries moe_ffn_forward_timed records (8 events delimit these 7 stages).
 STAGES = ("router", "permute", "up_gemm", "up_tails", "down_gemm", "down_tails", "combine")
 
@@ -72,6 +72,7 @@ def load_library(path: str = LIB_PATH):
         "moe_rmsnorm_residual_route": (I32, [D, P, P, P, F32, P, P, P, P, P]),
         "moe_ffn_forward_timed": (I32, [D, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P, P]),
         "moe_ffn_forward_routed_residual": (I32, [D, P, P, P, P, P, P, P, P, F32, P, P, P, P, P, P, SZ, P]),
+        "moe_ffn_forward_noalloc": (I32, [D, P, P, P, P, P, P, P, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

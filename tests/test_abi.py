@@ -266,3 +266,16 @@ def test_timed_and_residual_entry_points_validate():
     assert lib.moe_ffn_forward(ctypes.byref(dims), None, None, None, None, None, None, None, None, None, None,
                                None, ctypes.byref(q2), None) == 0
     assert q.value == q2.value > 0
+
+
+@needs_no_gpu
+def test_noalloc_rejects_a_layer_beyond_its_array():
+    # the workspace of 400 Mixtral-sized tokens on the prefill kernels exceeds the 32 MiB array:
+    # rejected on the host before anything else happens (no device is needed to see it)
+    lib = _lib()
+    dims = moe.make_dims(400, 4096, 14336, moe.MOE_BF16)
+    assert lib.moe_ffn_forward_noalloc(ctypes.byref(dims), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None,
+                                       None, None) == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+    bad = moe.make_dims(16, 4096, 14336, moe.MOE_BF16, E=4)
+    assert lib.moe_ffn_forward_noalloc(ctypes.byref(bad), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None,
+                                       None, None) == moe.MOE_ERR_UNSUPPORTED
