@@ -231,6 +231,22 @@ moe_status moe_ffn_forward_timed(const moe_dims* dims, const void* x, const void
                                  void* stream, void* const* stage_events, int64_t* up_gemm_clock);
 
 /*
+ * Measurement: the bf16 matrix-core ceiling of this GPU under its power
+ * limit.  Runs the prefill GEMM's MFMA pattern alone (each wave issues the
+ * 64 v_mfma_f32_16x16x32_bf16 of its 128 x 128 tile per 32-deep step,
+ * `iters` times, on distinct fragments of the caller's data; one wave per
+ * SIMD on G workgroups, G = the CU count rounded down to a multiple of 8)
+ * and stores per workgroup b the shader clock counter and the constant
+ * 100 MHz reference counter at the loop's start and end in
+ * clock_out[4b .. 4b+3].  Flops = G * 4 * 64 * iters * 16384.
+ *   operands: 32768 bf16 in device memory (64 fragments of 64 lanes x 8),
+ *   16-byte aligned; sink: G * 256 fp32 (written, keeps the work live).
+ *   NULL pointer, misalignment or iters < 1 -> MOE_ERR_INVALID_ARGUMENT.
+ */
+moe_status moe_mfma_ceiling(const void* operands, int64_t* clock_out, float* sink, int32_t iters,
+                            void* stream);
+
+/*
  * The whole layer from a routing computed elsewhere (by
  * moe_rmsnorm_residual_route, or any top-2 pairs and gates): permutation,
  * both expert projections and the combine, as moe_ffn_forward without its

@@ -604,6 +604,17 @@ moe_status moe_rmsnorm_residual_route(const moe_dims* dims, float* resid, const 
                                               static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_mfma_ceiling(const void* operands, int64_t* clock_out, float* sink, int32_t iters, void* stream) {
+  if (!operands || !clock_out || !sink || iters < 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(operands, 16) || !aligned(clock_out, 8) || !aligned(sink, 4)) return MOE_ERR_INVALID_ARGUMENT;
+  int n_cu = 0;
+  const moe_status st = cu_count(&n_cu);
+  if (st != MOE_OK) return st;
+  return hip_status(moe::launch_mfma_ceiling(static_cast<const bf16_t*>(operands),
+                                             reinterpret_cast<long long*>(clock_out), sink, iters, n_cu,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_load_balance_loss(const moe_dims* dims, const float* logits, const int32_t* topk_idx, float* loss,
                                  void* stream) {
   moe_status st = check_dims(dims);

@@ -131,6 +131,11 @@ hipError_t launch_route_permute(int dtype, const void* x, const void* wg, const 
 hipError_t launch_combine(int dtype, const float* y_rows, const float* y_rows2, const int32_t* slot_rows,
                           const float* topk_w, void* y, int64_t T, int d, int n_cu, hipStream_t s);
 
+// The bf16 MFMA ceiling probe: operands [64 x 64] bf16x8 (64 KiB), clk
+// [4 * prefill_grid(n_cu)] int64, sink [prefill_grid(n_cu) * 256] fp32.
+hipError_t launch_mfma_ceiling(const bf16_t* operands, long long* clk, float* sink, int iters, int n_cu,
+                               hipStream_t s);
+
 hipError_t launch_rmsnorm_residual(int dtype, float* resid, const void* y_add, void* u, int64_t T, int d, float eps,
                                    hipStream_t s);
 // The same glue with the next layer's router fused in (idx [T, 2], w [T, 2]);

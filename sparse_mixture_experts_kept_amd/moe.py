@@ -25,7 +25,8 @@ E_EXPERTS, TOP_K = 8, 2
 EXPORTED = ("moe_status_string", "moe_version", "moe_router_topk", "moe_permute", "moe_grouped_swiglu",
             "moe_expert_up", "moe_expert_down", "moe_combine", "moe_ffn_forward", "moe_rmsnorm_residual",
             "moe_load_balance_loss", "moe_ffn_forward_routed", "moe_rmsnorm_residual_route",
-            "moe_ffn_forward_timed", "moe_ffn_forward_routed_residual", "moe_ffn_forward_noalloc")
+            "moe_ffn_forward_timed", "moe_ffn_forward_routed_residual", "moe_ffn_forward_noalloc",
+            "moe_mfma_ceiling")
 # Stage boundaries moe_ffn_forward_timed records (8 events delimit these 7 stages).
 STAGES = ("router", "permute", "up_gemm", "up_tails", "down_gemm", "down_tails", "combine")
 
@@ -73,6 +74,7 @@ def load_library(path: str = LIB_PATH):
         "moe_ffn_forward_timed": (I32, [D, P, P, P, P, P, P, P, P, P, P, P, SZ, P, P, P]),
         "moe_ffn_forward_routed_residual": (I32, [D, P, P, P, P, P, P, P, P, F32, P, P, P, P, P, P, SZ, P]),
         "moe_ffn_forward_noalloc": (I32, [D, P, P, P, P, P, P, P, P, P, P, P]),
+        "moe_mfma_ceiling": (I32, [P, P, P, I32, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -125,6 +127,76 @@ def stream_handle():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+# --------------------------------------------------------------------------- debug bounds checks
+#
+# The library validates every argument it can see on the host, but the
+# permutation arrays a caller hands to moe_grouped_swiglu / moe_expert_up /
+# moe_expert_down / moe_combine live in device memory and are dereferenced by
+# the kernels unchecked (checking them would need a synchronisation).  With
+# MOE_DEBUG_BOUNDS=1 in the environment, this binding copies them to the host
+# and checks them before each such launch, turning an out-of-bounds index
+# into a Python exception instead of a GPU memory fault.
+
+DEBUG_BOUNDS = os.environ.get("MOE_DEBUG_BOUNDS", "0") not in ("", "0")
+
+
+class MoeIndexError(ValueError):
+    """Routing or permutation arrays that would make a kernel index out of bounds."""
+
+
+def check_routing(topk_idx, T=None):
+    """Host-side check that a routing is a top-2 routing: [T, 2] expert ids
+    in [0, E), the two of a token distinct.  (Not a memory-safety check: the
+    library gives an id outside [0, E) no row, so such ids are safe.)"""
+    idx = topk_idx.detach().cpu().to(torch.int64)
+    if idx.dim() != 2 or idx.shape[1] != TOP_K or (T is not None and idx.shape[0] != T):
+        raise MoeIndexError(f"topk_idx has shape {tuple(idx.shape)}, expected [{T}, {TOP_K}]")
+    if idx.numel() and (idx.min() < 0 or idx.max() >= E_EXPERTS):
+        raise MoeIndexError("expert id outside [0, 8)")
+    if idx.numel() and (idx[:, 0] == idx[:, 1]).any():
+        raise MoeIndexError("a token holds the same expert twice")
+
+
+def check_permutation(expert_offsets, sorted_slots, slot_rows=None, T=None, capacity=0):
+    """Host-side check of an expert-major permutation before kernels index
+    memory through it: offsets [E+1] start at 0, never decrease and end at
+    most at T*k (at most `capacity` rows per expert when one is set); the
+    first offsets[E] sorted slots are distinct slot ids in [0, T*k), each
+    expert's in increasing order; slot_rows (if given) is -1 or the inverse
+    position, and every placed slot has its row.  Raises MoeIndexError."""
+    offs = expert_offsets.detach().cpu().to(torch.int64)
+    ss = sorted_slots.detach().cpu().to(torch.int64)
+    n_slots = ss.numel() if T is None else int(T) * TOP_K
+    if offs.numel() != E_EXPERTS + 1:
+        raise MoeIndexError(f"expert_offsets has {offs.numel()} entries, expected {E_EXPERTS + 1}")
+    if int(offs[0]) != 0 or (offs[1:] < offs[:-1]).any() or int(offs[-1]) > n_slots or int(offs[-1]) > ss.numel():
+        raise MoeIndexError(f"expert_offsets not a prefix sum within [0, {n_slots}]: {offs.tolist()}")
+    if capacity > 0 and (offs[1:] - offs[:-1] > capacity).any():
+        raise MoeIndexError("an expert holds more rows than its capacity")
+    n = int(offs[-1])
+    used = ss[:n]
+    if n and (used.min() < 0 or used.max() >= n_slots):
+        raise MoeIndexError("sorted slot id outside [0, T*k)")
+    if torch.unique(used).numel() != n:
+        raise MoeIndexError("a slot is placed twice")
+    for e in range(E_EXPERTS):
+        seg = used[int(offs[e]):int(offs[e + 1])]
+        if seg.numel() > 1 and (seg[1:] <= seg[:-1]).any():
+            raise MoeIndexError(f"expert {e}'s slots are not in increasing order")
+    if slot_rows is not None:
+        rows = slot_rows.detach().cpu().to(torch.int64)
+        if rows.numel() != n_slots:
+            raise MoeIndexError(f"slot_rows has {rows.numel()} entries, expected {n_slots}")
+        if ((rows < -1) | (rows >= n)).any():
+            raise MoeIndexError("slot row outside [-1, offsets[E])")
+        placed = rows >= 0
+        if int(placed.sum()) != n:
+            raise MoeIndexError("slot_rows and the placed slots disagree in number")
+        pos = torch.arange(rows.numel())
+        if n and not torch.equal(used[rows[placed]], pos[placed]):
+            raise MoeIndexError("slot_rows is not the inverse of sorted_slots")
+
+
 def _layer_dims(x, w1, variant, gating=GATING_PAIR, capacity=0):
     T, d = x.shape
     f = w1.shape[1]
@@ -161,6 +233,8 @@ def permute(topk_idx, d=128, f=128, capacity=0, workspace=None):
     n = ctypes.c_size_t(workspace.numel())
     _check("moe_permute", lib.moe_permute(ctypes.byref(dims), ptr(topk_idx), ptr(offs), ptr(sorted_slots),
                                           ptr(slot_rows), ptr(workspace), ctypes.byref(n), stream_handle()))
+    if DEBUG_BOUNDS:
+        check_permutation(offs, sorted_slots, slot_rows, T, capacity)
     return offs, sorted_slots, slot_rows
 
 
@@ -179,6 +253,8 @@ def grouped_swiglu(x, expert_offsets, sorted_slots, w1, w3, w2, variant=VARIANT_
     dims = _layer_dims(x, w1, variant)
     T, d = x.shape
     f = w1.shape[1]
+    if DEBUG_BOUNDS:
+        check_permutation(expert_offsets, sorted_slots, None, T)
     h = torch.empty((T * TOP_K, f), dtype=x.dtype, device=x.device)
     y_rows = torch.empty((T * TOP_K, d), dtype=torch.float32, device=x.device)
     _check("moe_grouped_swiglu", lib.moe_grouped_swiglu(ctypes.byref(dims), ptr(x), ptr(expert_offsets),
@@ -192,6 +268,8 @@ def expert_up(x, expert_offsets, sorted_slots, w1, w3, variant=VARIANT_AUTO, h=N
     lib = load_library()
     dims = _layer_dims(x, w1, variant)
     T = x.shape[0]
+    if DEBUG_BOUNDS:
+        check_permutation(expert_offsets, sorted_slots, None, T)
     if h is None:
         h = torch.empty((T * TOP_K, w1.shape[1]), dtype=x.dtype, device=x.device)
     _check("moe_expert_up", lib.moe_expert_up(ctypes.byref(dims), ptr(x), ptr(expert_offsets), ptr(sorted_slots),
@@ -204,6 +282,10 @@ def expert_down(h, expert_offsets, w2, T, variant=VARIANT_AUTO, y_rows=None):
     lib = load_library()
     d, f = w2.shape[1], w2.shape[2]
     dims = make_dims(T, d, f, h.dtype, variant)
+    if DEBUG_BOUNDS:
+        offs = expert_offsets.detach().cpu().to(torch.int64)
+        if int(offs[0]) != 0 or (offs[1:] < offs[:-1]).any() or int(offs[-1]) > T * TOP_K:
+            raise MoeIndexError(f"expert_offsets not a prefix sum within [0, {T * TOP_K}]")
     if y_rows is None:
         y_rows = torch.empty((T * TOP_K, d), dtype=torch.float32, device=h.device)
     _check("moe_expert_down", lib.moe_expert_down(ctypes.byref(dims), ptr(h), ptr(expert_offsets), ptr(w2),
@@ -217,6 +299,10 @@ def combine(y_rows, slot_rows, topk_w, out_dtype):
     T = topk_w.shape[0]
     d = y_rows.shape[1]
     dims = make_dims(T, d, 128, out_dtype)
+    if DEBUG_BOUNDS:
+        rows = slot_rows.detach().cpu().to(torch.int64)
+        if rows.numel() != T * TOP_K or ((rows < -1) | (rows >= y_rows.shape[0])).any():
+            raise MoeIndexError("slot row outside [-1, rows of y_rows)")
     y = torch.empty((T, d), dtype=out_dtype, device=y_rows.device)
     _check("moe_combine", lib.moe_combine(ctypes.byref(dims), ptr(y_rows), ptr(slot_rows), ptr(topk_w), ptr(y),
                                           stream_handle()))
@@ -358,6 +444,13 @@ class RoutedResidualFFN:
             ctypes.byref(self.dims), ptr(x), ptr(topk_idx), ptr(topk_w), ptr(w1), ptr(w3), ptr(w2), ptr(resid),
             ptr(u_out), self.eps, ptr(w_gate_next), ptr(logit_bias_next), ptr(idx_next), ptr(w_next),
             ptr(self.counts), ptr(self.ws), ctypes.byref(self.ws_bytes), stream_handle()))
+
+
+def mfma_ceiling(operands, clock_out, sink, iters):
+    """Launch moe_mfma_ceiling on the current stream (see moe.h)."""
+    lib = load_library()
+    _check("moe_mfma_ceiling", lib.moe_mfma_ceiling(ptr(operands), ptr(clock_out), ptr(sink), int(iters),
+                                                    stream_handle()))
 
 
 def load_balance_loss(logits, topk_idx):

@@ -279,3 +279,13 @@ def test_noalloc_rejects_a_layer_beyond_its_array():
     bad = moe.make_dims(16, 4096, 14336, moe.MOE_BF16, E=4)
     assert lib.moe_ffn_forward_noalloc(ctypes.byref(bad), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, None,
                                        None, None) == moe.MOE_ERR_UNSUPPORTED
+
+
+@needs_no_gpu
+def test_mfma_ceiling_validates():
+    lib = _lib()
+    INV = moe.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_mfma_ceiling(None, FAKE, FAKE, 10, None) == INV
+    assert lib.moe_mfma_ceiling(FAKE, None, FAKE, 10, None) == INV
+    assert lib.moe_mfma_ceiling(FAKE, FAKE, FAKE, 0, None) == INV
+    assert lib.moe_mfma_ceiling(MISALIGNED, FAKE, FAKE, 10, None) == INV

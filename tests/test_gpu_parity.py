@@ -279,6 +279,53 @@ def test_variants_agree():
     assert (a - b).abs().max().item() <= 2e-2 * a.abs().max().item() + 2e-3
 
 
+@pytest.mark.parametrize("T,d,f,dtype", [(300, 256, 512, "bf16"), (40, 256, 512, "bf16"), (2100, 256, 256, "bf16"),
+                                         (100, 128, 256, "f32")])
+def test_non_finite_tokens_stay_contained(T, d, f, dtype):
+    """Tokens whose row holds NaN or +-Inf (undefined inputs: the pages fix
+    nothing for them) get a valid pair of distinct experts and leave every
+    other token's routing and output bit-identical to the clean run: each
+    token is transformed on its own ("Mixtral > Architecture Overview",
+    opening paragraphs).  Prefill kernels (with the remainder split at
+    T=2100), streaming decode kernels, fp32."""
+    layer = _layer(T, d, f, dtype=dtype, seed=900 + T)
+    args = (layer["w_gate"], layer["w1"], layer["w3"], layer["w2"])
+    y0, idx0, w0, _ = moe.ffn_forward(layer["x"], *args, return_routing=True)
+    bad = [3, T // 2, T - 1]
+    x = layer["x"].clone()
+    x[bad[0], 5] = float("nan")
+    x[bad[1], 0] = float("inf")
+    x[bad[2], d - 1] = float("-inf")
+    y1, idx1, w1, counts1 = moe.ffn_forward(x, *args, return_routing=True)
+    torch.cuda.synchronize()
+    good = np.setdiff1d(np.arange(T), bad)
+    sel = torch.from_numpy(good).cuda()
+    assert torch.equal(idx1[sel], idx0[sel]) and torch.equal(w1[sel], w0[sel])
+    assert torch.equal(y1[sel], y0[sel])
+    ids = idx1.cpu().numpy()
+    assert ((ids >= 0) & (ids < 8)).all() and (ids[:, 0] != ids[:, 1]).all()
+    assert int(counts1.sum()) == 2 * T
+
+
+def test_debug_bounds_mode_catches_a_bad_permutation_before_launch(monkeypatch):
+    # A permutation with a slot placed twice (indices still in range, so the
+    # launch itself could not fault) is refused by the binding's host-side
+    # check before anything is enqueued.
+    layer = _layer(300, 256, 512, seed=77)
+    idx, w = moe.router_topk(layer["x"], layer["w_gate"])
+    monkeypatch.setattr(moe, "DEBUG_BOUNDS", True)
+    offs, sorted_slots, slot_rows = moe.permute(idx, 256, 512)  # the library's own: passes the check
+    bad = sorted_slots.clone()
+    bad[1] = bad[0]
+    with pytest.raises(moe.MoeIndexError):
+        moe.grouped_swiglu(layer["x"], offs, bad, layer["w1"], layer["w3"], layer["w2"])
+    rows_bad = slot_rows.clone()
+    rows_bad[0] = 600 * 2
+    y_rows = torch.zeros((600, 256), dtype=torch.float32, device="cuda")
+    with pytest.raises(moe.MoeIndexError):
+        moe.combine(y_rows, rows_bad, w, torch.bfloat16)
+
+
 def test_deterministic():
     layer = _layer(1000, 256, 512, seed=13)
     f = moe.FFN(layer["x"], layer["w_gate"], layer["w1"], layer["w3"], layer["w2"])
@@ -604,12 +651,19 @@ def _unit_plan(counts, T, d, f, n_cu, k=2):
     # on the streaming kernel: units of 64 w2 rows, 2 waves per CU, the
     # reduction split in P parts (doubling up to 8 while the units fit and P
     # divides the 128-deep stages)
+    # The parts' partial sums live in the workspace's second region past the
+    # GEMM's partial planes (n_cu planes of 256 x 256 fp32 at most): a header
+    # and P x 8 experts x 32 rows x d fp32, P at most what fits.
     n_tails = sum(1 for c in counts if c > 256 and c - (c - 1) // 256 * 256 <= 32)
     units, stages, P = n_tails * (d // 64), f // 128, 1
+    region = -(-T * k * d * 4 // 256) * 256
+    rest = region - min(region, n_cu * 256 * 256 * 4)
+    pcap = min(8, max(0, rest - 256) // (8 * 32 * d * 4)) if rest > 256 else 0
     if down_unsplit and n_tails:
-        while 2 * P <= 8 and units * 2 * P <= 2 * n_cu and stages % (2 * P) == 0:
+        while 2 * P <= 8 and 2 * P <= pcap and units * 2 * P <= 2 * n_cu and stages % (2 * P) == 0:
             P *= 2
     out["tail_parts"] = P
+    out["tail_part_capacity"] = pcap
     return out
 
 
@@ -675,19 +729,25 @@ def test_prefill_tile_shapes_in_remainder_pieces():
     assert np.abs(O._f64(y.cpu()) - ref).max() <= _tol("bf16", ref)
 
 
-def test_down_unsplit_from_one_full_round():
-    # 2100 tokens at d=4096: 16 full m-tiles x 16 n-tiles = one full round of
+@pytest.mark.parametrize("T", [2100, 2400])
+def test_down_unsplit_from_one_full_round(T):
+    # T=2100 at d=4096: 16 full m-tiles x 16 n-tiles = one full round of
     # down-projection tiles, so the reduction is not split and the experts'
     # short tails (rows past their second full tile) go to the streaming
-    # kernel, its reduction split in parts and summed by the fixup launch.
-    T, d, f = 2100, 4096, 512
+    # kernel.  Its partial sums would need 4 MiB per part past the GEMM's
+    # 64 MiB of partial planes and only 1.7 MB are left: the tails run
+    # unsplit.  T=2400 leaves room for split tails (and a remainder round).
+    d, f = 4096, 512
     layer = inputs.make_custom(T, d, f, seed=47, device="cpu")
     layer = {k2: (v.cuda() if torch.is_tensor(v) else v) for k2, v in layer.items()}
     out = run_and_check(layer, variant=moe.VARIANT_PREFILL)
     counts = out["counts"].cpu().tolist()
     plan = _unit_plan(counts, T, d, f, torch.cuda.get_device_properties(0).multi_processor_count)
-    assert (T * 2 // 256) * (d // 256) == 256, plan
-    assert plan["tail_parts"] >= 2, (counts, plan)
+    if T == 2100:
+        assert (T * 2 // 256) * (d // 256) == 256, plan
+        assert plan["tail_part_capacity"] == 0 and plan["tail_parts"] == 1, (counts, plan)
+    else:
+        assert plan["tail_part_capacity"] >= 2, (counts, plan)
 
 
 @pytest.mark.parametrize("d,out", [(1152, "f32"), (5120, "f32"), (1152, "bf16"), (128, "bf16")])
