@@ -62,7 +62,7 @@ def parse():
     p.add_argument("--sweep-steps", type=int, default=10)
     p.add_argument("--sweep-t", default=None,
                    help="comma-separated token counts to run in the T-sweep (default: the whole sweep)")
-    p.add_argument("--stack-steps", type=int, default=3)
+    p.add_argument("--stack-steps", type=int, default=10)
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -312,6 +312,15 @@ def prefill_section(L, args, torch, moe, A, label, want_clock):
     counts = layer.counts.cpu().tolist()
     stages, stage_total = stage_times(layer, args.steps, torch, moe)
     out = {"t": t, "counts": counts, "stages": stages, "stage_total": stage_total}
+    # the standalone permutation (moe_permute: per-group counts, then one wave
+    # per 16-token group) on the layer's own routing, beside the layer's
+    # permutation stage (which takes the group counts from the router); its
+    # kernels' own durations are in the kernel trace, this figure is the
+    # binding's call between two events (output allocation and the gaps
+    # while Python issues the launches included)
+    ws = torch.empty((moe.permute_workspace_size(T),), dtype=torch.uint8, device="cuda")
+    tp = time_steps(lambda: moe.permute(layer.idx, workspace=ws), args.steps, 3, torch)
+    out["permute_standalone_ms"] = tp["median_ms"]
     if want_clock:
         n_cu = torch.cuda.get_device_properties(0).multi_processor_count
         G = (n_cu // 8) * 8
@@ -388,6 +397,7 @@ def main():
                        "routing": "near-uniform (router std 0.02)", "counts": P["counts"]},
             "layer_frac_of_bf16_peak": flops / sec / A.PEAK_BF16_FLOPS,
             "stage_ms": stages, "stage_ms_sum": sum(stages.values()), "stage_ms_event_span": P["stage_total"],
+            "moe_permute_call_ms": P["permute_standalone_ms"],
             "stage_ms_note": "medians over the timed steps of moe_ffn_forward_timed: the layer's own launches with "
                              "HIP events between stages on its stream",
             "clock_mhz": clock,
