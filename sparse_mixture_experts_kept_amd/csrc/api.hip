@@ -173,6 +173,24 @@ moe_status run_router(const moe_dims* dims, const void* x, const void* w_gate, c
                                       n_cu, s, group_counts));
 }
 
+// The permutation's form for T tokens: per-group counts then one wave per
+// 16-token group when the slots exceed one workgroup's ballot form and the
+// group counts fit; otherwise one workgroup.
+bool permute_by_groups(const moe_dims* dims) {
+  return dims->T * dims->k > moe::kPermuteSmallSlots && dims->T <= moe::kMaxGroupPermuteTokens;
+}
+
+// Permutation of the pairs in idx; group_counts [ceil(T/16), 8] int32 is
+// scratch for the multi-workgroup form.
+moe_status permute_slots(const moe_dims* dims, const int32_t* idx, int32_t* group_counts, int32_t* offs,
+                         int32_t* sorted, int32_t* rows, int32_t* counts_out, hipStream_t s) {
+  if (permute_by_groups(dims))
+    return hip_status(moe::launch_permute_counted(idx, static_cast<int32_t>(dims->T), group_counts, offs, sorted,
+                                                  rows, counts_out, dims->capacity, s));
+  return hip_status(moe::launch_permute(idx, static_cast<int32_t>(dims->T * dims->k), offs, sorted, rows,
+                                        counts_out, dims->capacity, s));
+}
+
 moe_status run_up(const moe_dims* dims, const void* x, const int32_t* offs, const int32_t* sorted, const void* w1,
                   const void* w3, void* h, hipStream_t s) {
   if (dims->dtype == MOE_F32)
@@ -271,7 +289,7 @@ moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* e
   if (!workspace_bytes) return MOE_ERR_INVALID_ARGUMENT;
   // Group counts [ceil(T/16), 8] for the multi-workgroup form (a token
   // count the one-workgroup forms handle still asks for a minimal workspace).
-  const bool groups = dims->T * dims->k > moe::kPermuteSmallSlots && dims->T <= moe::kMaxGroupPermuteTokens;
+  const bool groups = permute_by_groups(dims);
   const size_t need = groups ? align256(static_cast<size_t>((dims->T + 15) / 16) * dims->E * 4) : 256;
   if (!workspace) {
     *workspace_bytes = need;
@@ -283,13 +301,8 @@ moe_status moe_permute(const moe_dims* dims, const int32_t* topk_idx, int32_t* e
   if (!aligned(topk_idx, 4) || !aligned(expert_offsets, 4) || !aligned(sorted_slots, 4) || !aligned(slot_rows, 4) ||
       !aligned(workspace, 16))
     return MOE_ERR_INVALID_ARGUMENT;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (groups)
-    return hip_status(moe::launch_permute_counted(topk_idx, static_cast<int32_t>(dims->T),
-                                                  static_cast<int32_t*>(workspace), expert_offsets, sorted_slots,
-                                                  slot_rows, nullptr, dims->capacity, s));
-  return hip_status(moe::launch_permute(topk_idx, static_cast<int32_t>(dims->T * dims->k), expert_offsets,
-                                        sorted_slots, slot_rows, nullptr, dims->capacity, s));
+  return permute_slots(dims, topk_idx, static_cast<int32_t*>(workspace), expert_offsets, sorted_slots, slot_rows,
+                       nullptr, static_cast<hipStream_t>(stream));
 }
 
 moe_status moe_grouped_swiglu(const moe_dims* dims, const void* x, const int32_t* expert_offsets,
@@ -445,11 +458,11 @@ moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_g
 
   st = mark(marks, 0, s);
   if (st != MOE_OK) return st;
+  int32_t* gcounts = reinterpret_cast<int32_t*>(ws + plan.gcounts);
   if (routed) {
     st = mark(marks, 1, s);
     if (st != MOE_OK) return st;
-    st = hip_status(moe::launch_permute(pair, static_cast<int32_t>(dims->T * dims->k), offs, sorted, rows,
-                                        expert_counts_out, dims->capacity, s));
+    st = permute_slots(dims, pair, gcounts, offs, sorted, rows, expert_counts_out, s);
     if (st != MOE_OK) return st;
   } else if (dims->T <= kRoutePermuteMaxTokens) {
     // Small batch: routing and permutation in one workgroup.
@@ -462,7 +475,6 @@ moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_g
   } else if (dims->dtype == MOE_BF16 && dims->T <= moe::kMaxGroupPermuteTokens) {
     // The router counts each 16-token group's slots per expert; the
     // permutation then runs one wave per group.
-    int32_t* gcounts = reinterpret_cast<int32_t*>(ws + plan.gcounts);
     st = run_router(dims, x, w_gate, logit_bias, idx, w, nullptr, s, gcounts);
     if (st == MOE_OK) st = mark(marks, 1, s);
     if (st != MOE_OK) return st;
@@ -473,8 +485,7 @@ moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_g
     st = run_router(dims, x, w_gate, logit_bias, idx, w, nullptr, s);
     if (st == MOE_OK) st = mark(marks, 1, s);
     if (st != MOE_OK) return st;
-    st = hip_status(moe::launch_permute(idx, static_cast<int32_t>(dims->T * dims->k), offs, sorted, rows,
-                                        expert_counts_out, dims->capacity, s));
+    st = permute_slots(dims, idx, gcounts, offs, sorted, rows, expert_counts_out, s);
     if (st != MOE_OK) return st;
   }
   // (routing and permutation in one launch: the routing stage holds both)

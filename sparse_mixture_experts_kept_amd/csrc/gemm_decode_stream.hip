@@ -373,10 +373,16 @@ hipError_t launch_down_decode_stream(const bf16_t* h, const int32_t* offs, const
 
 // Tails of the prefill layer (rows of an expert past its last full 256-row
 // tile when at most 32): one pass of two token groups.  x / h as in the
-// prefill launch; n_slots = T * 2.
+// prefill launch; n_slots = T * 2.  Shapes measured on the T=4096 layer's
+// three tails (alternating launches in one process, bit-identical outputs):
+// up projection, units of 32 rows of w1 and w3, 3 stages, two waves per CU:
+// 119 us (units of 16 rows, 4 stages: 129; 512-byte runs: 123-143; three
+// waves per CU: 124-138; one: 146-183); down projection, units of 32 rows of
+// w2, 3 stages, three waves per CU: 60 us (64-row units, two waves per CU,
+// the earlier shape: 73; 512-byte runs: 76-86).
 hipError_t launch_up_tail_stream(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots, const bf16_t* w1,
                                  const bf16_t* w3, bf16_t* h, int64_t T, int d, int f, int n_cu, hipStream_t s) {
-  return launch_stream<true, 256, 2, 2, 4, 2, true>(x, sorted_slots, offs, w1, w3, h, d, f, static_cast<int>(T), n_cu,
+  return launch_stream<true, 256, 4, 2, 3, 2, true>(x, sorted_slots, offs, w1, w3, h, d, f, static_cast<int>(T), n_cu,
                                                      s);
 }
 
@@ -384,7 +390,7 @@ hipError_t launch_down_tail_stream(const bf16_t* h, const int32_t* offs, const b
                                    int d, int f, int n_cu, float* tail_part, int64_t tail_part_bytes, hipStream_t s) {
   const int n_slots = static_cast<int>(T) * kTopK;
   const int pcap = tail_part_capacity(tail_part, tail_part_bytes, d);
-  return launch_stream<false, 256, 4, 2, 3, 2, true>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s,
+  return launch_stream<false, 256, 2, 2, 3, 3, true>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s,
                                                      pcap >= 2 ? tail_part : nullptr, pcap);
 }
 

@@ -559,6 +559,34 @@ def test_capacity_large_enough_changes_nothing():
     assert torch.equal(y0, y1)
 
 
+@pytest.mark.parametrize("T,capacity", [(300, 60), (3000, 600)])
+def test_routed_layer_with_capacity(T, capacity):
+    # The routed entry point with a capacity (per-group counts for 3000
+    # tokens, the ballot form for 300): skewed given pairs, dropped slots add
+    # nothing, counts are the routed counts before dropping.
+    layer = _layer(T, 256, 512, seed=300 + T)
+    rng = np.random.default_rng(T)
+    scores = rng.standard_normal((T, 8)) + np.array([1.5, 0.8, 0, 0, 0, 0, -0.5, -1.0])
+    ids = O.select_top_k(scores, 2).astype(np.int32)
+    g0 = rng.uniform(0.5, 1.0, T)
+    gates = np.stack([g0, 1.0 - g0], axis=1).astype(np.float32)
+    counts_out = torch.empty(8, dtype=torch.int32, device="cuda")
+    rf = moe.RoutedFFN(layer["x"], layer["w1"], layer["w3"], layer["w2"], counts=counts_out, capacity=capacity)
+    y = rf(torch.from_numpy(ids).cuda(), torch.from_numpy(gates).cuda())
+    torch.cuda.synchronize()
+    counts = np.bincount(ids.ravel(), minlength=8)
+    assert counts.max() > capacity, counts  # something is dropped
+    np.testing.assert_array_equal(counts_out.cpu().numpy(), counts)
+    keep = O.capacity_keep(ids.astype(np.int64), capacity)
+    xs = O._f64(_cpu(layer["x"]))
+    widen = _widen_experts(layer)
+    ref = np.zeros((T, 256))
+    for e in range(8):
+        tok, slot = np.nonzero((ids == e) & keep)
+        np.add.at(ref, tok, gates[tok, slot].astype(np.float64)[:, None] * O.swiglu_expert(xs[tok], *widen(e)))
+    assert np.abs(O._f64(y.cpu()) - ref).max() <= _tol("bf16", ref)
+
+
 @pytest.mark.parametrize("T,capacity", [(200, 30), (3000, 500), (3000, 1)])
 def test_capacity_permutation_exact(T, capacity):
     rng = np.random.default_rng(T + capacity)
@@ -582,8 +610,8 @@ def test_capacity_permutation_exact(T, capacity):
 
 @pytest.mark.parametrize("T", [300, 3000])
 def test_out_of_range_ids_get_no_row(T):
-    # ids outside [0, 8) (ballot form for T <= 512, chunked form above) are
-    # left out like dropped slots, and the routed layer adds nothing for them
+    # ids outside [0, 8) (ballot form for T <= 512, per-group counts above)
+    # are left out like dropped slots, and the routed layer adds nothing for them
     rng = np.random.default_rng(T)
     idx = O.select_top_k(rng.standard_normal((T, 8)), 2).astype(np.int32)
     bad = rng.random((T, 2)) < 0.05
