@@ -676,28 +676,28 @@ def _unit_plan(counts, T, d, f, n_cu, k=2):
             P, rem = 1, 0
         out[name] = dict(n_full=n_full, rounds=R, rem=rem, parts=P)
     # down-projection tails (a last tile of at most 32 rows after a full one)
-    # on the streaming kernel: units of 64 w2 rows, 2 waves per CU, the
+    # on the streaming kernel: units of 32 w2 rows, 3 waves per CU, the
     # reduction split in P parts (doubling up to 8 while the units fit and P
     # divides the 128-deep stages)
     # The parts' partial sums live in the workspace's second region past the
     # GEMM's partial planes (n_cu planes of 256 x 256 fp32 at most): a header
     # and P x 8 experts x 32 rows x d fp32, P at most what fits.
     n_tails = sum(1 for c in counts if c > 256 and c - (c - 1) // 256 * 256 <= 32)
-    units, stages, P = n_tails * (d // 64), f // 128, 1
+    units, stages, P = n_tails * (d // 32), f // 128, 1
     region = -(-T * k * d * 4 // 256) * 256
     rest = region - min(region, n_cu * 256 * 256 * 4)
     pcap = min(8, max(0, rest - 256) // (8 * 32 * d * 4)) if rest > 256 else 0
     if down_unsplit and n_tails:
-        while 2 * P <= 8 and 2 * P <= pcap and units * 2 * P <= 2 * n_cu and stages % (2 * P) == 0:
+        while 2 * P <= 8 and 2 * P <= pcap and units * 2 * P <= 3 * n_cu and stages % (2 * P) == 0:
             P *= 2
     out["tail_parts"] = P
     out["tail_part_capacity"] = pcap
     return out
 
 
-@pytest.mark.parametrize("T,d,f,seed,bias7,tail_parts", [(4200, 4096, 256, 1, None, 2), (4200, 4096, 1024, 2, None, 2),
-                                                        (4200, 4096, 256, 5, -3.0, 1), (4160, 4096, 1024, 28, None, 8),
-                                                        (4160, 4096, 1024, 27, None, 4)])
+@pytest.mark.parametrize("T,d,f,seed,bias7,tail_parts", [(4200, 4096, 256, 1, None, 1), (4200, 4096, 1024, 2, None, 2),
+                                                        (4200, 4096, 256, 5, -3.0, 1), (4160, 4096, 1024, 28, None, 4),
+                                                        (4160, 4096, 1024, 27, None, 2)])
 def test_prefill_remainder_split(T, d, f, seed, bias7, tail_parts):
     # Layers whose work units leave a partial round of the grid: the units
     # past the last whole round are cut along the reduction and summed by the
@@ -705,9 +705,9 @@ def test_prefill_remainder_split(T, d, f, seed, bias7, tail_parts):
     # one whole round plus a split remainder in both projections; bias7
     # leaves expert 7 (the last in unit order) 14 rows, so its one m-tile
     # takes the thin path inside the split.  The down-projection tails are
-    # split too when few experts have one: three (2 parts), two (4), one
-    # (8).  Inputs are drawn on the CPU so the routing is fixed independently
-    # of the device.
+    # split too when few experts have one: four tails stream unsplit, three
+    # or two in 2 parts, one in 4.  Inputs are drawn on the CPU so the
+    # routing is fixed independently of the device.
     layer = inputs.make_custom(T, d, f, seed=seed, device="cpu")
     if bias7 is not None:
         layer["logit_bias"] = torch.tensor([0.0] * 7 + [bias7], dtype=torch.float32)
@@ -722,6 +722,22 @@ def test_prefill_remainder_split(T, d, f, seed, bias7, tail_parts):
     # deterministic: a second run gives the same bits
     y2 = moe.ffn_forward(layer["x"], layer["w_gate"], layer["w1"], layer["w3"], layer["w2"],
                          logit_bias=layer.get("logit_bias"), variant=moe.VARIANT_PREFILL)
+    assert torch.equal(out["y"], y2)
+
+
+def test_down_tail_in_eight_parts():
+    # One tailed expert (1286 rows: 6 past its fifth full tile) at d=2048:
+    # its 64 down-projection tail units split the reduction in 8 parts, the
+    # most the fixup adds, beside a split remainder round of the down GEMM.
+    T, d, f = 5200, 2048, 2048
+    layer = inputs.make_custom(T, d, f, seed=5, device="cpu")
+    layer = {k2: (v.cuda() if torch.is_tensor(v) else v) for k2, v in layer.items()}
+    out = run_and_check(layer, variant=moe.VARIANT_PREFILL)
+    counts = out["counts"].cpu().tolist()
+    plan = _unit_plan(counts, T, d, f, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert plan["tail_parts"] == 8 and plan["down"]["parts"] >= 2, (counts, plan)
+    y2 = moe.ffn_forward(layer["x"], layer["w_gate"], layer["w1"], layer["w3"], layer["w2"],
+                         variant=moe.VARIANT_PREFILL)
     assert torch.equal(out["y"], y2)
 
 
