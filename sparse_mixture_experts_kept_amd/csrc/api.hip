@@ -402,10 +402,6 @@ moe_status combine_or_glue(const moe_dims* dims, const float* y_rows, const floa
                                                       glue->eps, dims->gating, n_cu, s));
 }
 
-struct ResidualGlue;
-moe_status combine_or_glue(const moe_dims* dims, const float* y_rows, const float* y_rows2, const int32_t* rows,
-                           const float* gate, void* y, const ResidualGlue* glue, int n_cu, hipStream_t s);
-
 // The whole layer.  routed_idx / routed_w given: the routing was computed by
 // the caller (e.g. by moe_rmsnorm_residual_route) and the router is skipped.
 moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_gate, const float* logit_bias,
