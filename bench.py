@@ -62,7 +62,7 @@ def parse():
     p.add_argument("--sweep-steps", type=int, default=10)
     p.add_argument("--sweep-t", default=None,
                    help="comma-separated token counts to run in the T-sweep (default: the whole sweep)")
-    p.add_argument("--stack-steps", type=int, default=10)
+    p.add_argument("--stack-steps", type=int, default=20)
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -557,12 +557,12 @@ def main():
             stack.load_input(x0)
             stack.forward()
 
-        t = time_steps(stack_step, args.stack_steps, 1, torch)
+        t = time_steps(stack_step, args.stack_steps, 5, torch)
         hist = stack.hist.cpu().tolist()
         other = {}
         for mode in ("router", "none"):  # the combine as its own launch; also the router as its own launch
             stack.mode = mode
-            other[mode] = time_steps(stack_step, args.stack_steps, 1, torch)
+            other[mode] = time_steps(stack_step, max(2, args.stack_steps // 2), 2, torch)
         stack.mode = "combine"
         sec = t["mean_ms"] * 1e-3
         flops = w["layers"] * A.layer_flops(w["T"], d, f, E, k)
