@@ -13,9 +13,10 @@ namespace {
 using moe::bf16_t;
 
 // AUTO takes the streaming kernels up to here: measured on the full-size
-// layer, the grouped GEMM is faster from T = 96 on (four token groups per
-// pass load twice the weight bytes in token rows per stage).
-constexpr int64_t kDecodeMaxTokens = 64;
+// layer (d = 4096, f = 14336), they are 2-4% faster than the grouped GEMM up
+// to T = 128 (T = 80-128: 495-511 us against 510-523 us); beyond, experts
+// with more than 64 rows take further passes over their weights.
+constexpr int64_t kDecodeMaxTokens = 128;
 constexpr int64_t kRoutePermuteMaxTokens = 64;  // routing fused with the permutation (one workgroup)
 constexpr size_t kRouterLdsLimit = 128 * 1024;
 constexpr int kMaxDevices = 64;

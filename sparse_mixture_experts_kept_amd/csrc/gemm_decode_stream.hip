@@ -344,12 +344,18 @@ hipError_t launch_stream(const bf16_t* act, const int32_t* sorted_slots, const i
 
 // T <= 32: one token group per pass (16 rows; an expert with more takes a
 // second pass, rare with 8 rows per expert on average); T <= 64: two groups
-// per pass.  Shapes measured at d=4096, f=14336, T=32 on MI355X (alternating
-// launches in one process): up projection with 512-byte row runs, 3 stages
-// (277 us; 256-byte runs, 6 stages: 292 us), down projection with units of
-// 64 rows of w2, 3 stages (138-144 us; 32-row units: 159-163 us).  d and f
-// are multiples of 128 (checked at the boundary): 512-byte runs need d to be
-// a multiple of 256, the other shapes divide any such d and f.
+// per pass.  Shapes measured at d=4096, f=14336 on MI355X (alternating
+// launches in one process, two weight sets): T=32, up projection with
+// 512-byte row runs, 3 stages (268-277 us; 256-byte runs, 6 stages: 281-292
+// us), down projection with units of 64 rows of w2, 3 stages (138-144 us;
+// 32-row units: 158-163 us); T=48 and 64, up with 512-byte runs, 2 stages
+// (282-285 us; 256-byte runs: 292-306 us), down with 64-row units, 3 stages
+// (141 us; 32-row units: 161-170 us); T=96 and 128 (four groups per pass),
+// units of 32 rows of w1 and w3 / 64 rows of w2, 2 stages (up 318-330 us,
+// down 159-162 us; 16- and 32-row units with 3 stages: up 368-392, down
+// 193-197; 512-byte runs, one workgroup per CU: 633-643 and 317-325).  d and
+// f are multiples of 128 (checked at the boundary): 512-byte runs need d to
+// be a multiple of 256, the other shapes divide any such d and f.
 hipError_t launch_up_decode_stream(const bf16_t* x, const int32_t* offs, const int32_t* sorted_slots,
                                    const bf16_t* w1, const bf16_t* w3, bf16_t* h, int64_t T, int d, int f, int n_cu,
                                    hipStream_t s) {
@@ -358,8 +364,11 @@ hipError_t launch_up_decode_stream(const bf16_t* x, const int32_t* offs, const i
     if (d % 256 == 0) return launch_stream<true, 512, 2, 1, 3>(x, sorted_slots, offs, w1, w3, h, d, f, T, n_cu, s);
     return launch_stream<true, 256, 2, 1, 6>(x, sorted_slots, offs, w1, w3, h, d, f, T, n_cu, s);
   }
-  if (T <= 64) return launch_stream<true, 256, 2, 2, 4>(x, sorted_slots, offs, w1, w3, h, d, f, T, n_cu, s);
-  return launch_stream<true, 256, 2, 4, 3>(x, sorted_slots, offs, w1, w3, h, d, f, T, n_cu, s);
+  if (T <= 64) {
+    if (d % 256 == 0) return launch_stream<true, 512, 2, 2, 2>(x, sorted_slots, offs, w1, w3, h, d, f, T, n_cu, s);
+    return launch_stream<true, 256, 2, 2, 4>(x, sorted_slots, offs, w1, w3, h, d, f, T, n_cu, s);
+  }
+  return launch_stream<true, 256, 4, 4, 2>(x, sorted_slots, offs, w1, w3, h, d, f, T, n_cu, s);
 }
 
 hipError_t launch_down_decode_stream(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int64_t T,
@@ -367,8 +376,8 @@ hipError_t launch_down_decode_stream(const bf16_t* h, const int32_t* offs, const
   if (T > kStreamMaxTokens) return hipErrorInvalidValue;
   const int n_slots = static_cast<int>(T) * kTopK;
   if (T <= 32) return launch_stream<false, 256, 4, 1, 3>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s);
-  if (T <= 64) return launch_stream<false, 256, 2, 2, 4>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s);
-  return launch_stream<false, 256, 2, 4, 3>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s);
+  if (T <= 64) return launch_stream<false, 256, 4, 2, 3>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s);
+  return launch_stream<false, 256, 4, 4, 2>(h, nullptr, offs, w2, nullptr, y_rows, d, f, n_slots, n_cu, s);
 }
 
 // Tails of the prefill layer (rows of an expert past its last full 256-row

@@ -825,9 +825,13 @@ def test_combine_row_widths(d, out):
 # --------------------------------------------------------------------------- full Mixtral-sized layers (sampled)
 
 
-def test_decode_workload_full():
-    # T = 32: the oracle checks every token
-    layer = inputs.make_workload("decode", device="cuda")
+@pytest.mark.parametrize("T", [32, 64])
+def test_decode_workload_full(T):
+    # the decode workload (T = 32) and the largest batch the streaming
+    # kernels take by default (T = 64: two token groups per pass, 512-byte
+    # runs on the up projection, 64-row units on the down); the oracle checks
+    # every token
+    layer = inputs.make_workload("decode", device="cuda", T=T)
     run_and_check(layer)
 
 
