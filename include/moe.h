@@ -268,8 +268,8 @@ moe_status moe_ffn_forward_routed(const moe_dims* dims, const void* x, const int
  *   Arguments, outputs and errors as moe_ffn_forward; a layer whose
  *   workspace (moe_ffn_forward's size query) exceeds 32 MiB is rejected with
  *   MOE_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (at d = 4096,
- *   f = 14336: up to 272 tokens on the prefill kernels, 64 on the decode
- *   kernels).  All calls on one GPU share its array and it keeps the last
+ *   f = 14336: up to 272 tokens with the kernels AUTO picks, 372 with the
+ *   decode kernels forced).  All calls on one GPU share its array and it keeps the last
  *   call's contents (the layer writes every region before reading it, so
  *   nothing needs clearing): calls that overlap on one GPU -- on different
  *   streams or from different threads without ordering -- race and give
