@@ -219,15 +219,19 @@ def router_topk(x, w_gate, logit_bias=None, return_logits=False, gating=GATING_P
     return (idx, w, logits) if return_logits else (idx, w)
 
 
-def permute(topk_idx, d=128, f=128, capacity=0, workspace=None):
+def permute(topk_idx, d=128, f=128, capacity=0, workspace=None, out=None):
     """expert_offsets [9], sorted_slots [T*2], slot_rows [T*2] (int32; -1 for
-    a slot dropped by the expert capacity)."""
+    a slot dropped by the expert capacity).  ``out``: those three tensors,
+    preallocated (nothing is allocated then)."""
     lib = load_library()
     T = topk_idx.shape[0]
     dims = make_dims(T, d, f, MOE_BF16, capacity=capacity)
-    offs = torch.zeros((E_EXPERTS + 1,), dtype=torch.int32, device=topk_idx.device)
-    sorted_slots = torch.empty((T * TOP_K,), dtype=torch.int32, device=topk_idx.device)
-    slot_rows = torch.empty((T * TOP_K,), dtype=torch.int32, device=topk_idx.device)
+    if out is not None:
+        offs, sorted_slots, slot_rows = out
+    else:
+        offs = torch.zeros((E_EXPERTS + 1,), dtype=torch.int32, device=topk_idx.device)
+        sorted_slots = torch.empty((T * TOP_K,), dtype=torch.int32, device=topk_idx.device)
+        slot_rows = torch.empty((T * TOP_K,), dtype=torch.int32, device=topk_idx.device)
     if workspace is None:
         workspace = torch.empty((permute_workspace_size(T, capacity),), dtype=torch.uint8, device=topk_idx.device)
     n = ctypes.c_size_t(workspace.numel())

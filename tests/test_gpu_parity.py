@@ -559,6 +559,21 @@ def test_capacity_large_enough_changes_nothing():
     assert torch.equal(y0, y1)
 
 
+def test_permute_into_preallocated_buffers():
+    # moe_permute writing into caller buffers that hold stale values gives
+    # the same arrays as into fresh ones (every offset and every slot's row
+    # is written; the sorted slots up to offsets[E])
+    rng = np.random.default_rng(7)
+    T = 3000
+    idx = torch.from_numpy(O.select_top_k(rng.standard_normal((T, 8)), 2).astype(np.int32)).cuda()
+    ref = moe.permute(idx)
+    bufs = tuple(torch.full_like(r, -77) for r in ref)
+    got = moe.permute(idx, out=bufs)
+    assert all(g is b for g, b in zip(got, bufs))
+    n = int(ref[0][-1])
+    assert torch.equal(got[0], ref[0]) and torch.equal(got[2], ref[2]) and torch.equal(got[1][:n], ref[1][:n])
+
+
 @pytest.mark.parametrize("T,capacity", [(300, 60), (3000, 600)])
 def test_routed_layer_with_capacity(T, capacity):
     # The routed entry point with a capacity (per-group counts for 3000
