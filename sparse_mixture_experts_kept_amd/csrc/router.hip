@@ -362,9 +362,23 @@ __device__ __forceinline__ f32x4 router_scores_partial(const bf16_t* __restrict_
   const bf16_t* wp = wg + static_cast<int64_t>(real_row ? l16 : 0) * d + slice * ks + lg * 8;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const bf16x8 zero = {};
-  // ks is only a multiple of 32; the unroll keeps loads in flight.
-#pragma unroll 8
-  for (int k0 = 0; k0 < ks; k0 += 32) {
+  // ks is only a multiple of 32: the k-steps go in batches of 8 whose loads
+  // are all issued before their MFMAs (one memory latency per batch, not
+  // per step), then one step at a time.
+  constexpr int kBatch = 8;
+  int k0 = 0;
+  for (; k0 + kBatch * 32 <= ks; k0 += kBatch * 32) {
+    bf16x8 wa[kBatch], xa[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      wa[j] = *reinterpret_cast<const bf16x8*>(wp + k0 + 32 * j);
+      xa[j] = *reinterpret_cast<const bf16x8*>(xp + k0 + 32 * j);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(real_row ? wa[j] : zero, xa[j], acc, 0, 0, 0);
+  }
+  for (; k0 < ks; k0 += 32) {
     const bf16x8 wa = *reinterpret_cast<const bf16x8*>(wp + k0);
     const bf16x8 xa = *reinterpret_cast<const bf16x8*>(xp + k0);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(real_row ? wa : zero, xa, acc, 0, 0, 0);
@@ -510,12 +524,13 @@ namespace moe {
 // scores meet in LDS and are added in slice order; each group's pairs go to
 // global memory and to LDS, and the same workgroup then sorts the slots from
 // the LDS copy (no round trip through global memory).
+// kGroups token groups of 16 (T <= 16 * kGroups <= 64).
+template <int kGroups>
 __global__ void __launch_bounds__(kPermThreads) route_permute_mfma_kernel(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ wg, const float* __restrict__ bias,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out, int32_t T_tokens, int d, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_slots, int32_t* __restrict__ slot_rows, int32_t* __restrict__ counts_out,
     int gating, int capacity) {
-  constexpr int kGroups = 4;  // T <= 64
   __shared__ f32x4 part[kPermWaves][kGroups][kWave];
   __shared__ int32_t idx_s[kGroups * 16 * kTopK];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -534,8 +549,27 @@ __global__ void __launch_bounds__(kPermThreads) route_permute_mfma_kernel(
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
     const bf16x8 zero = {};
-#pragma unroll 4
-    for (int k0 = 0; k0 < ks; k0 += 32) {
+    // k-steps in batches whose loads are all issued before their MFMAs
+    // (groups past the batch's tokens load their clamped last row; the batch
+    // keeps the loaded fragments within the 128 registers of a 1024-thread
+    // workgroup), then one step at a time
+    constexpr int kBatch = kGroups <= 2 ? 4 : 2;
+    int k0 = 0;
+    for (; k0 + kBatch * 32 <= ks; k0 += kBatch * 32) {
+      bf16x8 wa[kBatch], xa[kBatch][kGroups];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        wa[j] = *reinterpret_cast<const bf16x8*>(wp + k0 + 32 * j);
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) xa[j][g] = *reinterpret_cast<const bf16x8*>(xp[g] + k0 + 32 * j);
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+          if (g < groups) acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(real_row ? wa[j] : zero, xa[j][g], acc[g], 0, 0, 0);
+    }
+    for (; k0 < ks; k0 += 32) {
       const bf16x8 wa = *reinterpret_cast<const bf16x8*>(wp + k0);
 #pragma unroll
       for (int g = 0; g < kGroups; ++g) {
@@ -591,9 +625,14 @@ hipError_t launch_route_permute(int dtype, const void* x, const void* wg, const 
                                 int32_t T, int d, int gating, int capacity, int32_t* offsets, int32_t* sorted_slots,
                                 int32_t* slot_rows, int32_t* counts_out, hipStream_t s) {
   if (dtype == kDtypeBF16) {
-    hipLaunchKernelGGL(route_permute_mfma_kernel, dim3(1), dim3(kPermThreads), 0, s, static_cast<const bf16_t*>(x),
-                       static_cast<const bf16_t*>(wg), bias, idx, w, T, d, offsets, sorted_slots, slot_rows,
-                       counts_out, gating, capacity);
+    if (T <= 32)
+      hipLaunchKernelGGL(route_permute_mfma_kernel<2>, dim3(1), dim3(kPermThreads), 0, s,
+                         static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(wg), bias, idx, w, T, d, offsets,
+                         sorted_slots, slot_rows, counts_out, gating, capacity);
+    else
+      hipLaunchKernelGGL(route_permute_mfma_kernel<4>, dim3(1), dim3(kPermThreads), 0, s,
+                         static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(wg), bias, idx, w, T, d, offsets,
+                         sorted_slots, slot_rows, counts_out, gating, capacity);
     return hipGetLastError();
   }
   const size_t lds = kExperts * static_cast<size_t>(d) * (dtype == kDtypeBF16 ? 2 : 4);
