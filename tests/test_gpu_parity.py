@@ -205,9 +205,10 @@ def test_bf16_prefill_kernels_tiny_batches(T):
 @pytest.mark.parametrize("T,d,f", [(32, 512, 1024), (64, 256, 512), (1, 256, 512), (7, 128, 256), (48, 384, 640),
                                    (33, 128, 128)])
 def test_bf16_decode_kernels(T, d, f):
-    # T <= 64: the streaming kernels (token groups of 16: two up to T=32,
-    # four above); d=128 or f=128 give units of a single stage, d=384 / f=640
-    # odd stage counts
+    # T <= 64: the streaming kernels (one token group of 16 per pass up to
+    # T=32, two above; the up projection's 512-byte row runs need d to be a
+    # multiple of 256, so d=384 and d=128 take the 256-byte form); d=128 or
+    # f=128 give units of a single stage, d=384 / f=640 odd stage counts
     run_and_check(_layer(T, d, f, seed=200 + T), variant=moe.VARIANT_DECODE)
 
 
