@@ -289,3 +289,40 @@ def test_mfma_ceiling_validates():
     assert lib.moe_mfma_ceiling(FAKE, None, FAKE, 10, None) == INV
     assert lib.moe_mfma_ceiling(FAKE, FAKE, FAKE, 0, None) == INV
     assert lib.moe_mfma_ceiling(MISALIGNED, FAKE, FAKE, 10, None) == INV
+
+
+def _expected_workspace(T, d, f, elem, prefill):
+    a = lambda n: (n + 255) // 256 * 256  # noqa: E731
+    slots = 2 * T
+    total = a(slots * 4) * 4 + a(9 * 4) + a((T + 15) // 16 * 8 * 4) + a(slots * f * elem) + a(slots * d * 4)
+    return total + (a(slots * d * 4) if prefill else 0)
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("T,d,f,dtype,variant,prefill", [
+    (1, 4096, 14336, "bf16", moe.VARIANT_AUTO, False), (32, 4096, 14336, "bf16", moe.VARIANT_AUTO, False),
+    (128, 4096, 14336, "bf16", moe.VARIANT_AUTO, False), (129, 4096, 14336, "bf16", moe.VARIANT_AUTO, True),
+    (4096, 4096, 14336, "bf16", moe.VARIANT_AUTO, True), (4096, 4096, 14336, "bf16", moe.VARIANT_DECODE, False),
+    (16, 512, 1024, "bf16", moe.VARIANT_PREFILL, True), (300, 128, 256, "bf16", moe.VARIANT_AUTO, False),
+    (300, 256, 128, "bf16", moe.VARIANT_PREFILL, False), (700, 256, 512, "f32", moe.VARIANT_AUTO, False),
+    (600000, 4096, 256, "bf16", moe.VARIANT_AUTO, False)])
+def test_workspace_layout(T, d, f, dtype, variant, prefill):
+    # The workspace is the routing, the permutation, the router's group
+    # counts, h and y_rows, each 256-byte aligned, plus the second fp32
+    # partial region only when the layer runs the bf16 prefill kernels: AUTO
+    # streams up to 128 tokens, the prefill kernels need d, f >= 256 and x
+    # below 4 GiB (600000 x 4096 bf16 is not), fp32 has its own kernels.
+    elem = 2 if dtype == "bf16" else 4
+    got = moe.workspace_size(T, d, f, torch.bfloat16 if dtype == "bf16" else torch.float32, variant)
+    assert got == _expected_workspace(T, d, f, elem, prefill)
+
+
+@needs_no_gpu
+def test_noalloc_token_limits():
+    # the fixed 32 MiB array holds the layer's workspace up to 272 Mixtral-
+    # sized tokens with the kernels AUTO picks and 372 with the streaming
+    # kernels forced
+    lim = 32 << 20
+    for variant, top in ((moe.VARIANT_AUTO, 272), (moe.VARIANT_DECODE, 372)):
+        assert moe.workspace_size(top, 4096, 14336, torch.bfloat16, variant) <= lim
+        assert moe.workspace_size(top + 1, 4096, 14336, torch.bfloat16, variant) > lim
