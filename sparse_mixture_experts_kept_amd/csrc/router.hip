@@ -192,8 +192,13 @@ struct GlueAddend {
 };
 
 // With wg == nullptr the routing is skipped (the glue after the last layer).
-template <typename T, bool COMBINE>
-__global__ void __launch_bounds__(256) rmsnorm_route_kernel(float* __restrict__ resid, GlueAddend add,
+// A row is kSteps steps of 8 elements per lane (d <= 512 * kSteps); rows of
+// up to 4096 take half the registers, and eight waves then share the LDS
+// copy of W_g (twice the waves per CU).
+template <typename T, bool COMBINE, int kSteps>
+__global__ void __launch_bounds__(kSteps <= 8 ? 512 : 256)
+    __attribute__((amdgpu_waves_per_eu(kSteps <= 8 ? 4 : 1))) rmsnorm_route_kernel(float* __restrict__ resid,
+                                                                                    GlueAddend add,
                                                             T* __restrict__ u, const T* __restrict__ wg,
                                                             const float* __restrict__ bias,
                                                             int32_t* __restrict__ idx_out, float* __restrict__ w_out,
@@ -204,7 +209,7 @@ __global__ void __launch_bounds__(256) rmsnorm_route_kernel(float* __restrict__ 
   if (wg) stage_router(wg, bias, wg_s, d, b);
   const T* __restrict__ y_add = static_cast<const T*>(add.y_add);
   constexpr int kVec = 8;                       // elements per lane and step
-  constexpr int kSteps = kMaxNormRouteD / (kWave * kVec);
+  static_assert(kSteps * kWave * kVec <= kMaxNormRouteD, "row length");
   const int lane = threadIdx.x % kWave;
   const int waves_per_block = blockDim.x / kWave;
   const int64_t n_waves = static_cast<int64_t>(gridDim.x) * waves_per_block;
@@ -309,21 +314,33 @@ __global__ void __launch_bounds__(256) rmsnorm_route_kernel(float* __restrict__ 
 }
 
 namespace {
-template <typename T, bool COMBINE>
-hipError_t launch_glue(float* resid, const GlueAddend& add, void* u, const void* wg, const float* bias, int32_t* idx,
-                       float* w, int64_t n_tokens, int d, float eps, int gating, int n_cu, hipStream_t s) {
+template <typename T, bool COMBINE, int kSteps>
+hipError_t launch_glue_rows(float* resid, const GlueAddend& add, void* u, const void* wg, const float* bias,
+                            int32_t* idx, float* w, int64_t n_tokens, int d, float eps, int gating, int n_cu,
+                            hipStream_t s) {
+  constexpr int kThreads = kSteps <= 8 ? 512 : 256;
+  constexpr int kRowsPerBlock = kThreads / kWave;  // a wave per row at a time
   const size_t lds = wg ? kExperts * static_cast<size_t>(d) * sizeof(T) : 0;
   if (lds > 64 * 1024) {
-    const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&rmsnorm_route_kernel<T, COMBINE>),
+    const hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&rmsnorm_route_kernel<T, COMBINE, kSteps>),
                                                hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (err != hipSuccess) return err;
   }
-  int64_t blocks = (n_tokens + 3) / 4;  // 4 waves, a row each
+  int64_t blocks = (n_tokens + kRowsPerBlock - 1) / kRowsPerBlock;
   const int64_t cap = static_cast<int64_t>(n_cu) * 2;
   if (blocks > cap) blocks = cap;
-  hipLaunchKernelGGL((rmsnorm_route_kernel<T, COMBINE>), dim3(blocks), dim3(256), lds, s, resid, add,
+  hipLaunchKernelGGL((rmsnorm_route_kernel<T, COMBINE, kSteps>), dim3(blocks), dim3(kThreads), lds, s, resid, add,
                      static_cast<T*>(u), static_cast<const T*>(wg), bias, idx, w, n_tokens, d, eps, gating);
   return hipGetLastError();
+}
+
+template <typename T, bool COMBINE>
+hipError_t launch_glue(float* resid, const GlueAddend& add, void* u, const void* wg, const float* bias, int32_t* idx,
+                       float* w, int64_t n_tokens, int d, float eps, int gating, int n_cu, hipStream_t s) {
+  if (d <= 8 * kWave * 8)
+    return launch_glue_rows<T, COMBINE, 8>(resid, add, u, wg, bias, idx, w, n_tokens, d, eps, gating, n_cu, s);
+  return launch_glue_rows<T, COMBINE, kMaxNormRouteD / (kWave * 8)>(resid, add, u, wg, bias, idx, w, n_tokens, d,
+                                                                    eps, gating, n_cu, s);
 }
 }  // namespace
 
