@@ -388,17 +388,17 @@ __device__ __forceinline__ f32x4 router_scores_partial(const bf16_t* __restrict_
     bf16x8 wa[kBatch], xa[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
-      wa[j] = *reinterpret_cast<const bf16x8*>(wp + k0 + 32 * j);
+      wa[j] = real_row ? *reinterpret_cast<const bf16x8*>(wp + k0 + 32 * j) : zero;  // rows 8..15: no load
       xa[j] = *reinterpret_cast<const bf16x8*>(xp + k0 + 32 * j);
     }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(real_row ? wa[j] : zero, xa[j], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[j], xa[j], acc, 0, 0, 0);
   }
   for (; k0 < ks; k0 += 32) {
-    const bf16x8 wa = *reinterpret_cast<const bf16x8*>(wp + k0);
+    const bf16x8 wa = real_row ? *reinterpret_cast<const bf16x8*>(wp + k0) : zero;
     const bf16x8 xa = *reinterpret_cast<const bf16x8*>(xp + k0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(real_row ? wa : zero, xa, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xa, acc, 0, 0, 0);
   }
   // acc[q] = score of expert 4*lg + q for token l16 (meaningful for lg < 2)
   return acc;
@@ -576,7 +576,7 @@ __global__ void __launch_bounds__(kPermThreads) route_permute_mfma_kernel(
       bf16x8 wa[kBatch], xa[kBatch][kGroups];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
-        wa[j] = *reinterpret_cast<const bf16x8*>(wp + k0 + 32 * j);
+        wa[j] = real_row ? *reinterpret_cast<const bf16x8*>(wp + k0 + 32 * j) : zero;  // rows 8..15: no load
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) xa[j][g] = *reinterpret_cast<const bf16x8*>(xp[g] + k0 + 32 * j);
       }
@@ -584,15 +584,15 @@ __global__ void __launch_bounds__(kPermThreads) route_permute_mfma_kernel(
       for (int j = 0; j < kBatch; ++j)
 #pragma unroll
         for (int g = 0; g < kGroups; ++g)
-          if (g < groups) acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(real_row ? wa[j] : zero, xa[j][g], acc[g], 0, 0, 0);
+          if (g < groups) acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[j], xa[j][g], acc[g], 0, 0, 0);
     }
     for (; k0 < ks; k0 += 32) {
-      const bf16x8 wa = *reinterpret_cast<const bf16x8*>(wp + k0);
+      const bf16x8 wa = real_row ? *reinterpret_cast<const bf16x8*>(wp + k0) : zero;
 #pragma unroll
       for (int g = 0; g < kGroups; ++g) {
         if (g < groups) {
           const bf16x8 xa = *reinterpret_cast<const bf16x8*>(xp[g] + k0);
-          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(real_row ? wa : zero, xa, acc[g], 0, 0, 0);
+          acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa, xa, acc[g], 0, 0, 0);
         }
       }
     }
