@@ -17,7 +17,10 @@ using moe::bf16_t;
 // to T = 128 (T = 80-128: 495-511 us against 510-523 us); beyond, experts
 // with more than 64 rows take further passes over their weights.
 constexpr int64_t kDecodeMaxTokens = 128;
-constexpr int64_t kRoutePermuteMaxTokens = 64;  // routing fused with the permutation (one workgroup)
+// Small batches: routing and permutation by launch_route_permute (bf16: a
+// workgroup per d-slice of the router, then one that routes and permutes).
+constexpr int64_t kRoutePermuteMaxTokens = 64;
+static_assert(kRoutePermuteMaxTokens <= moe::kRouteSplitMaxTokens, "small-batch router");
 constexpr size_t kRouterLdsLimit = 128 * 1024;
 constexpr int kMaxDevices = 64;
 
@@ -142,7 +145,7 @@ moe_status down_prefill(const moe_dims* dims, const bf16_t* h, const int32_t* of
 size_t align256(size_t v) { return (v + 255) & ~size_t{255}; }
 
 struct Workspace {
-  size_t idx, w, offsets, sorted, rows, gcounts, h, y_rows, y_rows2, total;
+  size_t idx, w, offsets, sorted, rows, gcounts, rpart, h, y_rows, y_rows2, total;
 };
 
 Workspace plan_workspace(const moe_dims* dims) {
@@ -155,6 +158,9 @@ Workspace plan_workspace(const moe_dims* dims) {
   ws.sorted = o; o += align256(slots * 4);
   ws.rows = o; o += align256(slots * 4);
   ws.gcounts = o; o += align256(static_cast<size_t>((dims->T + 15) / 16) * dims->E * 4);  // router group counts
+  // partial scores of the bf16 small-batch router (one workgroup per d-slice)
+  ws.rpart = o;
+  if (dims->dtype == MOE_BF16 && dims->T <= kRoutePermuteMaxTokens) o += align256(moe::route_partials_bytes(dims->T));
   ws.h = o; o += align256(slots * dims->f * elem_size(dims->dtype));
   ws.y_rows = o; o += align256(slots * dims->d * 4);
   // Second partial of the split down projection (and the prefill GEMMs'
@@ -462,10 +468,11 @@ moe_status ffn_forward_impl(const moe_dims* dims, const void* x, const void* w_g
     st = permute_slots(dims, pair, gcounts, offs, sorted, rows, expert_counts_out, s);
     if (st != MOE_OK) return st;
   } else if (dims->T <= kRoutePermuteMaxTokens) {
-    // Small batch: routing and permutation in one workgroup.
+    // Small batch: routing and permutation without the router's group counts.
     st = hip_status(moe::launch_route_permute(dims->dtype, x, w_gate, logit_bias, idx, w,
                                               static_cast<int32_t>(dims->T), dims->d, dims->gating,
-                                              dims->capacity, offs, sorted, rows, expert_counts_out, s));
+                                              dims->capacity, offs, sorted, rows, expert_counts_out,
+                                              reinterpret_cast<float*>(ws + plan.rpart), s));
     if (st != MOE_OK) return st;
     // (bf16 decode then runs the streaming up and down projections through
     // run_experts below.)

@@ -122,10 +122,18 @@ hipError_t launch_up_decode_stream(const bf16_t* x, const int32_t* offs, const i
 hipError_t launch_down_decode_stream(const bf16_t* h, const int32_t* offs, const bf16_t* w2, float* y_rows, int64_t T,
                                      int d, int f, int n_cu, hipStream_t s);
 
-// Small batches (T <= 64): routing + permutation in one workgroup.
+// Small batches (T <= 64): routing + permutation.  bf16: the router's
+// d-slices on one workgroup each, then one workgroup adds them, routes and
+// permutes; partials: route_partials_bytes(T) of device scratch.  fp32: one
+// workgroup (partials unused).
+constexpr int kRouteSlices = 16;           // d-slices of the bf16 small-batch router (at most)
+constexpr int64_t kRouteSplitMaxTokens = 64;
+inline size_t route_partials_bytes(int64_t T) {
+  return static_cast<size_t>(kRouteSlices) * static_cast<size_t>((T + 15) / 16) * 64 * 16;
+}
 hipError_t launch_route_permute(int dtype, const void* x, const void* wg, const float* bias, int32_t* idx, float* w,
                                 int32_t T, int d, int gating, int capacity, int32_t* offsets, int32_t* sorted_slots,
-                                int32_t* slot_rows, int32_t* counts_out, hipStream_t s);
+                                int32_t* slot_rows, int32_t* counts_out, float* partials, hipStream_t s);
 
 // y_rows2 (optional): a second partial-sum buffer added to y_rows first.
 hipError_t launch_combine(int dtype, const float* y_rows, const float* y_rows2, const int32_t* slot_rows,

@@ -295,6 +295,8 @@ def _expected_workspace(T, d, f, elem, prefill):
     a = lambda n: (n + 255) // 256 * 256  # noqa: E731
     slots = 2 * T
     total = a(slots * 4) * 4 + a(9 * 4) + a((T + 15) // 16 * 8 * 4) + a(slots * f * elem) + a(slots * d * 4)
+    if elem == 2 and T <= 64:  # the bf16 small-batch router's partial scores: 16 slices x 64 lanes x 16 B per group
+        total += a(16 * ((T + 15) // 16) * 64 * 16)
     return total + (a(slots * d * 4) if prefill else 0)
 
 
@@ -308,7 +310,8 @@ def _expected_workspace(T, d, f, elem, prefill):
     (600000, 4096, 256, "bf16", moe.VARIANT_AUTO, False)])
 def test_workspace_layout(T, d, f, dtype, variant, prefill):
     # The workspace is the routing, the permutation, the router's group
-    # counts, h and y_rows, each 256-byte aligned, plus the second fp32
+    # counts, the bf16 small-batch router's partial scores (T <= 64), h and
+    # y_rows, each 256-byte aligned, plus the second fp32
     # partial region only when the layer runs the bf16 prefill kernels: AUTO
     # streams up to 128 tokens, the prefill kernels need d, f >= 256 and x
     # below 4 GiB (600000 x 4096 bf16 is not), fp32 has its own kernels.
