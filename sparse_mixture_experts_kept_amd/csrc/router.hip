@@ -10,8 +10,9 @@
 // fp32: one wavefront per token; the router matrix W_g [8, d] is staged in
 // LDS, each lane accumulates 8 fp32 partial dot products over its share of
 // d, a butterfly (xor-shuffle) sum gives every lane all 8 scores, and lane 0
-// selects the pair.  For small batches one workgroup routes every token and
-// then sorts the slots.
+// selects the pair.  For small batches (T <= 64) the routing is followed by
+// the slot sort in the same workgroup: bf16 after a launch that computes the
+// router's d-slices on one workgroup each, fp32 in a single workgroup.
 #include "common.hpp"
 #include "launch.hpp"
 #include "permute_dev.hpp"
@@ -475,9 +476,9 @@ __global__ void __launch_bounds__(1024) router_mfma_kernel(const bf16_t* __restr
     router_finish_group(part, slices, blockIdx.x, T, bias, lane, gating, idx_out, w_out, logits_out, group_counts);
 }
 
-// Small batches: routing and the expert-major permutation in one workgroup
-// (one launch and one global round trip fewer).  16 waves route the tokens,
-// then the same workgroup sorts the slots.
+// fp32 small batches: routing and the expert-major permutation in one
+// workgroup (one launch and one global round trip fewer).  16 waves route
+// the tokens, then the same workgroup sorts the slots.
 template <typename T>
 __global__ void __launch_bounds__(kPermThreads) route_permute_kernel(
     const T* __restrict__ x, const T* __restrict__ wg, const float* __restrict__ bias, int32_t* __restrict__ idx_out,
